@@ -1,0 +1,90 @@
+"""numpy reference of the KDA recurrence (oracle, test infrastructure only).
+
+Follows "Understanding Kimi Delta Attention", section "The KDA Recurrence"
+(channel-wise update S_t = (I - beta k k^T) Diag(alpha) S_{t-1} + beta k v^T)
+and "kimi delta attn from first principles", section "KDA" (row-wise decay
+Diag(alpha) S_{t-1}, then the delta-rule error form of the update) and
+section "three gates" (read-out o_t = S_t^T q_t).
+
+Readings of the pages adopted here:
+  * decay before erase: the update multiplies Diag(alpha) onto S_{t-1} first
+    and the delta-rule error is taken against the decayed state (equation of
+    the first page's "The KDA Recurrence"; the step list "decay, erase,
+    write" of the second page's notebook toy);
+  * the gate scales rows, and rows are key channels (one forget gate per row
+    of the memory matrix, third page, section "Problems with GDN"/"KDA");
+  * the read-out uses the query and the updated state (third page, "three
+    gates"; the first page's "o_t = S_t k_t" is read as a garbled form);
+  * o is multiplied by the caller's `scale` (the pages give none);
+  * alpha = exp(g): the operator takes the log-gate g;
+  * a missing initial state is zero (the toy notebook "starts empty");
+  * packed sequences (cu_seqlens) are independent chains with their own
+    initial and final states.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _np(x, dtype):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach().to("cpu")
+        if str(x.dtype) == "torch.bfloat16":
+            x = x.float()
+        x = x.numpy()
+    return np.asarray(x, dtype=dtype)
+
+
+def chain_list(B, T, cu_seqlens):
+    """(row, start, end) for every sequence: rows of a [B, T] batch, or the
+    packed segments of cu_seqlens (then B must be 1)."""
+    if cu_seqlens is None:
+        return [(b, 0, T) for b in range(B)]
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    assert B == 1 and cu[0] == 0 and cu[-1] == T
+    return [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+
+
+def kda_forward(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None,
+                dtype=np.float64):
+    """Sequential KDA over every chain.
+
+    q, k, g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H];
+    initial_state: [N, H, dk, dv] or None (zeros); cu_seqlens: [N+1] or None.
+    Returns o [B, T, H, dv] and the final states [N, H, dk, dv] in `dtype`.
+    """
+    q, k, v, g, beta = (_np(x, dtype) for x in (q, k, v, g, beta))
+    h0 = _np(initial_state, dtype)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    chains = chain_list(B, T, cu_seqlens)
+    o = np.zeros((B, T, H, dv), dtype=dtype)
+    final = np.zeros((len(chains), H, dk, dv), dtype=dtype)
+    for n, (b, t0, t1) in enumerate(chains):
+        S = np.zeros((H, dk, dv), dtype=dtype) if h0 is None else h0[n].copy()
+        for t in range(t0, t1):
+            alpha = np.exp(g[b, t])                      # [H, dk]   step 1
+            S = alpha[:, :, None] * S                    # decay rows  step 2
+            pred = np.einsum("hkv,hk->hv", S, k[b, t])   # S^T k
+            u = beta[b, t][:, None] * (v[b, t] - pred)   # step 3
+            S = S + k[b, t][:, :, None] * u[:, None, :]  # step 4
+            o[b, t] = scale * np.einsum("hkv,hk->hv", S, q[b, t])  # step 5
+        final[n] = S
+    return o, final
+
+
+def kda_decode(q, k, v, g, beta, scale, state, dtype=np.float64):
+    """One token for each of N independent sequences.
+
+    q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H]; state [N, H, dk, dv].
+    Returns (o [N, H, dv], new_state).  This is the same recurrence with one
+    token per chain, which is what the single-token (fused recurrent) mode on
+    the first page computes.
+    """
+    q, k, v, g, beta = (_np(x, dtype) for x in (q, k, v, g, beta))
+    s = _np(state, dtype)
+    o, final = kda_forward(q[:, None], k[:, None], v[:, None], g[:, None], beta[:, None],
+                           scale, s, None, dtype)
+    return o[:, 0], final
