@@ -1,0 +1,215 @@
+"""Benchmark of the KDA operator on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  * chunked prefill of the packed varlen workload (64 sequences, 262144
+    tokens, H=32, d=128, bf16 q/k/v, fp32 g/beta/states, per-sequence
+    initial and final states), and
+  * one decode step of 256 sequences x 32 heads (state updated in place).
+
+`value` is prefill tokens/s (tokens counted once across heads) over the
+prefill launches of the timed steps; the decode step is reported beside it
+as state/total HBM GB/s.  Inputs are generated on the device before the
+timed region.  The roofline entry is for the prefill kernel: algorithmic
+bytes per launch / average launch time from HIP events on the launch stream.
+The CPU baseline is the C oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload varlen|long|prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_alg_bytes(tokens, H, dk, dv, N, in_bytes=2, out_bytes=4, h0=True, final=True):
+    """Bytes the prefill must move at least once: q, k, v, g, beta, o per token
+    and head, plus the initial and final states per sequence and head."""
+    per_th = (2 * dk + dv) * in_bytes + dk * 4 + 4 + dv * out_bytes
+    st = N * H * dk * dv * 4 * (int(h0) + int(final))
+    return tokens * H * per_th + st
+
+
+def prefill_alg_flops(tokens, H, dk, dv, C=64):
+    """Chunk-form FLOPs per token and head with triangles counted once:
+    2[(C/2)(3 dk + 2 dv) + 3 dk dv]."""
+    return tokens * H * 2 * ((C / 2) * (3 * dk + 2 * dv) + 3 * dk * dv)
+
+
+def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=4):
+    state = N * H * dk * dv * 4 * 2
+    other = N * H * ((2 * dk + dv) * in_bytes + dk * 4 + 4 + dv * out_bytes)
+    return state, state + other
+
+
+def cpu_baseline(x, budget_s=12.0):
+    """The C oracle (fp64, OpenMP over chains) on whole (sequence, head)
+    chains of the workload, sized to about `budget_s` of CPU work."""
+    import numpy as np
+    import torch
+    from oracle import cref
+    from oracle.ref import chain_list
+
+    threads = cref.max_threads()
+    B, T, H, dk = x.q.shape
+    chains = chain_list(B, T, x.cu_seqlens)
+    order = sorted(range(len(chains)), key=lambda n: chains[n][2] - chains[n][1])
+
+    def run(sel):
+        parts = [[], [], [], [], []]
+        h0s, starts, lens = [], [], []
+        row = 0
+        for n, h in sel:
+            b, t0, t1 = chains[n]
+            for i, src in enumerate((x.q, x.k, x.v, x.g, x.beta)):
+                parts[i].append(src[b, t0:t1, h].to("cpu", torch.float32).numpy())
+            if x.h0 is not None:
+                h0s.append(x.h0[n, h].to("cpu", torch.float64).numpy())
+            starts.append(row)
+            lens.append(t1 - t0)
+            row += t1 - t0
+        arrs = [np.concatenate(p) for p in parts]
+        t_0 = time.perf_counter()
+        cref.run_packed(starts, lens, dk, x.v.shape[-1], x.scale, *arrs,
+                        np.stack(h0s) if h0s else None, True, threads)
+        return row, time.perf_counter() - t_0
+
+    # calibrate on the shortest sequence, all heads
+    n0 = order[0]
+    ht, dt = run([(n0, h) for h in range(H)])
+    rate = ht / max(dt, 1e-6)
+    target = int(rate * budget_s)
+    sel, acc = [], 0
+    for n in order[1:]:
+        L = chains[n][2] - chains[n][1]
+        if acc + L * H > target:
+            break
+        sel += [(n, h) for h in range(H)]
+        acc += L * H
+    if not sel:
+        sel = [(n0, h) for h in range(H)]
+    ht, dt = run(sel)
+    seqs = len(sel) // H
+    return {"value": ht / dt / H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{seqs} whole sequences x {H} heads ({ht} head-tokens, {dt:.1f} s), "
+                      f"fp64 C recurrence, OpenMP over chains"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="varlen", choices=["varlen", "long", "prefill"])
+    ap.add_argument("--variant", default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(heads and sequences would shard across GPUs with no exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_89_amd as kda
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    print(f"bench: generating {args.workload} inputs on the device", file=sys.stderr, flush=True)
+    x = synth.make_inputs(args.workload, device=dev)
+    B, T, H, dk = x.q.shape
+    dv = x.v.shape[-1]
+    N = len(x.cu_seqlens) - 1 if x.cu_seqlens is not None else B
+    tokens = B * T
+    cu_dev = torch.as_tensor(x.cu_seqlens).to(dev) if x.cu_seqlens is not None else None
+    o = torch.empty(B, T, H, dv, device=dev, dtype=torch.float32)
+    fin = torch.empty(N, H, dk, dv, device=dev, dtype=torch.float32)
+    ws_bytes = kda.workspace_size(B, T, H, dk, dv, N, x.q.dtype, args.variant)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def prefill():
+        kda.chunk_fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0,
+                      x.cu_seqlens if cu_dev is None else cu_dev, o=o, final_state=fin,
+                      workspace=ws, variant=args.variant)
+
+    dec = None
+    if not args.no_decode:
+        d = synth.make_inputs("decode", device=dev)
+        dq, dk_, dvv, dg, db = (t[:, 0].contiguous() for t in (d.q, d.k, d.v, d.g, d.beta))
+        dstate = d.h0.clone()
+        dout = torch.empty(dq.shape[0], dq.shape[1], dv, device=dev)
+        dec = (dq, dk_, dvv, dg, db, dstate, dout, d.scale)
+
+    def decode():
+        dq, dk_, dvv, dg, db, dstate, dout, sc = dec
+        kda.decode_step(dq, dk_, dvv, dg, db, sc, dstate, o=dout)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        prefill()
+        if dec:
+            decode()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+        if dec:
+            decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    dec_ms = [b.elapsed_time(c) for _, b, c in ev]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+
+    alg_b = prefill_alg_bytes(tokens, H, dk, dv, N, h0=x.h0 is not None)
+    alg_f = prefill_alg_flops(tokens, H, dk, dv)
+    achieved = alg_b / (pre_avg * 1e-3) / 1e9
+    value = tokens / (pre_avg * 1e-3)
+    line = {
+        "metric": "KDA prefill tokens/s (H=32,d=128) + decode state HBM GB/s; % of roofline",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded, generated on the device)",
+        "config": {"workload": f"{args.workload}: {N} sequences, {tokens} tokens, H={H}, "
+                               f"d_k=d_v={dk}, bf16 q/k/v, fp32 g/beta/state/o",
+                   "global_batch": N, "seq_len": tokens, "parallelism": "none (1 GPU)"},
+        "prefill_ms": pre_avg, "prefill_ms_min": min(pre_ms),
+        "mfma_peak_equiv_frac": alg_f / (pre_avg * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": f"prefill ({args.variant})", "alg_bytes_per_launch": alg_b},
+    }
+    if dec:
+        N3, H3 = dec[0].shape[0], dec[0].shape[1]
+        sb, tb = decode_alg_bytes(N3, H3, 128, 128)
+        dm = sum(dec_ms) / len(dec_ms)
+        line["decode"] = {"us_per_step": dm * 1e3, "state_gbs": sb / (dm * 1e-3) / 1e9,
+                          "total_gbs": tb / (dm * 1e-3) / 1e9,
+                          "frac": tb / (dm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "config": f"{N3} sequences x {H3} heads, d=128"}
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) Kimi Delta Attention operator.
+
+The compute lives in libkda.so (hand-written HIP kernels behind the C ABI in
+include/kda.h); this package is a thin binding over it:
+
+    chunk_fwd(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None)
+        -> (o, final_state)          chunked prefill, varlen via cu_seqlens
+    decode_step(q, k, v, g, beta, scale, state) -> o
+                                     one token per sequence, state in place
+"""
+from ._lib import (KDAError, abi_version, chunk_fwd, decode_step, lib, status_str,  # noqa: F401
+                   workspace_size)

@@ -1,0 +1,228 @@
+// C ABI of the KDA operator: argument validation, variant choice, launches.
+// Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+using kda::DecodeArgs;
+using kda::PrefillArgs;
+
+bool head_size_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool dtype_ok(kda_dtype t) { return t == KDA_F32 || t == KDA_BF16; }
+size_t esize(kda_dtype t) { return t == KDA_BF16 ? 2 : 4; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const void* p, size_t bytes) {
+    uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return Range{b, b + bytes};
+}
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool chunk_supported(int32_t dk, int32_t dv, kda_dtype in) {
+    (void)dk;
+    (void)dv;
+    (void)in;
+    return false;
+}
+
+kda_variant resolve_variant(kda_variant v, int32_t dk, int32_t dv, kda_dtype in) {
+    if (v != KDA_VARIANT_AUTO) return v;
+    return chunk_supported(dk, dv, in) ? KDA_VARIANT_CHUNK : KDA_VARIANT_RECURRENT;
+}
+
+size_t workspace_for(kda_variant v, int32_t B, int32_t T, int32_t H, int32_t N) {
+    (void)B;
+    (void)T;
+    (void)H;
+    (void)N;
+    (void)v;
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_str(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "a size is negative or inconsistent";
+        case KDA_ERR_DTYPE: return "unknown dtype";
+        case KDA_ERR_UNSUPPORTED: return "unsupported head size, dtype or variant";
+        case KDA_ERR_SEQLENS: return "cu_seqlens must satisfy 0 = c0 <= c1 <= ... <= cN = T";
+        case KDA_ERR_ALIAS: return "an output overlaps an input or another output";
+        case KDA_ERR_ALIGN: return "a pointer is not aligned as required";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_HIP: return "a HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                    int32_t N, kda_dtype in_dtype, kda_variant variant) {
+    if (B < 0 || T < 0 || H < 0 || N < 0 || !head_size_ok(d_k) || !head_size_ok(d_v) ||
+        !dtype_ok(in_dtype))
+        return 0;
+    return workspace_for(resolve_variant(variant, d_k, d_v, in_dtype), B, T, H, N);
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float scale, const float* initial_state,
+                         const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t B,
+                         int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
+                         kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, kda_variant variant,
+                         void* stream) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
+    if (B < 0 || T < 0 || H < 0 || N < 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_SHAPE;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK_SCAN) return KDA_ERR_UNSUPPORTED;
+    if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr)) return KDA_ERR_NULL;
+    if (cu_seqlens) {
+        if (B != 1) return KDA_ERR_SHAPE;
+        if (cu_seqlens_host[0] != 0 || cu_seqlens_host[N] != T) return KDA_ERR_SEQLENS;
+        for (int32_t i = 0; i < N; ++i)
+            if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return KDA_ERR_SEQLENS;
+    } else if (N != B) {
+        return KDA_ERR_SHAPE;
+    }
+    if (!aligned(initial_state, 16) || !aligned(final_state, 16)) return KDA_ERR_ALIGN;
+    const int64_t tokens = static_cast<int64_t>(B) * T;
+    if (tokens == 0 || N == 0 || H == 0) {
+        // No token to process; a requested final state equals the initial one.
+        if (N > 0 && H > 0 && final_state) {
+            const int64_t n = static_cast<int64_t>(N) * H * d_k * d_v;
+            if (initial_state && initial_state != final_state &&
+                overlap(range(initial_state, n * 4), range(final_state, n * 4)))
+                return KDA_ERR_ALIAS;
+            if (kda::launch_copy_or_zero(final_state, initial_state, n,
+                                         static_cast<hipStream_t>(stream)) != hipSuccess)
+                return KDA_ERR_HIP;
+        }
+        return KDA_OK;
+    }
+    if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL;
+    if (static_cast<int64_t>(N) * H * 8 > INT32_MAX || H > 65535) return KDA_ERR_SHAPE;
+
+    const kda_variant var = resolve_variant(variant, d_k, d_v, in_dtype);
+    if ((var == KDA_VARIANT_CHUNK || var == KDA_VARIANT_CHUNK_SCAN) &&
+        !chunk_supported(d_k, d_v, in_dtype))
+        return KDA_ERR_UNSUPPORTED;
+
+    for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(o),
+                          static_cast<const void*>(initial_state),
+                          static_cast<const void*>(final_state)})
+        if (!aligned(p, 16)) return KDA_ERR_ALIGN;
+    if (!aligned(beta, 4) || !aligned(cu_seqlens, 4) || !aligned(workspace, 256))
+        return KDA_ERR_ALIGN;
+
+    const size_t ws_need = workspace_for(var, B, T, H, N);
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
+
+    const size_t th = static_cast<size_t>(tokens) * H;
+    const size_t state_bytes = static_cast<size_t>(N) * H * d_k * d_v * sizeof(float);
+    const Range in_r[] = {range(q, th * d_k * esize(in_dtype)), range(k, th * d_k * esize(in_dtype)),
+                          range(v, th * d_v * esize(in_dtype)), range(g, th * d_k * 4),
+                          range(beta, th * 4), range(initial_state, initial_state ? state_bytes : 0),
+                          range(cu_seqlens, cu_seqlens ? (static_cast<size_t>(N) + 1) * 4 : 0)};
+    const Range o_r = range(o, th * d_v * esize(out_dtype));
+    const Range f_r = range(final_state, final_state ? state_bytes : 0);
+    const Range w_r = range(workspace, ws_need > 0 ? workspace_bytes : 0);
+    for (const Range& r : in_r) {
+        if (overlap(o_r, r) || overlap(w_r, r)) return KDA_ERR_ALIAS;
+        const bool same_state = final_state && r.lo == reinterpret_cast<uintptr_t>(initial_state) &&
+                                static_cast<const void*>(final_state) == initial_state;
+        if (!same_state && overlap(f_r, r)) return KDA_ERR_ALIAS;
+    }
+    if (overlap(o_r, f_r) || overlap(o_r, w_r) || overlap(f_r, w_r)) return KDA_ERR_ALIAS;
+
+    PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.scale = scale;
+    a.h0 = initial_state;
+    a.cu = cu_seqlens;
+    a.cu_host = cu_seqlens_host;
+    a.B = B;
+    a.T = T;
+    a.H = H;
+    a.dk = d_k;
+    a.dv = d_v;
+    a.N = N;
+    a.in_bf16 = in_dtype == KDA_BF16;
+    a.out_bf16 = out_dtype == KDA_BF16;
+    a.o = o;
+    a.hT = final_state;
+    a.ws = workspace;
+    a.ws_bytes = workspace_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+
+    hipError_t e = hipErrorInvalidValue;
+    switch (var) {
+        case KDA_VARIANT_RECURRENT: e = kda::launch_recurrent(a); break;
+        default: return KDA_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float scale, float* state, int32_t N, int32_t H,
+                           int32_t d_k, int32_t d_v, kda_dtype in_dtype, kda_dtype out_dtype,
+                           void* o, void* stream) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
+    if (N < 0 || H < 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_SHAPE;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (N == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+    if (static_cast<int64_t>(N) * H > INT32_MAX) return KDA_ERR_SHAPE;
+    for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(state), static_cast<const void*>(o)})
+        if (!aligned(p, 16)) return KDA_ERR_ALIGN;
+    if (!aligned(beta, 4)) return KDA_ERR_ALIGN;
+    const size_t nh = static_cast<size_t>(N) * H;
+    const Range in_r[] = {range(q, nh * d_k * esize(in_dtype)), range(k, nh * d_k * esize(in_dtype)),
+                          range(v, nh * d_v * esize(in_dtype)), range(g, nh * d_k * 4),
+                          range(beta, nh * 4)};
+    const Range s_r = range(state, nh * d_k * d_v * 4);
+    const Range o_r = range(o, nh * d_v * esize(out_dtype));
+    for (const Range& r : in_r)
+        if (overlap(o_r, r) || overlap(s_r, r)) return KDA_ERR_ALIAS;
+    if (overlap(o_r, s_r)) return KDA_ERR_ALIAS;
+
+    DecodeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.scale = scale;
+    a.state = state;
+    a.N = N;
+    a.H = H;
+    a.dk = d_k;
+    a.dv = d_v;
+    a.in_bf16 = in_dtype == KDA_BF16;
+    a.out_bf16 = out_dtype == KDA_BF16;
+    a.o = o;
+    a.stream = static_cast<hipStream_t>(stream);
+    return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace kda {
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float scale;
+    const float* h0;     // [N, H, dk, dv] or nullptr
+    const int32_t* cu;   // device [N+1] or nullptr (then sequences are rows of length T)
+    const int32_t* cu_host;
+    int B, T, H, dk, dv, N;
+    bool in_bf16, out_bf16;
+    void* o;
+    float* hT;           // [N, H, dk, dv] or nullptr
+    void* ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float scale;
+    float* state;
+    int N, H, dk, dv;
+    bool in_bf16, out_bf16;
+    void* o;
+    hipStream_t stream;
+};
+
+// Calls f(integral_constant<int, DK>, integral_constant<int, DV>) for the
+// supported head sizes; returns hipErrorInvalidValue for anything else.
+template <typename F>
+hipError_t dispatch_head_sizes(int dk, int dv, F&& f) {
+    auto inner = [&](auto DK) -> hipError_t {
+        switch (dv) {
+            case 16: return f(DK, std::integral_constant<int, 16>{});
+            case 32: return f(DK, std::integral_constant<int, 32>{});
+            case 64: return f(DK, std::integral_constant<int, 64>{});
+            case 128: return f(DK, std::integral_constant<int, 128>{});
+            default: return hipErrorInvalidValue;
+        }
+    };
+    switch (dk) {
+        case 16: return inner(std::integral_constant<int, 16>{});
+        case 32: return inner(std::integral_constant<int, 32>{});
+        case 64: return inner(std::integral_constant<int, 64>{});
+        case 128: return inner(std::integral_constant<int, 128>{});
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);
+hipError_t launch_recurrent(const PrefillArgs& a);
+hipError_t launch_decode(const DecodeArgs& a);
+
+}  // namespace kda

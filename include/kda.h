@@ -1,0 +1,147 @@
+/* kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention operator.
+ *
+ * The operator is the channel-gated delta rule of "Understanding Kimi Delta
+ * Attention" (section "The KDA Recurrence: Scalar Gate vs Channel-wise
+ * Gate") and "kimi delta attn from first principles" (sections "KDA" and
+ * "three gates"): for every chain (one sequence, one head) a state S of
+ * d_k x d_v fp32 values, rows indexed by key channels, evolves per token as
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * i.e. decay each row by its own gate, take the delta-rule error against the
+ * decayed state, write rank 1, and read the updated state with the query.
+ * g is the log forget gate (alpha = exp(g), expected <= 0); beta is the
+ * update gate; q and k are used exactly as given (the layer normalises them
+ * upstream); `scale` multiplies the read-out (typically 1/sqrt(d_k)).
+ *
+ * Two modes, as on the first page ("Two execution modes"): chunked prefill
+ * over whole sequences (kda_chunk_fwd) and a single-token step that updates
+ * the state in place (kda_decode_step).  The caller chooses the mode.
+ *
+ * Conventions for every entry point:
+ *  - every tensor pointer is a device pointer owned by the caller, except
+ *    arguments whose name ends in _host; nothing is retained after return;
+ *  - tensors are dense, row-major, in the shapes given below (innermost last);
+ *  - all work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *    stream) and is asynchronous; outputs are valid after the stream is
+ *    synchronised;
+ *  - arguments are validated on the host before anything is enqueued; on an
+ *    error a status is returned, nothing is launched and no output is
+ *    written.  Device-side faults surface at the caller's next sync, as
+ *    usual in HIP.  Non-finite inputs propagate; they are not checked;
+ *  - supported head sizes: d_k, d_v in {16, 32, 64, 128}; q/k/v in fp32 or
+ *    bf16; g, beta, states in fp32; o in fp32 or bf16;
+ *  - pointers to fp32/bf16 tensors must be 16-byte aligned; beta and
+ *    cu_seqlens 4-byte aligned;
+ *  - the library allocates no device memory; scratch comes from the
+ *    caller's workspace.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL */
+    KDA_ERR_SHAPE = 2,       /* a size is negative or inconsistent */
+    KDA_ERR_DTYPE = 3,       /* unknown dtype code */
+    KDA_ERR_UNSUPPORTED = 4, /* valid but not supported (head size, variant) */
+    KDA_ERR_SEQLENS = 5,     /* cu_seqlens_host not 0 = c0 <= c1 <= ... <= cN = T */
+    KDA_ERR_ALIAS = 6,       /* an output overlaps an input or another output */
+    KDA_ERR_ALIGN = 7,       /* a pointer is not aligned as required */
+    KDA_ERR_WORKSPACE = 8,   /* workspace NULL or smaller than required */
+    KDA_ERR_HIP = 9          /* a HIP launch or copy failed */
+} kda_status;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Prefill implementations.  AUTO picks the fastest one that supports the
+ * arguments; the others exist to compare paths against each other.
+ *  RECURRENT  token-sequential fused recurrent kernel, any supported shape;
+ *  CHUNK      chunkwise kernel on bf16 MFMA, 64-token chunks, one workgroup
+ *             per chain (bf16 inputs, d_k = d_v = 128);
+ *  CHUNK_SCAN CHUNK plus a segment scan that runs each long chain on many
+ *             workgroups (same inputs as CHUNK). */
+typedef enum kda_variant {
+    KDA_VARIANT_AUTO = 0,
+    KDA_VARIANT_RECURRENT = 1,
+    KDA_VARIANT_CHUNK = 2,
+    KDA_VARIANT_CHUNK_SCAN = 3
+} kda_variant;
+
+/* ABI version (KDA_ABI_VERSION of the built library). */
+int kda_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* kda_status_str(kda_status status);
+
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes and variant
+ * (0 is a valid answer).  N is the number of sequences (B, or the length of
+ * cu_seqlens minus one).  Returns 0 for arguments kda_chunk_fwd would reject. */
+size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                    int32_t N, kda_dtype in_dtype, kda_variant variant);
+
+/* Chunked prefill over N independent sequences ("Understanding Kimi Delta
+ * Attention", section "The Chunkwise DPLR Algorithm": chunks of the
+ * sequence, results equal to the sequential recurrence).
+ *
+ *  q, k        [B, T, H, d_k]  in_dtype
+ *  v           [B, T, H, d_v]  in_dtype
+ *  g           [B, T, H, d_k]  fp32, log forget gate
+ *  beta        [B, T, H]       fp32, update gate
+ *  scale       read-out scale
+ *  initial_state [N, H, d_k, d_v] fp32, or NULL for zero states
+ *  cu_seqlens  [N+1] int32 device, or NULL: then N must equal B and row b of
+ *              the batch is sequence b.  With cu_seqlens B must be 1 and
+ *              sequence n is tokens cu[n] .. cu[n+1]-1 of the packed axis.
+ *  cu_seqlens_host  host copy of cu_seqlens (required with it; validated:
+ *              cu[0] = 0, non-decreasing, cu[N] = T).  Empty sequences are
+ *              allowed (their final state is the initial state).
+ *  o           [B, T, H, d_v] out_dtype (written for every token)
+ *  final_state [N, H, d_k, d_v] fp32, or NULL to skip; may be the same
+ *              pointer as initial_state (in-place update); no other overlap
+ *              between outputs and inputs is allowed.
+ *  workspace   device scratch of at least kda_chunk_fwd_workspace_size()
+ *              bytes (may be NULL when that is 0), 256-byte aligned.
+ * T = 0 or N = 0 is a successful no-op. */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float scale, const float* initial_state,
+                         const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                         int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
+                         kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, kda_variant variant,
+                         void* stream);
+
+/* One token for each of N independent sequences, state updated in place
+ * ("Understanding Kimi Delta Attention", section "Two execution modes":
+ * the fused recurrent step with constant memory; the recurrence of section
+ * "The KDA Recurrence").
+ *
+ *  q, k        [N, H, d_k]  in_dtype
+ *  v           [N, H, d_v]  in_dtype
+ *  g           [N, H, d_k]  fp32
+ *  beta        [N, H]       fp32
+ *  scale       read-out scale (the same convention as kda_chunk_fwd)
+ *  state       [N, H, d_k, d_v] fp32, read and overwritten with S_t
+ *  o           [N, H, d_v] out_dtype; must not overlap any input or state.
+ * N = 0 is a successful no-op. */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float scale, float* state, int32_t N, int32_t H,
+                           int32_t d_k, int32_t d_v, kda_dtype in_dtype, kda_dtype out_dtype,
+                           void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,127 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/kda.h
+declares, and rejects bad arguments with the documented status before any
+HIP call (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_89_amd as kda
+from gated_delta_rule_89_amd import _lib
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HEADER = os.path.join(HERE, "..", "include", "kda.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, SEQ, ALIAS, ALIGN, WS, HIP = range(10)
+F32, BF16 = 0, 1
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_match_header():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(kda.lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert kda.abi_version() == 1
+    for code in range(10):
+        s = kda.status_str(code)
+        assert isinstance(s, str) and s
+    assert kda.status_str(0) == "ok"
+
+
+# Fake device addresses: never dereferenced, every call below fails validation.
+BASE = 0x7F0000000000
+MB = 1 << 20
+
+
+def addr(i, off=0):
+    return P(BASE + i * 64 * MB + off)
+
+
+def chunk(q=None, k=None, v=None, g=None, beta=None, h0=None, cu=None, cu_host=None,
+          B=1, T=64, H=2, dk=16, dv=16, N=1, ind=F32, outd=F32, o=None, fin=None, ws=None,
+          ws_bytes=0, variant=0):
+    q = addr(0) if q is None else q
+    k = addr(1) if k is None else k
+    v = addr(2) if v is None else v
+    g = addr(3) if g is None else g
+    beta = addr(4) if beta is None else beta
+    o = addr(5) if o is None else o
+    return kda.lib.kda_chunk_fwd(q, k, v, g, beta, 0.25, h0, cu, cu_host, B, T, H, dk, dv, N,
+                                 ind, outd, o, fin, ws, ws_bytes, variant, None)
+
+
+def host_cu(vals):
+    arr = (ctypes.c_int32 * len(vals))(*vals)
+    return arr, ctypes.cast(arr, P)
+
+
+def test_chunk_validation():
+    assert chunk(ind=7) == DTYPE
+    assert chunk(outd=2) == DTYPE
+    assert chunk(T=-1) == SHAPE
+    assert chunk(dk=48) == UNSUP
+    assert chunk(dv=256) == UNSUP
+    assert chunk(variant=9) == UNSUP
+    assert chunk(N=2) == SHAPE                       # N != B without cu_seqlens
+    assert chunk(q=P(0)) == NULL
+    assert chunk(o=P(0)) == NULL
+    assert chunk(q=addr(0, 2)) == ALIGN
+    assert chunk(beta=addr(4, 2)) == ALIGN
+    assert chunk(fin=addr(7, 8), h0=addr(6)) == ALIGN
+    # cu_seqlens: device and host copies go together; B = 1; 0 = c0 <= ... <= cN = T
+    _, c = host_cu([0, 30, 64])
+    assert chunk(cu=addr(8), N=2) == NULL
+    assert chunk(cu_host=c, N=2) == NULL
+    assert chunk(cu=addr(8), cu_host=c, N=2, B=2) == SHAPE
+    keep, bad = host_cu([0, 40, 30, 64])
+    assert chunk(cu=addr(8), cu_host=bad, N=3) == SEQ
+    keep2, bad2 = host_cu([0, 30, 63])
+    assert chunk(cu=addr(8), cu_host=bad2, N=2) == SEQ
+    keep3, bad3 = host_cu([1, 30, 64])
+    assert chunk(cu=addr(8), cu_host=bad3, N=2) == SEQ
+    # aliasing: o over q; final over q; final partially over the initial state
+    assert chunk(o=addr(0)) == ALIAS
+    assert chunk(fin=addr(1)) == ALIAS
+    assert chunk(h0=addr(6), fin=addr(6, 1024)) == ALIAS
+    assert chunk(o=addr(7), fin=addr(7, 4096)) == ALIAS
+
+
+def test_workspace_size_rejects_bad_arguments():
+    assert kda.lib.kda_chunk_fwd_workspace_size(1, -1, 1, 128, 128, 1, BF16, 0) == 0
+    assert kda.lib.kda_chunk_fwd_workspace_size(1, 64, 1, 100, 128, 1, BF16, 0) == 0
+    assert kda.lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 1, 5, 0) == 0
+
+
+def decode(q=None, k=None, v=None, g=None, beta=None, state=None, N=4, H=2, dk=16, dv=16,
+           ind=F32, outd=F32, o=None):
+    q = addr(0) if q is None else q
+    k = addr(1) if k is None else k
+    v = addr(2) if v is None else v
+    g = addr(3) if g is None else g
+    beta = addr(4) if beta is None else beta
+    state = addr(5) if state is None else state
+    o = addr(6) if o is None else o
+    return kda.lib.kda_decode_step(q, k, v, g, beta, 0.25, state, N, H, dk, dv, ind, outd, o, None)
+
+
+def test_decode_validation():
+    assert decode(ind=3) == DTYPE
+    assert decode(N=-1) == SHAPE
+    assert decode(dk=7) == UNSUP
+    assert decode(state=P(0)) == NULL
+    assert decode(g=P(0)) == NULL
+    assert decode(q=addr(0, 4)) == ALIGN
+    assert decode(o=addr(5)) == ALIAS                 # o over the state
+    assert decode(state=addr(2)) == ALIAS             # state over v
+    assert decode(N=0) == OK                          # no-op, nothing launched

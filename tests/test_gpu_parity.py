@@ -1,0 +1,211 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Inputs come from the seeded generator in `synth`; the oracle receives the
+very same values (bf16 widened exactly).  Criteria: tests/parity.py.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import cref, ref
+from tests.parity import assert_parity, max_abs, rel_rms
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def _kda():
+    import gated_delta_rule_89_amd as kda
+    return kda
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def oracle_prefill(x, select=None):
+    return cref.kda_forward(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0, x.cu_seqlens,
+                            n_threads=THREADS)
+
+
+def run_prefill(x, variant="auto", **kw):
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    o, f = _kda().chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, xd.h0, x.cu_seqlens,
+                            variant=variant, **kw)
+    torch.cuda.synchronize()
+    return o, f
+
+
+VARIANTS = ["auto", "recurrent"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_tiny_fp32(variant):
+    say(f"tiny fp32 T=64 d=16 variant={variant}")
+    x = synth.make_inputs("tiny")
+    o, f = run_prefill(x, variant)
+    o_ref, f_ref = ref.kda_forward(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0)
+    assert_parity(o, o_ref, torch.float32, "o")
+    assert_parity(f, f_ref, torch.float32, "final")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_prefill_workload_full(variant):
+    say(f"prefill B=1 T=4096 H=8 d=128 bf16 variant={variant}")
+    x = synth.make_inputs("prefill")
+    o, f = run_prefill(x, variant)
+    o_ref, f_ref = oracle_prefill(x)
+    eo = assert_parity(o, o_ref, torch.bfloat16, "o")
+    ef = assert_parity(f, f_ref, torch.bfloat16, "final")
+    say(f"  o {eo:.2e} final {ef:.2e}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_varlen_ragged(variant):
+    lens = [1000, 0, 77, 2500, 64, 1, 130]
+    say(f"varlen lens={lens} H=4 bf16 variant={variant}")
+    x = synth.make_inputs("varlen", lens=lens, H=4)
+    o, f = run_prefill(x, variant)
+    o_ref, f_ref = oracle_prefill(x)
+    assert_parity(o, o_ref, torch.bfloat16, "o")
+    assert_parity(f, f_ref, torch.bfloat16, "final")
+    # the empty sequence keeps its initial state exactly
+    assert torch.equal(f[1].cpu(), x.h0[1])
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 16), (16, 128), (128, 128)])
+def test_head_sizes_fp32(dk, dv):
+    say(f"recurrent fp32 dk={dk} dv={dv} B=2 T=37 H=2")
+    rng = np.random.default_rng(dk * 1000 + dv)
+    B, T, H = 2, 37, 2
+    q = torch.tensor(rng.standard_normal((B, T, H, dk)), dtype=torch.float32)
+    k = torch.nn.functional.normalize(torch.tensor(rng.standard_normal((B, T, H, dk)),
+                                                   dtype=torch.float32), dim=-1)
+    v = torch.tensor(rng.standard_normal((B, T, H, dv)), dtype=torch.float32)
+    g = -torch.nn.functional.softplus(torch.tensor(rng.standard_normal((B, T, H, dk)),
+                                                   dtype=torch.float32))
+    beta = torch.sigmoid(torch.tensor(rng.standard_normal((B, T, H)), dtype=torch.float32))
+    h0 = torch.tensor(0.1 * rng.standard_normal((B, H, dk, dv)), dtype=torch.float32)
+    dev = torch.device("cuda")
+    o, f = _kda().chunk_fwd(q.to(dev), k.to(dev), v.to(dev), g.to(dev), beta.to(dev), 0.3,
+                            h0.to(dev), variant="recurrent")
+    o_ref, f_ref = ref.kda_forward(q, k, v, g, beta, 0.3, h0)
+    assert_parity(o, o_ref, torch.float32, "o")
+    assert_parity(f, f_ref, torch.float32, "final")
+
+
+def test_decode_workload_full():
+    say("decode N=256 H=32 d=128 bf16")
+    x = synth.make_inputs("decode")
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    st = xd.h0.clone()
+    o = _kda().decode_step(xd.q[:, 0], xd.k[:, 0], xd.v[:, 0], xd.g[:, 0], xd.beta[:, 0],
+                           x.scale, st)
+    torch.cuda.synchronize()
+    res = cref.kda_forward(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0, None, n_threads=THREADS)
+    o_ref, s_ref = res
+    e1 = max_abs(o[:, None], o_ref)
+    e2 = max_abs(st, s_ref)
+    say(f"  o max-abs {e1:.2e}  state max-abs {e2:.2e}")
+    # fp32 arithmetic on exact inputs: the fp32 bound applies
+    assert e1 <= 1e-4 and e2 <= 1e-4
+
+
+@pytest.mark.parametrize("dk,dv,ind", [(16, 16, torch.float32), (64, 128, torch.bfloat16),
+                                        (128, 32, torch.float32), (32, 16, torch.bfloat16)])
+def test_decode_head_sizes(dk, dv, ind):
+    say(f"decode dk={dk} dv={dv} {ind}")
+    rng = np.random.default_rng(dk + dv)
+    N, H = 5, 3
+    q = torch.tensor(rng.standard_normal((N, H, dk)), dtype=torch.float32).to(ind)
+    k = torch.nn.functional.normalize(torch.tensor(rng.standard_normal((N, H, dk))), dim=-1).to(ind)
+    v = torch.tensor(rng.standard_normal((N, H, dv)), dtype=torch.float32).to(ind)
+    g = -torch.rand(N, H, dk, generator=torch.Generator().manual_seed(1))
+    beta = torch.rand(N, H, generator=torch.Generator().manual_seed(2))
+    s0 = torch.randn(N, H, dk, dv, generator=torch.Generator().manual_seed(3))
+    dev = torch.device("cuda")
+    st = s0.to(dev)
+    o = _kda().decode_step(q.to(dev), k.to(dev), v.to(dev), g.to(dev), beta.to(dev), 0.7, st)
+    o_ref, s_ref = ref.kda_decode(q, k, v, g, beta, 0.7, s0)
+    assert max_abs(o, o_ref) <= 1e-4 and max_abs(st, s_ref) <= 1e-4
+
+
+def test_prefill_then_decode_equals_prefill():
+    say("prefill T-1 then decode == prefill T (H=4, T=300)")
+    x = synth.make_inputs("prefill", T=300, H=4)
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    kda = _kda()
+    o_all, f_all = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, xd.h0)
+    _, f1 = kda.chunk_fwd(xd.q[:, :-1].contiguous(), xd.k[:, :-1].contiguous(),
+                          xd.v[:, :-1].contiguous(), xd.g[:, :-1].contiguous(),
+                          xd.beta[:, :-1].contiguous(), x.scale, xd.h0)
+    od = kda.decode_step(xd.q[:, -1].contiguous(), xd.k[:, -1].contiguous(),
+                         xd.v[:, -1].contiguous(), xd.g[:, -1].contiguous(),
+                         xd.beta[:, -1].contiguous(), x.scale, f1)
+    torch.cuda.synchronize()
+    assert rel_rms(od, o_all[:, -1]) <= 2e-2
+    assert rel_rms(f1, f_all) <= 2e-2
+
+
+def test_split_call_state_passing():
+    say("split call at 700 of T=1500 H=2")
+    x = synth.make_inputs("prefill", T=1500, H=2)
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    kda = _kda()
+    sl = lambda t, a, b: t[:, a:b].contiguous()
+    o_all, f_all = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, xd.h0)
+    o1, f1 = kda.chunk_fwd(*(sl(t, 0, 700) for t in (xd.q, xd.k, xd.v, xd.g, xd.beta)),
+                           x.scale, xd.h0)
+    o2, f2 = kda.chunk_fwd(*(sl(t, 700, 1500) for t in (xd.q, xd.k, xd.v, xd.g, xd.beta)),
+                           x.scale, f1)
+    torch.cuda.synchronize()
+    assert rel_rms(torch.cat([o1, o2], 1), o_all) <= 2e-2
+    assert rel_rms(f2, f_all) <= 2e-2
+
+
+def test_in_place_final_state_and_bf16_output():
+    say("final_state is initial_state; bf16 o equals the fp32 o rounded")
+    x = synth.make_inputs("prefill", T=130, H=2)
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    kda = _kda()
+    o32, f32 = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, xd.h0)
+    st = xd.h0.clone()
+    o16, f16 = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, st, final_state=st,
+                             out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert f16.data_ptr() == st.data_ptr()
+    assert torch.equal(f16, f32)
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_empty_inputs():
+    say("T=0 copies the initial state; N=0 is a no-op")
+    dev = torch.device("cuda")
+    kda = _kda()
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt, device=dev)
+    h0 = torch.randn(1, 2, 128, 128, device=dev)
+    o, f = kda.chunk_fwd(z(1, 0, 2, 128), z(1, 0, 2, 128), z(1, 0, 2, 128),
+                         z(1, 0, 2, 128, dt=torch.float32), z(1, 0, 2, dt=torch.float32),
+                         0.1, h0)
+    o2, f2 = kda.chunk_fwd(z(1, 0, 2, 128), z(1, 0, 2, 128), z(1, 0, 2, 128),
+                           z(1, 0, 2, 128, dt=torch.float32), z(1, 0, 2, dt=torch.float32), 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(f, h0) and o.numel() == 0
+    assert torch.count_nonzero(f2).item() == 0
+
+
+def test_run_to_run_determinism():
+    say("bitwise determinism, varlen H=4")
+    x = synth.make_inputs("varlen", lens=[300, 17, 900], H=4)
+    a = run_prefill(x)
+    b = run_prefill(x)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
