@@ -30,24 +30,20 @@ bool overlap(Range a, Range b) {
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-bool chunk_supported(int32_t dk, int32_t dv, kda_dtype in) {
-    (void)dk;
-    (void)dv;
-    (void)in;
-    return false;
+// The chunked kernels take bf16 q/k/v with d_k = d_v = 128.
+bool chunk_supported(kda_variant v, int32_t dk, int32_t dv, kda_dtype in) {
+    if (v == KDA_VARIANT_CHUNK_SCAN) return false;
+    return in == KDA_BF16 && dk == 128 && dv == 128;
 }
 
 kda_variant resolve_variant(kda_variant v, int32_t dk, int32_t dv, kda_dtype in) {
     if (v != KDA_VARIANT_AUTO) return v;
-    return chunk_supported(dk, dv, in) ? KDA_VARIANT_CHUNK : KDA_VARIANT_RECURRENT;
+    return chunk_supported(KDA_VARIANT_CHUNK, dk, dv, in) ? KDA_VARIANT_CHUNK : KDA_VARIANT_RECURRENT;
 }
 
 size_t workspace_for(kda_variant v, int32_t B, int32_t T, int32_t H, int32_t N) {
-    (void)B;
-    (void)T;
-    (void)H;
-    (void)N;
-    (void)v;
+    if (v == KDA_VARIANT_CHUNK || v == KDA_VARIANT_CHUNK_SCAN)
+        return kda::chunk_workspace_bytes(B, T, H, N, v == KDA_VARIANT_CHUNK_SCAN);
     return 0;
 }
 
@@ -121,7 +117,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
 
     const kda_variant var = resolve_variant(variant, d_k, d_v, in_dtype);
     if ((var == KDA_VARIANT_CHUNK || var == KDA_VARIANT_CHUNK_SCAN) &&
-        !chunk_supported(d_k, d_v, in_dtype))
+        !chunk_supported(var, d_k, d_v, in_dtype))
         return KDA_ERR_UNSUPPORTED;
 
     for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(o),
@@ -178,6 +174,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     hipError_t e = hipErrorInvalidValue;
     switch (var) {
         case KDA_VARIANT_RECURRENT: e = kda::launch_recurrent(a); break;
+        case KDA_VARIANT_CHUNK: e = kda::launch_chunk(a, false); break;
         default: return KDA_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

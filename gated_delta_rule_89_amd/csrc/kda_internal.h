@@ -68,4 +68,8 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStrea
 hipError_t launch_recurrent(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 
+// Chunked MFMA prefill (bf16 inputs, d_k = d_v = 128).
+size_t chunk_workspace_bytes(int B, int T, int H, int N, bool scan);
+hipError_t launch_chunk(const PrefillArgs& a, bool scan);
+
 }  // namespace kda
