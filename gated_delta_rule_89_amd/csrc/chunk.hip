@@ -42,6 +42,10 @@
 namespace kda {
 namespace chunkk {
 
+#ifndef KDA_CHUNK_WG_PER_CU
+#define KDA_CHUNK_WG_PER_CU 1  // chains resident per CU (sets the register budget)
+#endif
+
 constexpr int C = 32;   // tokens per chunk
 constexpr int SB = 16;  // tokens per sub-block
 constexpr int D = 128;  // head size (d_k = d_v)
@@ -68,7 +72,8 @@ struct alignas(16) Smem {
     uint16_t v[C][QP];       // v tile (bf16 bits)            [token][column]
     float gp[2][6][SB][GP];  // Gram partial sums, one per channel half
     float x[2][SB][GP];      // (I + A_II)^-1 for the two diagonal blocks
-    float tot[2][D];         // per-channel sum of g over each sub-block
+    alignas(16) float a[2][SB][20];  // A_II^T: column m of Diag(beta) Gram in row m
+    float etot[2][D];        // per-channel exp(sum of g over each sub-block)
     float lam[D];            // Lambda_last = exp(Gamma over the chunk)
     float beta[C];
 };
@@ -95,10 +100,21 @@ __device__ __forceinline__ float row_scan16(float x) {
     return x;
 }
 
-__device__ __forceinline__ float wave_max(float m) {
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
-    return m;
+// Maximum of a non-negative value over the wave: prefix maxima inside each
+// 16-lane row, then across rows with the row broadcasts; lane 63 ends up with
+// the total, which is read back as a wave-uniform value.
+__device__ __forceinline__ float wave_max_nonneg(float m) {
+    m = fmaxf(m, row_shr<1>(m));
+    m = fmaxf(m, row_shr<2>(m));
+    m = fmaxf(m, row_shr<4>(m));
+    m = fmaxf(m, row_shr<8>(m));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0x142, 0xa, 0xf, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(m), __float_as_int(m), 0x143, 0xc, 0xf, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
+}
+
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ h8 cat(h4 a, h4 b) {
@@ -114,7 +130,7 @@ __device__ __forceinline__ void unpack_bf16x8(u4 w, float* out) {
 }
 
 template <typename Tout>
-__global__ __launch_bounds__(256, 2) void chunk_kernel(
+__global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, const float* __restrict__ h0,
@@ -143,8 +159,10 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * D * D;
     const int colw = 32 * w;  // first state column of this wave
 
-    // State: S[16 rt + 4 g4 + i][colw + 16 ct + r] in S[rt][ct][i].
+    // State, kept as S * 2^ex: S[16 rt + 4 g4 + i][colw + 16 ct + r] in S[rt][ct][i].
+    // ex is a per-wave exponent that keeps the fp16 copies of S and v in range.
     f4 S[8][2];
+    int ex = 0;
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -153,132 +171,137 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
             for (int i = 0; i < 4; ++i)
                 S[rt][ct][i] = h0 ? h0[sbase + (16 * rt + 4 * g4 + i) * D + colw + 16 * ct + r] : 0.f;
 
+    // Raw inputs of the next chunk, fetched one chunk ahead: k, q, g of this
+    // lane's token and channels (gate layout), its beta, and two 16-byte
+    // pieces of the v tile (staging layout).
+    const int tok = SB * I + r;
+    const int vt = tid >> 3, vc = (tid & 7) * 16;
+    u4 kw[2], qw[2], va, vb;
+    f4 ga[2], gb[2];
+    float bt;
+    auto fetch = [&](int64_t cs) {
+        const int vld = static_cast<int>(t1 - cs < C ? t1 - cs : C);
+        const bool in = tok < vld;
+        const int64_t rowq = ((cs + tok) * H + h) * D;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int ch = 64 * hh + 32 * ks + 8 * g4;
+            kw[ks] = u4{0, 0, 0, 0};
+            qw[ks] = u4{0, 0, 0, 0};
+            ga[ks] = f4{0.f, 0.f, 0.f, 0.f};
+            gb[ks] = f4{0.f, 0.f, 0.f, 0.f};
+            if (in) {
+                kw[ks] = *reinterpret_cast<const u4*>(k + rowq + ch);
+                qw[ks] = *reinterpret_cast<const u4*>(q + rowq + ch);
+                ga[ks] = *reinterpret_cast<const f4*>(g + rowq + ch);
+                gb[ks] = *reinterpret_cast<const f4*>(g + rowq + ch + 4);
+            }
+        }
+        bt = in ? beta[(cs + tok) * H + h] : 0.f;
+        va = u4{0, 0, 0, 0};
+        vb = u4{0, 0, 0, 0};
+        if (vt < vld) {
+            const uint16_t* src = v + ((cs + vt) * H + h) * D + vc;
+            va = *reinterpret_cast<const u4*>(src);
+            vb = *reinterpret_cast<const u4*>(src + 8);
+        }
+    };
+    if (t0 < t1) fetch(t0);
+
     for (int64_t c0 = t0; c0 < t1; c0 += C) {
         const int valid = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
 
         // ---------------- gate phase 1: loads, cumulative gates, diagonal Grams
-        const int tok = SB * I + r;
-        const bool in = tok < valid;
-        const int64_t rowq = ((c0 + tok) * H + h) * D;
-        float kf[16], qf[16], gl[16];
+        h8 l16[2], q16[2], rb16[2];  // L, Lq, k exp(tot - G) as fp16 (k-step ks, slot m)
+        {
+            f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ch = 64 * hh + 32 * ks + 8 * g4;
-            u4 kw = {0, 0, 0, 0}, qw = {0, 0, 0, 0};
-            f4 ga = {0.f, 0.f, 0.f, 0.f}, gb = {0.f, 0.f, 0.f, 0.f};
-            if (in) {
-                kw = *reinterpret_cast<const u4*>(k + rowq + ch);
-                qw = *reinterpret_cast<const u4*>(q + rowq + ch);
-                ga = *reinterpret_cast<const f4*>(g + rowq + ch);
-                gb = *reinterpret_cast<const f4*>(g + rowq + ch + 4);
+            for (int ks = 0; ks < 2; ++ks) {
+                const int ch = 64 * hh + 32 * ks + 8 * g4;
+                float kf[8], qf[8];
+                unpack_bf16x8(kw[ks], kf);
+                unpack_bf16x8(qw[ks], qf);
+                b8 lh, ll, qh, ql, rh, rl;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const float G = row_scan16(m < 4 ? ga[ks][m] : gb[ks][m - 4]);  // Gamma from the sub-block start
+                    const float e1 = gate_exp(G);            // <= 1
+                    const float e2 = gate_exp(-G);           // >= 1
+                    const float etot = __shfl(e1, 15, 16);   // exp(sum of g over the sub-block)
+                    const float L = kf[m] * e1, Lq = qf[m] * e1, R = kf[m] * e2;
+                    l16[ks][m] = static_cast<_Float16>(L);
+                    q16[ks][m] = static_cast<_Float16>(Lq);
+                    rb16[ks][m] = static_cast<_Float16>(R * etot);  // k exp(tot - G) <= 1
+                    if (r == 15) sm.etot[I][ch + m] = etot;
+                    lh[m] = static_cast<__bf16>(L);
+                    ll[m] = static_cast<__bf16>(L - static_cast<float>(lh[m]));
+                    qh[m] = static_cast<__bf16>(Lq);
+                    ql[m] = static_cast<__bf16>(Lq - static_cast<float>(qh[m]));
+                    rh[m] = static_cast<__bf16>(R);
+                    rl[m] = static_cast<__bf16>(R - static_cast<float>(rh[m]));
+                }
+                accA = mfmab(lh, rh, accA);
+                accA = mfmab(lh, rl, accA);
+                accA = mfmab(ll, rh, accA);
+                accP = mfmab(qh, rh, accP);
+                accP = mfmab(qh, rl, accP);
+                accP = mfmab(ql, rh, accP);
+                if (I == 0) *reinterpret_cast<h8*>(&sm.r0[r][ch]) = rb16[ks];
             }
-            unpack_bf16x8(kw, kf + 8 * ks);
-            unpack_bf16x8(qw, qf + 8 * ks);
+            // Row 4 g4 + i of the Gram tile is token 4 g4 + i of the sub-block: scale A by its beta.
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                gl[8 * ks + m] = ga[m];
-                gl[8 * ks + 4 + m] = gb[m];
+            for (int i = 0; i < 4; ++i) {
+                const float bi = __shfl(bt, (l & 48) | (4 * g4 + i));
+                sm.gp[hh][2 * I][4 * g4 + i][r] = accA[i] * bi;
+                sm.gp[hh][2 * I + 1][4 * g4 + i][r] = accP[i];
             }
-        }
-        float tot[16], L[16], Lq[16], Rb[16];
-        f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            b8 lh, ll, qh, ql, rh, rl;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int e = 8 * ks + m;
-                const float G = row_scan16(gl[e]);      // Gamma relative to the sub-block start
-                tot[e] = __shfl(G, 15, 16);             // sum over the sub-block
-                const float e1 = gate_exp(G);           // <= 1
-                const float e2 = gate_exp(-G);          // >= 1 (diagonal blocks only)
-                const float e3 = gate_exp(tot[e] - G);  // <= 1
-                L[e] = kf[e] * e1;
-                Lq[e] = qf[e] * e1;
-                Rb[e] = kf[e] * e3;
-                const float R = kf[e] * e2;
-                lh[m] = static_cast<__bf16>(L[e]);
-                ll[m] = static_cast<__bf16>(L[e] - static_cast<float>(lh[m]));
-                qh[m] = static_cast<__bf16>(Lq[e]);
-                ql[m] = static_cast<__bf16>(Lq[e] - static_cast<float>(qh[m]));
-                rh[m] = static_cast<__bf16>(R);
-                rl[m] = static_cast<__bf16>(R - static_cast<float>(rh[m]));
-            }
-            accA = mfmab(lh, rh, accA);
-            accA = mfmab(lh, rl, accA);
-            accA = mfmab(ll, rh, accA);
-            accP = mfmab(qh, rh, accP);
-            accP = mfmab(qh, rl, accP);
-            accP = mfmab(ql, rh, accP);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sm.gp[hh][2 * I][4 * g4 + i][r] = accA[i];
-            sm.gp[hh][2 * I + 1][4 * g4 + i][r] = accP[i];
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ch = 64 * hh + 32 * ks + 8 * g4;
-            if (I == 0) {
-                h8 rv;
-#pragma unroll
-                for (int m = 0; m < 8; ++m) rv[m] = static_cast<_Float16>(Rb[8 * ks + m]);
-                *reinterpret_cast<h8*>(&sm.r0[r][ch]) = rv;
-            }
-            if (r == 15) {
-#pragma unroll
-                for (int m = 0; m < 8; ++m) sm.tot[I][ch + m] = tot[8 * ks + m];
-            }
+            if (hh == 0 && g4 == 0) sm.beta[tok] = bt;
         }
         __syncthreads();  // B1
 
-        // ---------------- gate phase 2: chunk-referenced operands, cross-block Grams, v, beta
+        // ---------------- gate phase 2: chunk-referenced operands, cross-block Grams, v
         {
             f4 a10 = {0.f, 0.f, 0.f, 0.f}, p10 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int ch = 64 * hh + 32 * ks + 8 * g4;
-                h8 qv, l16, q16;
+                const f4 oa = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch]);
+                const f4 ob = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch + 4]);
+                h8 qv;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
-                    const int e = 8 * ks + m;
-                    const float t0c = sm.tot[0][ch + m], t1c = sm.tot[1][ch + m];
-                    const float base = I ? t0c : 0.f;                   // Gamma at the sub-block start
-                    const float fb = gate_exp(base);                    // <= 1
-                    const float fl = gate_exp(t0c + t1c - base - tot[e]);  // <= 1
-                    qv[m] = static_cast<_Float16>(Lq[e] * fb);
-                    sm.ktt[ch + m][tok] = static_cast<_Float16>(L[e] * fb);
-                    sm.kbt[ch + m][tok] = static_cast<_Float16>(Rb[e] * fl);
-                    if (I == 0 && r == 0) sm.lam[ch + m] = gate_exp(t0c + t1c);
-                    l16[m] = static_cast<_Float16>(L[e]);
-                    q16[m] = static_cast<_Float16>(Lq[e]);
+                    const float other = m < 4 ? oa[m] : ob[m - 4];  // exp(sum of g over the other sub-block)
+                    const float L = static_cast<float>(l16[ks][m]), Lq = static_cast<float>(q16[ks][m]);
+                    const float Rb = static_cast<float>(rb16[ks][m]);
+                    // sub-block 0: Gamma_r = G, K-bar needs exp(tot1); sub-block 1: Gamma_r = tot0 + G
+                    const float fq = I ? other : 1.f, fk = I ? 1.f : other;
+                    qv[m] = static_cast<_Float16>(Lq * fq);
+                    sm.ktt[ch + m][tok] = static_cast<_Float16>(L * fq);
+                    sm.kbt[ch + m][tok] = static_cast<_Float16>(Rb * fk);
                 }
                 *reinterpret_cast<h8*>(&sm.qt[tok][ch]) = qv;
                 if (I == 1) {
                     const h8 rv = *reinterpret_cast<const h8*>(&sm.r0[r][ch]);
-                    a10 = mfma16(l16, rv, a10);
-                    p10 = mfma16(q16, rv, p10);
+                    a10 = mfma16(l16[ks], rv, a10);
+                    p10 = mfma16(q16[ks], rv, p10);
                 }
             }
             if (I == 1) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    sm.gp[hh][GA10][4 * g4 + i][r] = a10[i];
+                    const float bi = sm.beta[SB + 4 * g4 + i];
+                    sm.gp[hh][GA10][4 * g4 + i][r] = a10[i] * bi;
                     sm.gp[hh][GP10][4 * g4 + i][r] = p10[i];
                 }
             }
-            if (tid < C) sm.beta[tid] = tid < valid ? beta[(c0 + tid) * H + h] : 0.f;
-            {
-                const int vt = tid >> 3, vc = (tid & 7) * 16;
-                u4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-                if (vt < valid) {
-                    const uint16_t* src = v + ((c0 + vt) * H + h) * D + vc;
-                    a = *reinterpret_cast<const u4*>(src);
-                    b = *reinterpret_cast<const u4*>(src + 8);
-                }
-                *reinterpret_cast<u4*>(&sm.v[vt][vc]) = a;
-                *reinterpret_cast<u4*>(&sm.v[vt][vc + 8]) = b;
+            if (tid < D) sm.lam[tid] = sm.etot[0][tid] * sm.etot[1][tid];
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const int e = tid + 256 * qq, J = e >> 8, i = (e >> 4) & 15, m = e & 15;
+                sm.a[J][m][i] = sm.gp[0][2 * J][i][m] + sm.gp[1][2 * J][i][m];  // stored by column
             }
+            *reinterpret_cast<u4*>(&sm.v[vt][vc]) = va;
+            *reinterpret_cast<u4*>(&sm.v[vt][vc + 8]) = vb;
         }
         __syncthreads();  // B2
 
@@ -286,15 +309,26 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
         if (w < 2) {
             const int J = w;  // diagonal block
             const int j = r;  // column of the inverse owned by this lane
+            // Column j of (I + A_JJ)^-1 by forward substitution, column-oriented:
+            // once x_m is final, every later row subtracts A[i][m] x_m (independent
+            // updates).  Columns of A are read one step ahead.
             float xcol[SB];
 #pragma unroll
-            for (int i = 0; i < SB; ++i) {
-                float s = (i == j) ? 1.f : 0.f;
-                const float bi = sm.beta[SB * J + i];
+            for (int i = 0; i < SB; ++i) xcol[i] = (i == j) ? 1.f : 0.f;
+            f4 col[4], ncol[4];
 #pragma unroll
-                for (int m = 0; m < i; ++m)
-                    s -= bi * (sm.gp[0][2 * J][i][m] + sm.gp[1][2 * J][i][m]) * xcol[m];
-                xcol[i] = s;
+            for (int c = 0; c < 4; ++c) col[c] = *reinterpret_cast<const f4*>(&sm.a[J][0][4 * c]);
+#pragma unroll
+            for (int m = 0; m < SB; ++m) {
+                if (m + 1 < SB) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) ncol[c] = *reinterpret_cast<const f4*>(&sm.a[J][m + 1][4 * c]);
+                }
+                const float xm = xcol[m];
+#pragma unroll
+                for (int i = m + 1; i < SB; ++i) xcol[i] = fmaf(-col[i >> 2][i & 3], xm, xcol[i]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) col[c] = ncol[c];
             }
             if (g4 == 0) {
                 const float bj = sm.beta[SB * J + j];
@@ -326,28 +360,84 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
         }
         __syncthreads();  // B3
 
-        // ---------------- solve: off-diagonal block X10 = -X11 A10 X00 (every wave: 4 columns)
-        {
-            const int i = r, j = 4 * w + g4;
-            const float bi = sm.beta[SB + i];
-            float y = 0.f;
+        // ---------------- solve: off-diagonal block X10 = -X11 (A10 X00), fp32 MFMA on wave 0
+        if (w == 0) {
+            f4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < SB; ++m)
-                y += bi * (sm.gp[0][GA10][i][m] + sm.gp[1][GA10][i][m]) * sm.x[0][m][j];
-            float x10 = 0.f;
+            for (int ks = 0; ks < 4; ++ks) {
+                const int m = 4 * ks + g4;
+                y = mfma4(sm.gp[0][GA10][r][m] + sm.gp[1][GA10][r][m], sm.x[0][m][r], y);
+            }
+            // y[i] = Y[4 g4 + i][r]; contract X11 Y with k index m = 4 g4 + ks
+            f4 x10 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < SB; ++m) x10 -= sm.x[1][i][m] * __shfl(y, (l & 48) | m);
-            sm.t[SB + i][j] = static_cast<_Float16>(x10 * sm.beta[j]);
+            for (int ks = 0; ks < 4; ++ks) x10 = mfma4(sm.x[1][r][4 * g4 + ks], y[ks], x10);
+            const float bj = sm.beta[r];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.t[SB + 4 * g4 + i][r] = static_cast<_Float16>(-x10[i] * bj);
         }
         __syncthreads();  // B4
 
         // ---------------- state pass on this wave's 32 columns
+        if (c0 + C < t1) fetch(c0 + C);
         {
-            // W^T = K~^T T^T, kept in registers as the A operand of W S.
+            // Exponent for this chunk from max(|S|, |v|) over the wave's columns.
+            float mv = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    mv = fmaxf(mv, fabsf(bf16_to_f32(sm.v[8 * g4 + m][colw + 16 * ct + r])));
+            float ms = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[rt][ct][i]));
+            const float mx = wave_max_nonneg(fmaxf(ms * ldexpf(1.f, -ex), mv));
+            int nex = ex;
+            if (mx > 0.f && mx < 3.0e38f) {
+                int e2;
+                (void)frexpf(mx, &e2);
+                nex = 10 - e2;
+                nex = nex < -120 ? -120 : (nex > 120 ? 120 : nex);
+            }
+            if (nex != ex) {  // wave-uniform
+                const float f = ldexpf(1.f, nex - ex);
+#pragma unroll
+                for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) S[rt][ct] *= f;
+                ex = nex;
+            }
+            const float sig = ldexpf(1.f, ex);
+
+            h8 s16[4][2];  // B operand of W S and Q~ S: [channel k-step][column tile]
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        s16[ks][ct][m] = static_cast<_Float16>(S[2 * ks][ct][m]);
+                        s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
+                    }
+
+            // Delta = T v - W S (scaled), W = T K~ built per channel k-step from K~^T T^T.
             h8 tf[2];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) tf[rt] = *reinterpret_cast<const h8*>(&sm.t[16 * rt + r][8 * g4]);
-            h8 wf[2][4];  // A operand of (-W) S: [token tile][channel k-step]
+            f4 dl[2][2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                h8 v16;
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    v16[m] = static_cast<_Float16>(bf16_to_f32(sm.v[8 * g4 + m][colw + 16 * ct + r]) * sig);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) dl[rt][ct] = mfma16(tf[rt], v16, f4{0.f, 0.f, 0.f, 0.f});
+            }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 f4 wa[2][2];
@@ -358,66 +448,17 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
                     for (int rt = 0; rt < 2; ++rt) wa[hx][rt] = mfma16(kt, tf[rt], f4{0.f, 0.f, 0.f, 0.f});
                 }
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < 2; ++rt) {
+                    h8 wf;
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        wf[rt][ks][m] = static_cast<_Float16>(-wa[0][rt][m]);
-                        wf[rt][ks][4 + m] = static_cast<_Float16>(-wa[1][rt][m]);
+                        wf[m] = static_cast<_Float16>(-wa[0][rt][m]);
+                        wf[4 + m] = static_cast<_Float16>(-wa[1][rt][m]);
                     }
-            }
-
-            // Value scale from max(|S|, |v|) over this wave's columns.
-            float vv[2][8];
-            float mx = 0.f;
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    vv[ct][m] = bf16_to_f32(sm.v[8 * g4 + m][colw + 16 * ct + r]);
-                    mx = fmaxf(mx, fabsf(vv[ct][m]));
+                    for (int ct = 0; ct < 2; ++ct) dl[rt][ct] = mfma16(wf, s16[ks][ct], dl[rt][ct]);
                 }
-#pragma unroll
-            for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(S[rt][ct][i]));
-            mx = wave_max(mx);
-            int ex = 0;
-            if (mx > 0.f && mx < 3.0e38f) {
-                (void)frexpf(mx, &ex);
-                ex = 10 - ex;
-                ex = ex < -120 ? -120 : (ex > 120 ? 120 : ex);
             }
-            const float sig = ldexpf(1.f, ex), isig = ldexpf(1.f, -ex);
-
-            h8 s16[4][2];  // B operand of W S and Q~ S: [channel k-step][column tile]
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        s16[ks][ct][m] = static_cast<_Float16>(S[2 * ks][ct][m] * sig);
-                        s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m] * sig);
-                    }
-            h8 v16[2];
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int m = 0; m < 8; ++m) v16[ct][m] = static_cast<_Float16>(vv[ct][m] * sig);
-
-            // Delta = T v - W S  (scaled by sig)
-            f4 dl[2][2];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    f4 a = mfma16(tf[rt], v16[ct], f4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) a = mfma16(wf[rt][ks], s16[ks][ct], a);
-                    dl[rt][ct] = a;
-                }
             h8 d16[2];  // B operand (k = tokens, permuted)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
@@ -428,6 +469,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
                 }
 
             // O = scale (Q~ S + P Delta)
+            const float os = scale * ldexpf(1.f, -ex);
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 h8 qf8[4];
@@ -442,39 +484,40 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(
                     f4 a = mfma16(pf, d16[ct], f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) a = mfma16(qf8[ks], s16[ks][ct], a);
-                    const float os = scale * isig;
+                    Tout* op = o + ((c0 + 16 * rt + 4 * g4) * H + h) * D + colw + 16 * ct + r;
+                    const int64_t stride = static_cast<int64_t>(H) * D;
+                    if (valid == C) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int tt = 16 * rt + 4 * g4 + i;
-                        if (tt < valid) st(o, ((c0 + tt) * H + h) * D + colw + 16 * ct + r, a[i] * os);
+                        for (int i = 0; i < 4; ++i) st(op, i * stride, a[i] * os);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (16 * rt + 4 * g4 + i < valid) st(op, i * stride, a[i] * os);
                     }
                 }
             }
 
-            // S <- Lambda_last S + K-bar^T Delta
+            // S <- Lambda_last S + K-bar^T Delta  (all in the scaled units)
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt) {
                 const f4 lam = *reinterpret_cast<const f4*>(&sm.lam[16 * rt + 4 * g4]);
                 const h8 kb = cat(*reinterpret_cast<const h4*>(&sm.kbt[16 * rt + r][4 * g4]),
                                   *reinterpret_cast<const h4*>(&sm.kbt[16 * rt + r][16 + 4 * g4]));
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    f4 a = S[rt][ct] * (lam * sig);
-                    a = mfma16(kb, d16[ct], a);
-                    S[rt][ct] = a * isig;
-                }
+                for (int ct = 0; ct < 2; ++ct) S[rt][ct] = mfma16(kb, d16[ct], S[rt][ct] * lam);
             }
         }
     }
 
     if (hT) {
+        const float un = ldexpf(1.f, -ex);
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    hT[sbase + (16 * rt + 4 * g4 + i) * D + colw + 16 * ct + r] = S[rt][ct][i];
+                    hT[sbase + (16 * rt + 4 * g4 + i) * D + colw + 16 * ct + r] = S[rt][ct][i] * un;
     }
 }
 
