@@ -40,7 +40,7 @@ def _load() -> ctypes.CDLL:
     lib.kda_abi_version.restype = ctypes.c_int
     lib.kda_status_str.argtypes = [ctypes.c_int]
     lib.kda_status_str.restype = ctypes.c_char_p
-    lib.kda_chunk_fwd_workspace_size.argtypes = [I32] * 6 + [ctypes.c_int, ctypes.c_int]
+    lib.kda_chunk_fwd_workspace_size.argtypes = [I32] * 6 + [P, ctypes.c_int, ctypes.c_int]
     lib.kda_chunk_fwd_workspace_size.restype = SZ
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P,
                                   I32, I32, I32, I32, I32, I32, ctypes.c_int, ctypes.c_int,
@@ -91,8 +91,11 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def workspace_size(B, T, H, dk, dv, N, in_dtype=torch.bfloat16, variant="auto") -> int:
-    return int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, N, _dt(in_dtype),
+def workspace_size(B, T, H, dk, dv, N, in_dtype=torch.bfloat16, variant="auto",
+                   cu_seqlens_host=None) -> int:
+    """Workspace bytes for these sizes; cu_seqlens_host is an int32 CPU tensor or None."""
+    ptr = None if cu_seqlens_host is None else ctypes.c_void_p(cu_seqlens_host.data_ptr())
+    return int(lib.kda_chunk_fwd_workspace_size(B, T, H, dk, dv, N, ptr, _dt(in_dtype),
                                                 VARIANTS[variant]))
 
 
@@ -102,10 +105,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               output_final_state: bool = True, out_dtype: torch.dtype = torch.float32,
               variant: str = "auto", o: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None):
+              workspace: Optional[torch.Tensor] = None,
+              cu_seqlens_host: Optional[torch.Tensor] = None):
     """kda_chunk_fwd on torch tensors.  q, k, g: [B, T, H, dk]; v: [B, T, H, dv];
     beta: [B, T, H]; initial_state [N, H, dk, dv] fp32 or None; cu_seqlens int32
-    [N+1] (device tensor, CPU tensor, numpy array or list) or None.
+    [N+1] (device tensor, CPU tensor, numpy array or list) or None.  A caller
+    holding both copies passes the device tensor as cu_seqlens and an int32 CPU
+    tensor as cu_seqlens_host, and no copy is made.
     Returns (o [B, T, H, dv], final_state [N, H, dk, dv] or None)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         _dev(t, name)
@@ -113,7 +119,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     dv = v.shape[-1]
     dev = q.device
     cu_dev = cu_host = None
-    if cu_seqlens is not None:
+    if cu_seqlens is not None and cu_seqlens_host is not None:
+        cu_dev, cu_host = cu_seqlens, cu_seqlens_host
+        _dev(cu_dev, "cu_seqlens")
+        if cu_host.is_cuda or cu_host.dtype != torch.int32 or not cu_host.is_contiguous():
+            raise ValueError("cu_seqlens_host must be a contiguous int32 CPU tensor")
+        N = cu_host.numel() - 1
+    elif cu_seqlens is not None:
         if isinstance(cu_seqlens, torch.Tensor):
             cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
             cu_dev = cu_seqlens if (cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32
@@ -132,7 +144,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
     if not output_final_state:
         final_state = None
-    ws_bytes = workspace_size(B, T, H, dk, dv, N, q.dtype, variant)
+    ws_bytes = workspace_size(B, T, H, dk, dv, N, q.dtype, variant, cu_host)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     code = lib.kda_chunk_fwd(

@@ -31,20 +31,53 @@ bool overlap(Range a, Range b) {
 }
 
 // The chunked kernels take bf16 q/k/v with d_k = d_v = 128.
-bool chunk_supported(kda_variant v, int32_t dk, int32_t dv, kda_dtype in) {
-    if (v == KDA_VARIANT_CHUNK_SCAN) return false;
+bool chunk_supported(int32_t dk, int32_t dv, kda_dtype in) {
     return in == KDA_BF16 && dk == 128 && dv == 128;
 }
 
-kda_variant resolve_variant(kda_variant v, int32_t dk, int32_t dv, kda_dtype in) {
-    if (v != KDA_VARIANT_AUTO) return v;
-    return chunk_supported(KDA_VARIANT_CHUNK, dk, dv, in) ? KDA_VARIANT_CHUNK : KDA_VARIANT_RECURRENT;
+// Compute units of the current device, cached per device id.
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
-size_t workspace_for(kda_variant v, int32_t B, int32_t T, int32_t H, int32_t N) {
+// AUTO: the chunked kernel, with the segment scan when the longest sequence
+// alone would take well over the average work per CU (one chain per
+// workgroup runs sequentially over its chunks).
+kda_variant resolve_variant(kda_variant v, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
+                            int32_t N, kda_dtype in, const int32_t* cu_host) {
+    if (v != KDA_VARIANT_AUTO) return v;
+    if (!chunk_supported(dk, dv, in)) return KDA_VARIANT_RECURRENT;
+    int64_t longest = 0, chunks = 0;
+    for (int32_t n = 0; n < N; ++n) {
+        const int64_t len = cu_host ? cu_host[n + 1] - cu_host[n] : T;
+        longest = len > longest ? len : longest;
+        chunks += (len + 31) / 32;
+    }
+    (void)B;
+    const int64_t per_cu = chunks * H / cu_count();
+    return (longest + 31) / 32 > 2 * per_cu + 16 ? KDA_VARIANT_CHUNK_SCAN : KDA_VARIANT_CHUNK;
+}
+
+size_t workspace_for(kda_variant v, int32_t B, int32_t T, int32_t H, int32_t N, const int32_t* cu_host) {
     if (v == KDA_VARIANT_CHUNK || v == KDA_VARIANT_CHUNK_SCAN)
-        return kda::chunk_workspace_bytes(B, T, H, N, v == KDA_VARIANT_CHUNK_SCAN);
+        return kda::chunk_workspace_bytes(B, T, H, N, cu_host, v == KDA_VARIANT_CHUNK_SCAN);
     return 0;
+}
+
+bool seqlens_ok(const int32_t* cu_host, int32_t N, int32_t T) {
+    if (cu_host[0] != 0 || cu_host[N] != T) return false;
+    for (int32_t i = 0; i < N; ++i)
+        if (cu_host[i + 1] < cu_host[i]) return false;
+    return true;
 }
 
 }  // namespace
@@ -70,11 +103,14 @@ const char* kda_status_str(kda_status s) {
 }
 
 size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                                    int32_t N, kda_dtype in_dtype, kda_variant variant) {
+                                    int32_t N, const int32_t* cu_seqlens_host, kda_dtype in_dtype,
+                                    kda_variant variant) {
     if (B < 0 || T < 0 || H < 0 || N < 0 || !head_size_ok(d_k) || !head_size_ok(d_v) ||
-        !dtype_ok(in_dtype))
+        !dtype_ok(in_dtype) || variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK_SCAN)
         return 0;
-    return workspace_for(resolve_variant(variant, d_k, d_v, in_dtype), B, T, H, N);
+    if (cu_seqlens_host ? (B != 1 || !seqlens_ok(cu_seqlens_host, N, T)) : N != B) return 0;
+    const kda_variant v = resolve_variant(variant, B, T, H, d_k, d_v, N, in_dtype, cu_seqlens_host);
+    return workspace_for(v, B, T, H, N, cu_seqlens_host);
 }
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
@@ -91,9 +127,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr)) return KDA_ERR_NULL;
     if (cu_seqlens) {
         if (B != 1) return KDA_ERR_SHAPE;
-        if (cu_seqlens_host[0] != 0 || cu_seqlens_host[N] != T) return KDA_ERR_SEQLENS;
-        for (int32_t i = 0; i < N; ++i)
-            if (cu_seqlens_host[i + 1] < cu_seqlens_host[i]) return KDA_ERR_SEQLENS;
+        if (!seqlens_ok(cu_seqlens_host, N, T)) return KDA_ERR_SEQLENS;
     } else if (N != B) {
         return KDA_ERR_SHAPE;
     }
@@ -115,9 +149,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL;
     if (static_cast<int64_t>(N) * H * 8 > INT32_MAX || H > 65535) return KDA_ERR_SHAPE;
 
-    const kda_variant var = resolve_variant(variant, d_k, d_v, in_dtype);
-    if ((var == KDA_VARIANT_CHUNK || var == KDA_VARIANT_CHUNK_SCAN) &&
-        !chunk_supported(var, d_k, d_v, in_dtype))
+    const kda_variant var = resolve_variant(variant, B, T, H, d_k, d_v, N, in_dtype, cu_seqlens_host);
+    if ((var == KDA_VARIANT_CHUNK || var == KDA_VARIANT_CHUNK_SCAN) && !chunk_supported(d_k, d_v, in_dtype))
         return KDA_ERR_UNSUPPORTED;
 
     for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(o),
@@ -127,7 +160,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if (!aligned(beta, 4) || !aligned(cu_seqlens, 4) || !aligned(workspace, 256))
         return KDA_ERR_ALIGN;
 
-    const size_t ws_need = workspace_for(var, B, T, H, N);
+    const size_t ws_need = workspace_for(var, B, T, H, N, cu_seqlens_host);
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
 
     const size_t th = static_cast<size_t>(tokens) * H;
@@ -175,6 +208,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     switch (var) {
         case KDA_VARIANT_RECURRENT: e = kda::launch_recurrent(a); break;
         case KDA_VARIANT_CHUNK: e = kda::launch_chunk(a, false); break;
+        case KDA_VARIANT_CHUNK_SCAN: e = kda::launch_chunk(a, true); break;
         default: return KDA_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

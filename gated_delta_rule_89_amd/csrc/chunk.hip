@@ -16,35 +16,54 @@
 //   S   <- Diag(Lambda_last) S + K-bar^T Delta,  K-bar = (Lambda_last / Lambda) k
 //
 // so one chunk maps S to (Diag(Lambda_last) - K-bar^T W) S + K-bar^T U: a
-// diagonal-plus-low-rank transition, the structure named on that page.
+// diagonal-plus-low-rank transition, the structure named on that page.  A run
+// of chunks therefore maps S_in to M S_in + B; "map" mode of the kernel below
+// computes (B, M) for a segment by running the same pass on the 128 x 256
+// state [B | M] from [0 | I] (v drives only the B half).
 //
 // Design on this GPU:
-//  * C = 32 tokens per chunk, split in two 16-token sub-blocks; a workgroup of
-//    4 waves owns one (sequence, head) chain; LDS use is ~63 KB so two chains
-//    share a CU.
+//  * C = 32 tokens per chunk, two 16-token sub-blocks; a workgroup of NW waves
+//    owns one chain segment (one sequence, one head).  Gate-side work (cumulative
+//    gates, Grams, the triangular solve) is split over the waves by sub-block
+//    and channel part; the state pass is split by state columns (columns of S
+//    are independent), 16 NCT columns per wave.
 //  * Gate exponents stay in range: inside a sub-block every factor is taken
 //    relative to the sub-block start, across sub-blocks relative to the end
 //    of the earlier one, so all factors are <= 1 except the in-block
 //    exp(-Gamma) of the diagonal Gram blocks.  Those two diagonal blocks run
 //    on split bf16 operands (hi + lo, three MFMAs) that keep fp32 range; every
-//    other product runs on fp16 MFMA with fp32 accumulation.
-//  * Columns of S are independent, so the state pass is split by columns:
-//    wave w owns d_v columns [32w, 32w+32) of S, U, Delta and O.  S lives in
-//    MFMA accumulators for the whole chain; its fp16 copy and Delta's are fed
-//    back as MFMA operands straight from the accumulator registers, using a
-//    k-order permutation that the gate-side operands read from LDS follow too.
+//    other product runs on fp16 MFMA with fp32 accumulation.  The kernel needs
+//    the sum of g over any 16 consecutive tokens of a channel to stay above
+//    about -85 (exp of the negated sum must be finite in fp32).
+//  * S lives in MFMA accumulators for the whole segment; its fp16 copy and
+//    Delta's are fed back as MFMA operands straight from the accumulator
+//    registers, using a k-order permutation that the gate-side operands read
+//    from LDS follow too.
 //  * Value-side fp16 operands (S, v, Delta) carry a per-wave power-of-two scale
 //    chosen every chunk from max(|S|, |v|), which keeps them inside fp16 range
 //    and away from subnormals; the scale is exact and is removed in fp32.
+//  * The next chunk's inputs are fetched into registers during the state pass.
 #include "dev_common.h"
 #include "kda_internal.h"
 
 namespace kda {
-namespace chunkk {
 
-#ifndef KDA_CHUNK_WG_PER_CU
-#define KDA_CHUNK_WG_PER_CU 1  // chains resident per CU (sets the register budget)
-#endif
+// One workgroup's work: tokens [t0, t1) of one sequence, for head blockIdx % H.
+struct ChunkItem {
+    int64_t t0, t1;
+    int32_t sin;   // initial state: >= 0 row of h0, <= -2 row (-sin - 2) of the staged states, -1 zero
+    int32_t sout;  // final state (or map slot in map mode): >= 0 row of the output, -1 none
+};
+
+// Scan over the segment maps of one sequence (all heads).
+struct ScanItem {
+    int32_t first_map;  // slot of the first segment's map
+    int32_t nmaps;      // number of maps (segments - 1)
+    int32_t h0;         // row of h0 or -1 for zero
+    int32_t first_seg;  // staged-state slot of the first segment
+};
+
+namespace chunkk {
 
 constexpr int C = 32;   // tokens per chunk
 constexpr int SB = 16;  // tokens per sub-block
@@ -62,6 +81,8 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 // Gram tiles: A00, P00, A11, P11, A10, P10.
 enum { GA00 = 0, GP00 = 1, GA11 = 2, GP11 = 3, GA10 = 4, GP10 = 5 };
 
+// Per-workgroup LDS; NP = channel parts per sub-block (one Gram partial each).
+template <int NP>
 struct alignas(16) Smem {
     _Float16 qt[C][QP];      // Q~ = Lambda q                 [token][channel]
     _Float16 kbt[D][TP];     // K-bar^T                       [channel][token]
@@ -70,9 +91,9 @@ struct alignas(16) Smem {
     _Float16 t[C][TP];       // T = (I + A)^-1 Diag(beta)     [token][token]
     _Float16 p[C][TP];       // P                             [token][token]
     uint16_t v[C][QP];       // v tile (bf16 bits)            [token][column]
-    float gp[2][6][SB][GP];  // Gram partial sums, one per channel half
+    float gp[NP][6][SB][GP]; // Gram partial sums, one per channel part
     float x[2][SB][GP];      // (I + A_II)^-1 for the two diagonal blocks
-    alignas(16) float a[2][SB][20];  // A_II^T: column m of Diag(beta) Gram in row m
+    float a[2][SB][20];      // A_II^T: column m of Diag(beta) Gram in row m
     float etot[2][D];        // per-channel exp(sum of g over each sub-block)
     float lam[D];            // Lambda_last = exp(Gamma over the chunk)
     float beta[C];
@@ -83,6 +104,9 @@ __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
 }
 __device__ __forceinline__ f4 mfmab(b8 a, b8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // Value of lane i - n of the same 16-lane DPP row (0 for i < n).
@@ -113,10 +137,6 @@ __device__ __forceinline__ float wave_max_nonneg(float m) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
 }
 
-__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ h8 cat(h4 a, h4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -129,81 +149,111 @@ __device__ __forceinline__ void unpack_bf16x8(u4 w, float* out) {
     }
 }
 
-template <typename Tout>
-__global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
+// Exponent e with max(|S|, |v|) * 2^e in [2^9, 2^10): the fp16 copies of the
+// value-side operands then stay far from both ends of the fp16 range.
+__device__ __forceinline__ int value_exponent(float mx, int ex) {
+    if (!(mx > 0.f) || !(mx < 3.0e38f)) return ex;
+    int e2;
+    (void)frexpf(mx, &e2);
+    const int e = 10 - e2;
+    return e < -120 ? -120 : (e > 120 ? 120 : e);
+}
+
+// NW waves; each owns NCT 16-column tiles of the state.  Full mode: state = S
+// (NW * 16 NCT = 128 columns), writes o and the final state.  Map mode: state
+// = [B | M] (256 columns), no o, writes the segment's (B, M).
+template <int NW, int NCT, bool MAP, typename Tout>
+__global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
-    const float* __restrict__ beta, float scale, const float* __restrict__ h0,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ perm, int T, int H,
-    Tout* __restrict__ o, float* __restrict__ hT) {
-    __shared__ Smem sm;
+    const float* __restrict__ beta, float scale, const ChunkItem* __restrict__ items, int H,
+    const float* __restrict__ h0, const float* __restrict__ staged, Tout* __restrict__ o,
+    float* __restrict__ out_state) {
+    constexpr int NP = NW / 2;      // channel parts per sub-block
+    constexpr int CPG = D / NP;     // channels per gate wave
+    constexpr int KS = CPG / 32;    // 32-channel k-steps per gate wave
+    constexpr int CPW = 16 * NCT;   // state columns per wave
+    constexpr int NT = NW * 64;     // threads
+    constexpr int VU = (C * D / 8) / NT;  // 16-byte pieces of the v tile per thread
+    static_assert(KS >= 1 && VU >= 1, "unsupported wave count");
+    static_assert(MAP ? NW * CPW == 2 * D : NW * CPW == D, "state columns must match the mode");
+    __shared__ Smem<NP> sm;
+
     const int tid = threadIdx.x;
     const int w = tid >> 6;      // wave
     const int l = tid & 63;      // lane
     const int r = l & 15;        // MFMA row / column index
     const int g4 = l >> 4;       // MFMA k group
-    const int I = w >> 1;        // gate phase: sub-block of this wave
-    const int hh = w & 1;        // gate phase: channel half of this wave
+    const int I = w / NP;        // gate phase: sub-block of this wave
+    const int part = w % NP;     // gate phase: channel part of this wave
 
-    const int rank = blockIdx.x / H;
-    const int h = blockIdx.x - rank * H;
-    const int n = perm ? perm[rank] : rank;
-    int64_t t0, t1;
-    if (cu) {
-        t0 = cu[n];
-        t1 = cu[n + 1];
-    } else {
-        t0 = static_cast<int64_t>(n) * T;
-        t1 = t0 + T;
-    }
-    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * D * D;
-    const int colw = 32 * w;  // first state column of this wave
+    const ChunkItem it = items[blockIdx.x / H];
+    const int h = blockIdx.x % H;
+    const int64_t t0 = it.t0, t1 = it.t1;
+    const int colg = CPW * w;            // first state column (of 256 in map mode)
+    const bool mhalf = MAP && colg >= D; // this wave propagates M (no v)
+    const int col = colg & (D - 1);      // column inside S, B or M
 
-    // State, kept as S * 2^ex: S[16 rt + 4 g4 + i][colw + 16 ct + r] in S[rt][ct][i].
-    // ex is a per-wave exponent that keeps the fp16 copies of S and v in range.
-    f4 S[8][2];
+    // State, kept as S * 2^ex: S[16 rt + 4 g4 + i][col + 16 ct + r] in S[rt][ct][i].
+    f4 S[8][NCT];
     int ex = 0;
+    {
+        const float* src = nullptr;
+        if (!MAP) {
+            if (it.sin >= 0 && h0) src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
+            else if (it.sin <= -2) src = staged + (static_cast<int64_t>(-it.sin - 2) * H + h) * D * D;
+        }
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+        for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[rt][ct][i] = h0 ? h0[sbase + (16 * rt + 4 * g4 + i) * D + colw + 16 * ct + r] : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * rt + 4 * g4 + i, cc = col + 16 * ct + r;
+                    S[rt][ct][i] = (mhalf && row == cc) ? 1.f : 0.f;
+                }
+        if (src) {
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
+        }
+    }
 
     // Raw inputs of the next chunk, fetched one chunk ahead: k, q, g of this
-    // lane's token and channels (gate layout), its beta, and two 16-byte
-    // pieces of the v tile (staging layout).
+    // lane's token and channels (gate layout), its beta, and pieces of the v
+    // tile (staging layout).
     const int tok = SB * I + r;
-    const int vt = tid >> 3, vc = (tid & 7) * 16;
-    u4 kw[2], qw[2], va, vb;
-    f4 ga[2], gb[2];
+    u4 kw[KS], qw[KS], vp[VU];
+    f4 ga[KS], gb[KS];
     float bt;
     auto fetch = [&](int64_t cs) {
         const int vld = static_cast<int>(t1 - cs < C ? t1 - cs : C);
         const bool in = tok < vld;
         const int64_t rowq = ((cs + tok) * H + h) * D;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ch = 64 * hh + 32 * ks + 8 * g4;
+        for (int ks = 0; ks < KS; ++ks) {
+            const int ch = CPG * part + 32 * ks + 8 * g4;
             kw[ks] = u4{0, 0, 0, 0};
             qw[ks] = u4{0, 0, 0, 0};
             ga[ks] = f4{0.f, 0.f, 0.f, 0.f};
             gb[ks] = f4{0.f, 0.f, 0.f, 0.f};
             if (in) {
                 kw[ks] = *reinterpret_cast<const u4*>(k + rowq + ch);
-                qw[ks] = *reinterpret_cast<const u4*>(q + rowq + ch);
+                if (!MAP) qw[ks] = *reinterpret_cast<const u4*>(q + rowq + ch);
                 ga[ks] = *reinterpret_cast<const f4*>(g + rowq + ch);
                 gb[ks] = *reinterpret_cast<const f4*>(g + rowq + ch + 4);
             }
         }
         bt = in ? beta[(cs + tok) * H + h] : 0.f;
-        va = u4{0, 0, 0, 0};
-        vb = u4{0, 0, 0, 0};
-        if (vt < vld) {
-            const uint16_t* src = v + ((cs + vt) * H + h) * D + vc;
-            va = *reinterpret_cast<const u4*>(src);
-            vb = *reinterpret_cast<const u4*>(src + 8);
+#pragma unroll
+        for (int j = 0; j < VU; ++j) {
+            const int e = tid + NT * j, vt = e >> 4, vc = (e & 15) * 8;
+            vp[j] = u4{0, 0, 0, 0};
+            if (vt < vld) vp[j] = *reinterpret_cast<const u4*>(v + ((cs + vt) * H + h) * D + vc);
         }
     };
     if (t0 < t1) fetch(t0);
@@ -211,13 +261,13 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
     for (int64_t c0 = t0; c0 < t1; c0 += C) {
         const int valid = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
 
-        // ---------------- gate phase 1: loads, cumulative gates, diagonal Grams
-        h8 l16[2], q16[2], rb16[2];  // L, Lq, k exp(tot - G) as fp16 (k-step ks, slot m)
+        // ---------------- gate phase 1: cumulative gates, diagonal Grams
+        h8 l16[KS], q16[KS], rb16[KS];  // L, Lq, k exp(tot - G) as fp16 (k-step ks, slot m)
         {
             f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int ch = 64 * hh + 32 * ks + 8 * g4;
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ch = CPG * part + 32 * ks + 8 * g4;
                 float kf[8], qf[8];
                 unpack_bf16x8(kw[ks], kf);
                 unpack_bf16x8(qw[ks], qf);
@@ -228,34 +278,39 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
                     const float e1 = gate_exp(G);            // <= 1
                     const float e2 = gate_exp(-G);           // >= 1
                     const float etot = __shfl(e1, 15, 16);   // exp(sum of g over the sub-block)
-                    const float L = kf[m] * e1, Lq = qf[m] * e1, R = kf[m] * e2;
+                    const float L = kf[m] * e1, R = kf[m] * e2;
                     l16[ks][m] = static_cast<_Float16>(L);
-                    q16[ks][m] = static_cast<_Float16>(Lq);
                     rb16[ks][m] = static_cast<_Float16>(R * etot);  // k exp(tot - G) <= 1
                     if (r == 15) sm.etot[I][ch + m] = etot;
                     lh[m] = static_cast<__bf16>(L);
                     ll[m] = static_cast<__bf16>(L - static_cast<float>(lh[m]));
-                    qh[m] = static_cast<__bf16>(Lq);
-                    ql[m] = static_cast<__bf16>(Lq - static_cast<float>(qh[m]));
                     rh[m] = static_cast<__bf16>(R);
                     rl[m] = static_cast<__bf16>(R - static_cast<float>(rh[m]));
+                    if (!MAP) {
+                        const float Lq = qf[m] * e1;
+                        q16[ks][m] = static_cast<_Float16>(Lq);
+                        qh[m] = static_cast<__bf16>(Lq);
+                        ql[m] = static_cast<__bf16>(Lq - static_cast<float>(qh[m]));
+                    }
                 }
                 accA = mfmab(lh, rh, accA);
                 accA = mfmab(lh, rl, accA);
                 accA = mfmab(ll, rh, accA);
-                accP = mfmab(qh, rh, accP);
-                accP = mfmab(qh, rl, accP);
-                accP = mfmab(ql, rh, accP);
+                if (!MAP) {
+                    accP = mfmab(qh, rh, accP);
+                    accP = mfmab(qh, rl, accP);
+                    accP = mfmab(ql, rh, accP);
+                }
                 if (I == 0) *reinterpret_cast<h8*>(&sm.r0[r][ch]) = rb16[ks];
             }
             // Row 4 g4 + i of the Gram tile is token 4 g4 + i of the sub-block: scale A by its beta.
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float bi = __shfl(bt, (l & 48) | (4 * g4 + i));
-                sm.gp[hh][2 * I][4 * g4 + i][r] = accA[i] * bi;
-                sm.gp[hh][2 * I + 1][4 * g4 + i][r] = accP[i];
+                sm.gp[part][2 * I][4 * g4 + i][r] = accA[i] * bi;
+                if (!MAP) sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
             }
-            if (hh == 0 && g4 == 0) sm.beta[tok] = bt;
+            if (part == 0 && g4 == 0) sm.beta[tok] = bt;
         }
         __syncthreads();  // B1
 
@@ -263,49 +318,51 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
         {
             f4 a10 = {0.f, 0.f, 0.f, 0.f}, p10 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int ch = 64 * hh + 32 * ks + 8 * g4;
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ch = CPG * part + 32 * ks + 8 * g4;
                 const f4 oa = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch]);
                 const f4 ob = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch + 4]);
                 h8 qv;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
                     const float other = m < 4 ? oa[m] : ob[m - 4];  // exp(sum of g over the other sub-block)
-                    const float L = static_cast<float>(l16[ks][m]), Lq = static_cast<float>(q16[ks][m]);
-                    const float Rb = static_cast<float>(rb16[ks][m]);
                     // sub-block 0: Gamma_r = G, K-bar needs exp(tot1); sub-block 1: Gamma_r = tot0 + G
                     const float fq = I ? other : 1.f, fk = I ? 1.f : other;
-                    qv[m] = static_cast<_Float16>(Lq * fq);
-                    sm.ktt[ch + m][tok] = static_cast<_Float16>(L * fq);
-                    sm.kbt[ch + m][tok] = static_cast<_Float16>(Rb * fk);
+                    sm.ktt[ch + m][tok] = static_cast<_Float16>(static_cast<float>(l16[ks][m]) * fq);
+                    sm.kbt[ch + m][tok] = static_cast<_Float16>(static_cast<float>(rb16[ks][m]) * fk);
+                    if (!MAP) qv[m] = static_cast<_Float16>(static_cast<float>(q16[ks][m]) * fq);
                 }
-                *reinterpret_cast<h8*>(&sm.qt[tok][ch]) = qv;
+                if (!MAP) *reinterpret_cast<h8*>(&sm.qt[tok][ch]) = qv;
                 if (I == 1) {
                     const h8 rv = *reinterpret_cast<const h8*>(&sm.r0[r][ch]);
                     a10 = mfma16(l16[ks], rv, a10);
-                    p10 = mfma16(q16[ks], rv, p10);
+                    if (!MAP) p10 = mfma16(q16[ks], rv, p10);
                 }
             }
             if (I == 1) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float bi = sm.beta[SB + 4 * g4 + i];
-                    sm.gp[hh][GA10][4 * g4 + i][r] = a10[i] * bi;
-                    sm.gp[hh][GP10][4 * g4 + i][r] = p10[i];
+                    sm.gp[part][GA10][4 * g4 + i][r] = a10[i] * sm.beta[SB + 4 * g4 + i];
+                    if (!MAP) sm.gp[part][GP10][4 * g4 + i][r] = p10[i];
                 }
             }
             if (tid < D) sm.lam[tid] = sm.etot[0][tid] * sm.etot[1][tid];
+            for (int e = tid; e < 2 * SB * SB; e += NT) {
+                const int J = e >> 8, i = (e >> 4) & 15, m = e & 15;
+                float s = 0.f;
 #pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-                const int e = tid + 256 * qq, J = e >> 8, i = (e >> 4) & 15, m = e & 15;
-                sm.a[J][m][i] = sm.gp[0][2 * J][i][m] + sm.gp[1][2 * J][i][m];  // stored by column
+                for (int pp = 0; pp < NP; ++pp) s += sm.gp[pp][2 * J][i][m];
+                sm.a[J][m][i] = s;  // stored by column
             }
-            *reinterpret_cast<u4*>(&sm.v[vt][vc]) = va;
-            *reinterpret_cast<u4*>(&sm.v[vt][vc + 8]) = vb;
+#pragma unroll
+            for (int j = 0; j < VU; ++j) {
+                const int e = tid + NT * j, vt = e >> 4, vc = (e & 15) * 8;
+                *reinterpret_cast<u4*>(&sm.v[vt][vc]) = vp[j];
+            }
         }
         __syncthreads();  // B2
 
-        // ---------------- solve: diagonal block inverses (waves 0, 1), P (waves 2, 3)
+        // ---------------- solve: diagonal block inverses (waves 0, 1), P and zero fill (others)
         if (w < 2) {
             const int J = w;  // diagonal block
             const int j = r;  // column of the inverse owned by this lane
@@ -315,20 +372,20 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
             float xcol[SB];
 #pragma unroll
             for (int i = 0; i < SB; ++i) xcol[i] = (i == j) ? 1.f : 0.f;
-            f4 col[4], ncol[4];
+            f4 cl[4], ncl[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) col[c] = *reinterpret_cast<const f4*>(&sm.a[J][0][4 * c]);
+            for (int c = 0; c < 4; ++c) cl[c] = *reinterpret_cast<const f4*>(&sm.a[J][0][4 * c]);
 #pragma unroll
             for (int m = 0; m < SB; ++m) {
                 if (m + 1 < SB) {
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) ncol[c] = *reinterpret_cast<const f4*>(&sm.a[J][m + 1][4 * c]);
+                    for (int c = 0; c < 4; ++c) ncl[c] = *reinterpret_cast<const f4*>(&sm.a[J][m + 1][4 * c]);
                 }
                 const float xm = xcol[m];
 #pragma unroll
-                for (int i = m + 1; i < SB; ++i) xcol[i] = fmaf(-col[i >> 2][i & 3], xm, xcol[i]);
+                for (int i = m + 1; i < SB; ++i) xcol[i] = fmaf(-cl[i >> 2][i & 3], xm, xcol[i]);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) col[c] = ncol[c];
+                for (int c = 0; c < 4; ++c) cl[c] = ncl[c];
             }
             if (g4 == 0) {
                 const float bj = sm.beta[SB * J + j];
@@ -340,23 +397,21 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
             }
         } else {
             const int t2 = tid - 128;
+            constexpr int NT2 = NT - 128;
+            if (!MAP) {
+                for (int e = t2; e < C * C; e += NT2) {
+                    const int R = e >> 5, Cc = e & 31;
+                    float val = 0.f;
+                    if (Cc <= R) {
+                        const int tile = R < SB ? GP00 : (Cc >= SB ? GP11 : GP10);
+                        const int rr = R & 15, cc = Cc & 15;
 #pragma unroll
-            for (int qq = 0; qq < 8; ++qq) {
-                const int e = t2 + 128 * qq;
-                const int R = e >> 5, Cc = e & 31;
-                float val = 0.f;
-                if (Cc <= R) {
-                    if (R < SB) val = sm.gp[0][GP00][R][Cc] + sm.gp[1][GP00][R][Cc];
-                    else if (Cc >= SB) val = sm.gp[0][GP11][R - SB][Cc - SB] + sm.gp[1][GP11][R - SB][Cc - SB];
-                    else val = sm.gp[0][GP10][R - SB][Cc] + sm.gp[1][GP10][R - SB][Cc];
+                        for (int pp = 0; pp < NP; ++pp) val += sm.gp[pp][tile][rr][cc];
+                    }
+                    sm.p[R][Cc] = static_cast<_Float16>(val);
                 }
-                sm.p[R][Cc] = static_cast<_Float16>(val);
             }
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-                const int e = t2 + 128 * qq;
-                sm.t[e >> 4][SB + (e & 15)] = static_cast<_Float16>(0.f);
-            }
+            for (int e = t2; e < SB * SB; e += NT2) sm.t[e >> 4][SB + (e & 15)] = static_cast<_Float16>(0.f);
         }
         __syncthreads();  // B3
 
@@ -366,7 +421,10 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int m = 4 * ks + g4;
-                y = mfma4(sm.gp[0][GA10][r][m] + sm.gp[1][GA10][r][m], sm.x[0][m][r], y);
+                float a = 0.f;
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) a += sm.gp[pp][GA10][r][m];
+                y = mfma4(a, sm.x[0][m][r], y);
             }
             // y[i] = Y[4 g4 + i][r]; contract X11 Y with k index m = 4 g4 + ks
             f4 x10 = {0.f, 0.f, 0.f, 0.f};
@@ -378,46 +436,41 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
         }
         __syncthreads();  // B4
 
-        // ---------------- state pass on this wave's 32 columns
+        // ---------------- state pass on this wave's columns
         if (c0 + C < t1) fetch(c0 + C);
         {
             // Exponent for this chunk from max(|S|, |v|) over the wave's columns.
             float mv = 0.f;
+            if (!mhalf) {
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                for (int m = 0; m < 8; ++m)
-                    mv = fmaxf(mv, fabsf(bf16_to_f32(sm.v[8 * g4 + m][colw + 16 * ct + r])));
+                    for (int m = 0; m < 8; ++m)
+                        mv = fmaxf(mv, fabsf(bf16_to_f32(sm.v[8 * g4 + m][col + 16 * ct + r])));
+            }
             float ms = 0.f;
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[rt][ct][i]));
-            const float mx = wave_max_nonneg(fmaxf(ms * ldexpf(1.f, -ex), mv));
-            int nex = ex;
-            if (mx > 0.f && mx < 3.0e38f) {
-                int e2;
-                (void)frexpf(mx, &e2);
-                nex = 10 - e2;
-                nex = nex < -120 ? -120 : (nex > 120 ? 120 : nex);
-            }
+            const int nex = value_exponent(wave_max_nonneg(fmaxf(ms * ldexpf(1.f, -ex), mv)), ex);
             if (nex != ex) {  // wave-uniform
                 const float f = ldexpf(1.f, nex - ex);
 #pragma unroll
                 for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) S[rt][ct] *= f;
+                    for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= f;
                 ex = nex;
             }
             const float sig = ldexpf(1.f, ex);
 
-            h8 s16[4][2];  // B operand of W S and Q~ S: [channel k-step][column tile]
+            h8 s16[4][NCT];  // B operand of W S and Q~ S: [channel k-step][column tile]
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+                for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         s16[ks][ct][m] = static_cast<_Float16>(S[2 * ks][ct][m]);
@@ -428,15 +481,20 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
             h8 tf[2];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) tf[rt] = *reinterpret_cast<const h8*>(&sm.t[16 * rt + r][8 * g4]);
-            f4 dl[2][2];
+            f4 dl[2][NCT];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                h8 v16;
+            for (int ct = 0; ct < NCT; ++ct) {
+                if (mhalf) {
 #pragma unroll
-                for (int m = 0; m < 8; ++m)
-                    v16[m] = static_cast<_Float16>(bf16_to_f32(sm.v[8 * g4 + m][colw + 16 * ct + r]) * sig);
+                    for (int rt = 0; rt < 2; ++rt) dl[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+                } else {
+                    h8 v16;
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) dl[rt][ct] = mfma16(tf[rt], v16, f4{0.f, 0.f, 0.f, 0.f});
+                    for (int m = 0; m < 8; ++m)
+                        v16[m] = static_cast<_Float16>(bf16_to_f32(sm.v[8 * g4 + m][col + 16 * ct + r]) * sig);
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) dl[rt][ct] = mfma16(tf[rt], v16, f4{0.f, 0.f, 0.f, 0.f});
+                }
             }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
@@ -456,12 +514,12 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
                         wf[4 + m] = static_cast<_Float16>(-wa[1][rt][m]);
                     }
 #pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) dl[rt][ct] = mfma16(wf, s16[ks][ct], dl[rt][ct]);
+                    for (int ct = 0; ct < NCT; ++ct) dl[rt][ct] = mfma16(wf, s16[ks][ct], dl[rt][ct]);
                 }
             }
-            h8 d16[2];  // B operand (k = tokens, permuted)
+            h8 d16[NCT];  // B operand (k = tokens, permuted)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     d16[ct][m] = static_cast<_Float16>(dl[0][ct][m]);
@@ -469,30 +527,32 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
                 }
 
             // O = scale (Q~ S + P Delta)
-            const float os = scale * ldexpf(1.f, -ex);
+            if (!MAP) {
+                const float os = scale * ldexpf(1.f, -ex);
+                const int64_t stride = static_cast<int64_t>(H) * D;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                h8 qf8[4];
+                for (int rt = 0; rt < 2; ++rt) {
+                    h8 qf8[4];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    qf8[ks] = cat(*reinterpret_cast<const h4*>(&sm.qt[16 * rt + r][32 * ks + 4 * g4]),
-                                  *reinterpret_cast<const h4*>(&sm.qt[16 * rt + r][32 * ks + 16 + 4 * g4]));
-                const h8 pf = cat(*reinterpret_cast<const h4*>(&sm.p[16 * rt + r][4 * g4]),
-                                  *reinterpret_cast<const h4*>(&sm.p[16 * rt + r][16 + 4 * g4]));
+                    for (int ks = 0; ks < 4; ++ks)
+                        qf8[ks] = cat(*reinterpret_cast<const h4*>(&sm.qt[16 * rt + r][32 * ks + 4 * g4]),
+                                      *reinterpret_cast<const h4*>(&sm.qt[16 * rt + r][32 * ks + 16 + 4 * g4]));
+                    const h8 pf = cat(*reinterpret_cast<const h4*>(&sm.p[16 * rt + r][4 * g4]),
+                                      *reinterpret_cast<const h4*>(&sm.p[16 * rt + r][16 + 4 * g4]));
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    f4 a = mfma16(pf, d16[ct], f4{0.f, 0.f, 0.f, 0.f});
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        f4 a = mfma16(pf, d16[ct], f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) a = mfma16(qf8[ks], s16[ks][ct], a);
-                    Tout* op = o + ((c0 + 16 * rt + 4 * g4) * H + h) * D + colw + 16 * ct + r;
-                    const int64_t stride = static_cast<int64_t>(H) * D;
-                    if (valid == C) {
+                        for (int ks = 0; ks < 4; ++ks) a = mfma16(qf8[ks], s16[ks][ct], a);
+                        Tout* op = o + ((c0 + 16 * rt + 4 * g4) * H + h) * D + col + 16 * ct + r;
+                        if (valid == C) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) st(op, i * stride, a[i] * os);
-                    } else {
+                            for (int i = 0; i < 4; ++i) st(op, i * stride, a[i] * os);
+                        } else {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (16 * rt + 4 * g4 + i < valid) st(op, i * stride, a[i] * os);
+                            for (int i = 0; i < 4; ++i)
+                                if (16 * rt + 4 * g4 + i < valid) st(op, i * stride, a[i] * os);
+                        }
                     }
                 }
             }
@@ -504,71 +564,286 @@ __global__ __launch_bounds__(256, KDA_CHUNK_WG_PER_CU) void chunk_kernel(
                 const h8 kb = cat(*reinterpret_cast<const h4*>(&sm.kbt[16 * rt + r][4 * g4]),
                                   *reinterpret_cast<const h4*>(&sm.kbt[16 * rt + r][16 + 4 * g4]));
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) S[rt][ct] = mfma16(kb, d16[ct], S[rt][ct] * lam);
+                for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb, d16[ct], S[rt][ct] * lam);
             }
         }
     }
 
-    if (hT) {
+    // Final state (full mode) or this segment's (B, M) (map mode, rows of 256).
+    if (it.sout >= 0 && out_state) {
         const float un = ldexpf(1.f, -ex);
+        constexpr int64_t ld = MAP ? 2 * D : D;
+        float* dst = out_state + (static_cast<int64_t>(it.sout) * H + h) * D * ld;
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dst[(16 * rt + 4 * g4 + i) * ld + colg + 16 * ct + r] = S[rt][ct][i] * un;
+    }
+}
+
+// Initial states of every segment, staged in the workspace: S_0 = h0 (or
+// zero) and S_{j+1} = M_j S_j + B_j along each sequence, for every head.
+// Staging S_0 too means the segment pass never reads the caller's initial
+// state, so an in-place final state cannot race with it.  One workgroup of 4 waves per
+// (sequence, head); wave w owns state columns [32 w, 32 w + 32).  The 128 x 128
+// products run on split bf16 MFMA (hi + lo on both operands, three products),
+// which keeps about 16 significant bits per operand; accumulation is fp32.
+__global__ __launch_bounds__(256, 1) void segment_scan_kernel(
+    const ScanItem* __restrict__ sitems, int H, const float* __restrict__ h0,
+    const float* __restrict__ maps, float* __restrict__ staged) {
+    const ScanItem it = sitems[blockIdx.x / H];
+    const int h = blockIdx.x % H;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g4 = l >> 4;
+    const int col = 32 * w;
+    f4 S[8][2];
+    const float* src = (it.h0 >= 0 && h0) ? h0 + (static_cast<int64_t>(it.h0) * H + h) * D * D : nullptr;
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[rt][ct][i] = src ? src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] : 0.f;
+    auto stage = [&](int slot) {
+        float* dst = staged + (static_cast<int64_t>(slot) * H + h) * D * D;
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    hT[sbase + (16 * rt + 4 * g4 + i) * D + colw + 16 * ct + r] = S[rt][ct][i] * un;
+                for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] = S[rt][ct][i];
+    };
+    stage(it.first_seg);
+
+    for (int j = 0; j < it.nmaps; ++j) {
+        const float* mp = maps + (static_cast<int64_t>(it.first_map + j) * H + h) * D * (2 * D);
+        // B operands from S (k = rows of S, permuted as in the chunk kernel), split hi/lo.
+        b8 sh[4][2], sl[4][2];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const float x = m < 4 ? S[2 * ks][ct][m] : S[2 * ks + 1][ct][m - 4];
+                    sh[ks][ct][m] = static_cast<__bf16>(x);
+                    sl[ks][ct][m] = static_cast<__bf16>(x - static_cast<float>(sh[ks][ct][m]));
+                }
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt) {
+            f4 acc[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[ct][i] = mp[(16 * rt + 4 * g4 + i) * (2 * D) + col + 16 * ct + r];
+            const float* mrow = mp + (16 * rt + r) * (2 * D) + D;  // row of M
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const f4 lo4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 4 * g4);
+                const f4 hi4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 16 + 4 * g4);
+                b8 ah, al;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    const float x = m < 4 ? lo4[m] : hi4[m - 4];
+                    ah[m] = static_cast<__bf16>(x);
+                    al[m] = static_cast<__bf16>(x - static_cast<float>(ah[m]));
+                }
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    acc[ct] = mfmab(ah, sh[ks][ct], acc[ct]);
+                    acc[ct] = mfmab(ah, sl[ks][ct], acc[ct]);
+                    acc[ct] = mfmab(al, sh[ks][ct], acc[ct]);
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) S[rt][ct] = acc[ct];
+        }
+        stage(it.first_seg + j + 1);
     }
 }
 
 // Longest-sequence-first order of the N sequences (ties by index): the
 // dispatcher hands workgroups out in index order, so launching long chains
-// first gives a longest-processing-time schedule.
-__global__ void lpt_plan_kernel(const int32_t* __restrict__ cu, int N, int32_t* __restrict__ perm) {
+// first gives a longest-processing-time schedule.  One item per sequence.
+__global__ void plan_sequences_kernel(const int32_t* __restrict__ cu, int N, int T, int lpt,
+                                      int has_h0, int has_hT, ChunkItem* __restrict__ items) {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= N) return;
-    const int len = cu[n + 1] - cu[n];
-    int rank = 0;
-    for (int m = 0; m < N; ++m) {
-        const int lm = cu[m + 1] - cu[m];
-        rank += (lm > len) || (lm == len && m < n);
+    const int64_t a = cu ? cu[n] : static_cast<int64_t>(n) * T;
+    const int64_t b = cu ? cu[n + 1] : a + T;
+    int rank = n;
+    if (lpt) {
+        const int len = static_cast<int>(b - a);
+        rank = 0;
+        for (int m = 0; m < N; ++m) {
+            const int lm = cu[m + 1] - cu[m];
+            rank += (lm > len) || (lm == len && m < n);
+        }
     }
-    perm[rank] = n;
+    items[rank] = ChunkItem{a, b, has_h0 ? n : -1, has_hT ? n : -1};
+}
+
+// Segments of every sequence (seg tokens each, the last one shorter), the
+// map items of all segments but the last, and one scan item per sequence.
+// A single workgroup walks the sequences in blocks of 256 with a block scan.
+__global__ __launch_bounds__(256) void plan_segments_kernel(
+    const int32_t* __restrict__ cu, int N, int T, int seg, int has_h0, int has_hT,
+    ChunkItem* __restrict__ seg_items, ChunkItem* __restrict__ map_items,
+    ScanItem* __restrict__ scan_items) {
+    __shared__ int sc[256];
+    __shared__ int base;
+    if (threadIdx.x == 0) base = 0;
+    __syncthreads();
+    for (int n0 = 0; n0 < N; n0 += 256) {
+        const int n = n0 + threadIdx.x;
+        int64_t a = 0, b = 0;
+        int G = 0;
+        if (n < N) {
+            a = cu ? cu[n] : static_cast<int64_t>(n) * T;
+            b = cu ? cu[n + 1] : a + T;
+            const int64_t len = b - a;
+            G = len > 0 ? static_cast<int>((len + seg - 1) / seg) : 1;
+        }
+        sc[threadIdx.x] = G;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of G
+            const int x = threadIdx.x >= off ? sc[threadIdx.x - off] : 0;
+            __syncthreads();
+            sc[threadIdx.x] += x;
+            __syncthreads();
+        }
+        const int segs_before = base + sc[threadIdx.x] - G;  // segments of earlier sequences
+        const int maps_before = segs_before - n;             // each earlier sequence has G - 1 maps
+        if (n < N) {
+            for (int gi = 0; gi < G; ++gi) {
+                const int64_t sa = a + static_cast<int64_t>(gi) * seg;
+                const int64_t sb = sa + seg < b ? sa + seg : b;
+                const int sin = -2 - (segs_before + gi);  // staged by the scan
+                const int sout = gi == G - 1 ? (has_hT ? n : -1) : -1;
+                seg_items[segs_before + gi] = ChunkItem{sa, sb, sin, sout};
+                if (gi < G - 1) map_items[maps_before + gi] = ChunkItem{sa, sb, -1, maps_before + gi};
+            }
+            scan_items[n] = ScanItem{maps_before, G - 1, has_h0 ? n : -1, segs_before};
+        }
+        __syncthreads();
+        if (threadIdx.x == 255) base += sc[255];
+        __syncthreads();
+    }
 }
 
 }  // namespace chunkk
 
-constexpr int kLptMaxSeqs = 16384;
+namespace {
 
-size_t chunk_workspace_bytes(int B, int T, int H, int N, bool scan) {
+constexpr int kLptMaxSeqs = 16384;
+constexpr int kWaves = 8;  // waves per chain in the full-mode kernel
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Host mirror of the segment plan (same formula as plan_segments_kernel).
+void count_segments(const int32_t* cu_host, int N, int T, int seg, int64_t* nseg, int64_t* nmap) {
+    int64_t s = 0, m = 0;
+    for (int n = 0; n < N; ++n) {
+        const int64_t len = cu_host ? cu_host[n + 1] - cu_host[n] : T;
+        const int64_t G = len > 0 ? (len + seg - 1) / seg : 1;
+        s += G;
+        m += G - 1;
+    }
+    *nseg = s;
+    *nmap = m;
+}
+
+struct ScanLayout {
+    size_t seg_items, map_items, scan_items, maps, staged, total;
+};
+
+ScanLayout scan_layout(int64_t nseg, int64_t nmap, int N, int H) {
+    ScanLayout L{};
+    size_t off = 0;
+    L.seg_items = off;
+    off = align256(off + nseg * sizeof(ChunkItem));
+    L.map_items = off;
+    off = align256(off + nmap * sizeof(ChunkItem));
+    L.scan_items = off;
+    off = align256(off + static_cast<size_t>(N) * sizeof(ScanItem));
+    L.maps = off;
+    off = align256(off + static_cast<size_t>(nmap) * H * chunkk::D * 2 * chunkk::D * sizeof(float));
+    L.staged = off;
+    off = align256(off + static_cast<size_t>(nseg) * H * chunkk::D * chunkk::D * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host) {
+    // Long sequences are cut so that about four segments (workgroups) per CU
+    // exist over all heads; segments are a whole number of chunks.
     (void)B;
-    (void)T;
-    (void)H;
-    (void)scan;
-    return N <= kLptMaxSeqs ? ((static_cast<size_t>(N) * 4 + 255) / 256) * 256 : 0;
+    int64_t total = 0;
+    for (int n = 0; n < N; ++n) total += cu_host ? cu_host[n + 1] - cu_host[n] : T;
+    const int64_t target_items = 4 * 256 / (H > 0 ? H : 1) + 1;
+    int64_t seg = (total + target_items - 1) / target_items;
+    seg = (seg + chunkk::C - 1) / chunkk::C * chunkk::C;
+    if (seg < 16 * chunkk::C) seg = 16 * chunkk::C;
+    return static_cast<int>(seg > (1 << 30) ? (1 << 30) : seg);
+}
+
+size_t chunk_workspace_bytes(int B, int T, int H, int N, const int32_t* cu_host, bool scan) {
+    if (!scan) return align256(static_cast<size_t>(N) * sizeof(ChunkItem));
+    const int seg = chunk_segment_tokens(B, T, H, N, cu_host);
+    int64_t nseg, nmap;
+    count_segments(cu_host, N, T, seg, &nseg, &nmap);
+    return scan_layout(nseg, nmap, N, H).total;
 }
 
 hipError_t launch_chunk(const PrefillArgs& a, bool scan) {
-    (void)scan;
-    const int32_t* perm = nullptr;
-    if (a.cu && a.N > 1 && a.N <= kLptMaxSeqs) {
-        int32_t* p = static_cast<int32_t*>(a.ws);
-        hipLaunchKernelGGL(chunkk::lpt_plan_kernel, dim3((a.N + 255) / 256), dim3(256), 0, a.stream,
-                           a.cu, a.N, p);
-        perm = p;
+    using namespace chunkk;
+    char* ws = static_cast<char*>(a.ws);
+    auto launch_full = [&](const ChunkItem* items, int64_t nitems, const float* staged) {
+        const dim3 grid(static_cast<uint32_t>(nitems * a.H));
+        if (a.out_bf16)
+            hipLaunchKernelGGL((chunk_kernel<kWaves, 1, false, bf16_t>), grid, dim3(kWaves * 64), 0,
+                               a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
+                               staged, static_cast<bf16_t*>(a.o), a.hT);
+        else
+            hipLaunchKernelGGL((chunk_kernel<kWaves, 1, false, float>), grid, dim3(kWaves * 64), 0,
+                               a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
+                               staged, static_cast<float*>(a.o), a.hT);
+    };
+    if (!scan) {
+        ChunkItem* items = reinterpret_cast<ChunkItem*>(ws);
+        const int lpt = (a.cu && a.N > 1 && a.N <= kLptMaxSeqs) ? 1 : 0;
+        hipLaunchKernelGGL(plan_sequences_kernel, dim3((a.N + 255) / 256), dim3(256), 0, a.stream,
+                           a.cu, a.N, a.T, lpt, a.h0 ? 1 : 0, a.hT ? 1 : 0, items);
+        launch_full(items, a.N, nullptr);
+        return hipGetLastError();
     }
-    const dim3 grid(static_cast<uint32_t>(a.N) * a.H);
-    if (a.out_bf16) {
-        hipLaunchKernelGGL(chunkk::chunk_kernel<bf16_t>, grid, dim3(256), 0, a.stream,
-                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                           static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, a.h0, a.cu, perm,
-                           a.T, a.H, static_cast<bf16_t*>(a.o), a.hT);
-    } else {
-        hipLaunchKernelGGL(chunkk::chunk_kernel<float>, grid, dim3(256), 0, a.stream,
-                           static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                           static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, a.h0, a.cu, perm,
-                           a.T, a.H, static_cast<float*>(a.o), a.hT);
-    }
+    const int seg = chunk_segment_tokens(a.B, a.T, a.H, a.N, a.cu_host);
+    int64_t nseg, nmap;
+    count_segments(a.cu_host, a.N, a.T, seg, &nseg, &nmap);
+    const ScanLayout L = scan_layout(nseg, nmap, a.N, a.H);
+    ChunkItem* seg_items = reinterpret_cast<ChunkItem*>(ws + L.seg_items);
+    ChunkItem* map_items = reinterpret_cast<ChunkItem*>(ws + L.map_items);
+    ScanItem* scan_items = reinterpret_cast<ScanItem*>(ws + L.scan_items);
+    float* maps = reinterpret_cast<float*>(ws + L.maps);
+    float* staged = reinterpret_cast<float*>(ws + L.staged);
+    hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T, seg,
+                       a.h0 ? 1 : 0, a.hT ? 1 : 0, seg_items, map_items, scan_items);
+    if (nmap > 0)
+        hipLaunchKernelGGL((chunk_kernel<8, 2, true, float>), dim3(static_cast<uint32_t>(nmap * a.H)),
+                           dim3(8 * 64), 0, a.stream, static_cast<const uint16_t*>(a.q),
+                           static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.g,
+                           a.beta, a.scale, map_items, a.H, static_cast<const float*>(nullptr),
+                           static_cast<const float*>(nullptr), static_cast<float*>(nullptr), maps);
+    hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<uint32_t>(a.N) * a.H), dim3(256), 0,
+                       a.stream, scan_items, a.H, a.h0, maps, staged);
+    launch_full(seg_items, nseg, staged);
     return hipGetLastError();
 }
 

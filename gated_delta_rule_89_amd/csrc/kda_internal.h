@@ -68,8 +68,11 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStrea
 hipError_t launch_recurrent(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 
-// Chunked MFMA prefill (bf16 inputs, d_k = d_v = 128).
-size_t chunk_workspace_bytes(int B, int T, int H, int N, bool scan);
+// Chunked MFMA prefill (bf16 inputs, d_k = d_v = 128).  With scan = true long
+// sequences are cut into segments whose (B, M) maps are composed by a scan.
+// cu_host may be null (then the N sequences are rows of length T).
+int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host);
+size_t chunk_workspace_bytes(int B, int T, int H, int N, const int32_t* cu_host, bool scan);
 hipError_t launch_chunk(const PrefillArgs& a, bool scan);
 
 }  // namespace kda

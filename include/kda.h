@@ -68,10 +68,13 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 /* Prefill implementations.  AUTO picks the fastest one that supports the
  * arguments; the others exist to compare paths against each other.
  *  RECURRENT  token-sequential fused recurrent kernel, any supported shape;
- *  CHUNK      chunkwise kernel on bf16 MFMA, 64-token chunks, one workgroup
- *             per chain (bf16 inputs, d_k = d_v = 128);
- *  CHUNK_SCAN CHUNK plus a segment scan that runs each long chain on many
- *             workgroups (same inputs as CHUNK). */
+ *  CHUNK      chunkwise kernel on fp16/bf16 MFMA, 32-token chunks, one
+ *             workgroup per (sequence, head) (bf16 inputs, d_k = d_v = 128);
+ *  CHUNK_SCAN CHUNK on segments of long sequences: each segment's affine
+ *             state map is computed in parallel, composed by a scan, and the
+ *             segments then run in parallel from their initial states (same
+ *             inputs as CHUNK).  AUTO takes it when the longest sequence
+ *             would otherwise dominate the run time. */
 typedef enum kda_variant {
     KDA_VARIANT_AUTO = 0,
     KDA_VARIANT_RECURRENT = 1,
@@ -85,11 +88,14 @@ int kda_abi_version(void);
 /* Static, NUL-terminated description of a status code. */
 const char* kda_status_str(kda_status status);
 
-/* Bytes of device workspace kda_chunk_fwd needs for these sizes and variant
- * (0 is a valid answer).  N is the number of sequences (B, or the length of
- * cu_seqlens minus one).  Returns 0 for arguments kda_chunk_fwd would reject. */
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes, sequence
+ * lengths and variant (0 is a valid answer).  N is the number of sequences
+ * (B, or the length of cu_seqlens minus one); cu_seqlens_host is the host
+ * copy of cu_seqlens or NULL, exactly as later passed to kda_chunk_fwd.
+ * Returns 0 for arguments kda_chunk_fwd would reject. */
 size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
-                                    int32_t N, kda_dtype in_dtype, kda_variant variant);
+                                    int32_t N, const int32_t* cu_seqlens_host, kda_dtype in_dtype,
+                                    kda_variant variant);
 
 /* Chunked prefill over N independent sequences ("Understanding Kimi Delta
  * Attention", section "The Chunkwise DPLR Algorithm": chunks of the
@@ -112,7 +118,11 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
  *              pointer as initial_state (in-place update); no other overlap
  *              between outputs and inputs is allowed.
  *  workspace   device scratch of at least kda_chunk_fwd_workspace_size()
- *              bytes (may be NULL when that is 0), 256-byte aligned.
+ *              bytes (may be NULL when that is 0), 256-byte aligned; its
+ *              contents on entry do not matter and are overwritten.
+ * The chunked variants need the sum of g over any 16 consecutive tokens of a
+ * channel to stay above about -85; beyond that their results are undefined
+ * (the recurrent variant has no such limit).
  * T = 0 or N = 0 is a successful no-op. */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, float scale, const float* initial_state,

@@ -98,9 +98,25 @@ def test_chunk_validation():
 
 
 def test_workspace_size_rejects_bad_arguments():
-    assert kda.lib.kda_chunk_fwd_workspace_size(1, -1, 1, 128, 128, 1, BF16, 0) == 0
-    assert kda.lib.kda_chunk_fwd_workspace_size(1, 64, 1, 100, 128, 1, BF16, 0) == 0
-    assert kda.lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 1, 5, 0) == 0
+    ws = kda.lib.kda_chunk_fwd_workspace_size
+    assert ws(1, -1, 1, 128, 128, 1, None, BF16, 0) == 0
+    assert ws(1, 64, 1, 100, 128, 1, None, BF16, 0) == 0
+    assert ws(1, 64, 1, 128, 128, 1, None, 5, 0) == 0
+    assert ws(1, 64, 1, 128, 128, 1, None, BF16, 7) == 0
+    keep, bad = host_cu([0, 40, 30])
+    assert ws(1, 30, 1, 128, 128, 2, bad, BF16, 2) == 0     # non-monotone lengths
+    assert ws(2, 64, 1, 128, 128, 1, None, BF16, 0) == 0    # N != B without lengths
+
+
+def test_workspace_size_grows_with_segments():
+    """The segment scan needs map and staged-state space; the plain chunked
+    path only an item list; the recurrent path nothing."""
+    ws = kda.lib.kda_chunk_fwd_workspace_size
+    keep, cu = host_cu([0, 100000, 100100])
+    plain = ws(1, 100100, 4, 128, 128, 2, cu, BF16, 2)
+    scan = ws(1, 100100, 4, 128, 128, 2, cu, BF16, 3)
+    assert 0 < plain < 4096 and scan > 4 * 128 * 128 * 4
+    assert ws(1, 100100, 4, 128, 128, 2, cu, BF16, 1) == 0
 
 
 def decode(q=None, k=None, v=None, g=None, beta=None, state=None, N=4, H=2, dk=16, dv=16,

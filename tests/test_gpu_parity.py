@@ -41,7 +41,7 @@ def run_prefill(x, variant="auto", **kw):
     return o, f
 
 
-VARIANTS = ["auto", "recurrent", "chunk"]
+VARIANTS = ["auto", "recurrent", "chunk", "chunk_scan"]
 
 
 @pytest.mark.parametrize("variant", ["auto", "recurrent"])
@@ -252,3 +252,37 @@ def test_chunk_matches_recurrent_varlen():
     oc, fc = run_prefill(x, "chunk")
     orc, frc = run_prefill(x, "recurrent")
     assert rel_rms(oc, orc) <= 2e-2 and rel_rms(fc, frc) <= 2e-2
+
+
+@pytest.mark.parametrize("T,H", [(20000, 2), (1500, 3)])
+def test_scan_long_sequence(T, H):
+    """A long sequence cut into segments: maps, scan and segment pass against
+    the sequential oracle, with a random initial state."""
+    say(f"chunk_scan one sequence T={T} H={H}")
+    x = synth.make_inputs("long", T=T, H=H, seed=9)
+    x.h0 = 0.02 * torch.randn(1, H, 128, 128, generator=torch.Generator().manual_seed(3))
+    o, f = run_prefill(x, "chunk_scan")
+    o_ref, f_ref = oracle_prefill(x)
+    eo = assert_parity(o, o_ref, torch.bfloat16, "o")
+    ef = assert_parity(f, f_ref, torch.bfloat16, "final")
+    say(f"  o {eo:.2e} final {ef:.2e}")
+
+
+def test_scan_in_place_state_and_agreement():
+    """Segment scan with final_state == initial_state, compared with the
+    one-workgroup-per-sequence chunked path on the GPU."""
+    lens = [6000, 40, 0, 3000]
+    say(f"chunk_scan in place, lens={lens} H=2")
+    x = synth.make_inputs("varlen", lens=lens, H=2)
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    kda = _kda()
+    oc, fc = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, xd.h0, x.cu_seqlens,
+                           variant="chunk")
+    st = xd.h0.clone()
+    os_, fs = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, st, x.cu_seqlens,
+                            variant="chunk_scan", final_state=st)
+    torch.cuda.synchronize()
+    assert fs.data_ptr() == st.data_ptr()
+    assert rel_rms(os_, oc) <= 2e-2 and rel_rms(fs, fc) <= 2e-2
+    assert torch.equal(fs[2], xd.h0[2])  # empty sequence keeps its state
