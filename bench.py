@@ -50,6 +50,22 @@ def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=4):
     return state, state + other
 
 
+def measured_traffic(key, workload_label):
+    """HBM bytes per launch from the committed rocprofv3 counter record
+    (profiles/hbm_traffic.json), or None when the kernel source has changed
+    since the counters were taken or the workload differs."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))["kernels"][key]
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"] or rec["workload"] != workload_label:
+        return None
+    return rec["traffic_bytes"]
+
+
 def cpu_baseline(x, budget_s=12.0):
     """The C oracle (fp64, OpenMP over chains) on a sample of the workload's
     (sequence, head) chains, each cut to a prefix so that the sample takes
@@ -84,11 +100,20 @@ def cpu_baseline(x, budget_s=12.0):
                         np.stack(h0s) if h0s else None, True, threads)
         return row, time.perf_counter() - t_0
 
-    # one chain per thread, all heads of the first sequences first
-    sel = [(n, h) for n in range(len(chains)) for h in range(H)][:max(threads, 1)]
-    ht, dt = run(sel, 256)                                   # calibration
-    rate = ht / max(dt, 1e-6)
-    cap = max(256, int(rate * budget_s / len(sel)))
+    # calibrate on short prefixes of one chain per thread
+    order = [(n, h) for n in range(len(chains)) for h in range(H)]
+    sel = order[:max(threads, 1)]
+    ht, dt = run(sel, 256)
+    target = int(ht / max(dt, 1e-6) * budget_s)
+    # whole chains in order, each cut to at most target/threads tokens, until the target
+    cap = max(256, target // max(threads, 1))
+    sel, acc = [], 0
+    for n, h in order:
+        if acc >= target:
+            break
+        b, t0, t1 = chains[n]
+        sel.append((n, h))
+        acc += min(t1 - t0, cap)
     ht, dt = run(sel, cap)
     return {"value": ht / dt / H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(sel)} (sequence, head) chains, first <= {cap} tokens each "
@@ -105,6 +130,8 @@ def main():
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one 1 GiB device copy first (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -147,6 +174,12 @@ def main():
         dq, dk_, dvv, dg, db, dstate, dout, sc = dec
         kda.decode_step(dq, dk_, dvv, dg, db, sc, dstate, o=dout)
 
+    if args.copy_probe:
+        src = torch.ones(1 << 28, device=dev)  # 1 GiB of fp32
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
+
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         prefill()
@@ -172,6 +205,10 @@ def main():
     pre_avg = sum(pre_ms) / len(pre_ms)
 
     alg_b = prefill_alg_bytes(tokens, H, dk, dv, N, h0=x.h0 is not None)
+    traffic = None
+    if args.workload == "varlen" and args.variant == "auto":
+        t = measured_traffic("chunk", "packed varlen prefill: 64 sequences, 262144 tokens, H=32, d=128")
+        traffic = None if t is None else t / 1e9
     alg_f = prefill_alg_flops(tokens, H, dk, dv)
     achieved = alg_b / (pre_avg * 1e-3) / 1e9
     value = tokens / (pre_avg * 1e-3)
@@ -187,14 +224,16 @@ def main():
         "prefill_ms": pre_avg, "prefill_ms_min": min(pre_ms),
         "mfma_peak_equiv_frac": alg_f / (pre_avg * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "traffic_unit": "GB per launch",
                      "kernel": f"prefill ({args.variant})", "alg_bytes_per_launch": alg_b},
     }
     if dec:
         N3, H3 = dec[0].shape[0], dec[0].shape[1]
         sb, tb = decode_alg_bytes(N3, H3, 128, 128)
         dm = sum(dec_ms) / len(dec_ms)
+        td = measured_traffic("decode", "decode step: 256 sequences x 32 heads, d=128, state in place")
         line["decode"] = {"us_per_step": dm * 1e3, "state_gbs": sb / (dm * 1e-3) / 1e9,
+                          "traffic_gb": None if td is None else td / 1e9,
                           "total_gbs": tb / (dm * 1e-3) / 1e9,
                           "frac": tb / (dm * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "config": f"{N3} sequences x {H3} heads, d=128"}
