@@ -65,6 +65,10 @@ struct ScanItem {
 
 namespace chunkk {
 
+#ifndef KDA_CHUNK_WG_PER_CU
+#define KDA_CHUNK_WG_PER_CU 1  // chains resident per CU; sets the register budget per wave
+#endif
+
 constexpr int C = 32;   // tokens per chunk
 constexpr int SB = 16;  // tokens per sub-block
 constexpr int D = 128;  // head size (d_k = d_v)
@@ -163,7 +167,8 @@ __device__ __forceinline__ int value_exponent(float mx, int ex) {
 // (NW * 16 NCT = 128 columns), writes o and the final state.  Map mode: state
 // = [B | M] (256 columns), no o, writes the segment's (B, M).
 template <int NW, int NCT, bool MAP, typename Tout>
-__global__ __launch_bounds__(NW * 64, 1) void chunk_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4 * KDA_CHUNK_WG_PER_CU)))
+void chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, const ChunkItem* __restrict__ items, int H,

@@ -286,3 +286,65 @@ def test_scan_in_place_state_and_agreement():
     assert fs.data_ptr() == st.data_ptr()
     assert rel_rms(os_, oc) <= 2e-2 and rel_rms(fs, fc) <= 2e-2
     assert torch.equal(fs[2], xd.h0[2])  # empty sequence keeps its state
+
+
+def _sampled_chains(x, chains):
+    """Oracle results for selected (sequence, head) chains of a full-size batch,
+    computed by the C oracle from the exact inputs given to the GPU."""
+    return cref.kda_forward_chains(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0, x.cu_seqlens,
+                                   select=chains, n_threads=THREADS)
+
+
+def test_varlen_workload_full_size_sampled():
+    """The full packed varlen workload (64 sequences, 262144 tokens, H=32) in the
+    launch configuration the benchmark times (AUTO); the oracle checks whole
+    chains: the longest sequence on two heads and four other (sequence, head)
+    pairs, o over every token of those chains and their final states."""
+    say("varlen full size 262144 tokens H=32, sampled chains")
+    dev = torch.device("cuda")
+    x = synth.make_inputs("varlen", device=dev)
+    lens = np.diff(x.cu_seqlens)
+    longest = int(np.argmax(lens))
+    chains = [(longest, 0), (longest, 31), (int(np.argmin(lens)), 5), (3, 7), (40, 20), (63, 31)]
+    o, f = _kda().chunk_fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0, x.cu_seqlens)
+    torch.cuda.synchronize()
+    res = _sampled_chains(x, chains)
+    for (n, h), (oc, fc) in zip(chains, res):
+        a, b = int(x.cu_seqlens[n]), int(x.cu_seqlens[n + 1])
+        assert_parity(o[0, a:b, h], oc, torch.bfloat16, f"o seq {n} head {h}")
+        assert_parity(f[n, h], fc, torch.bfloat16, f"final seq {n} head {h}")
+
+
+def test_long_workload_full_size_sampled():
+    """The full long workload (one sequence of 1,048,576 tokens, H=32) through
+    AUTO (the segment scan), checked three ways: the oracle on the first 40000
+    tokens of four heads (covering the first segment boundary), a split call
+    at a chunk-unaligned point that must agree with the whole call, and the
+    chunked path without segments on two heads."""
+    say("long full size 1048576 tokens H=32")
+    dev = torch.device("cuda")
+    x = synth.make_inputs("long", device=dev)
+    kda = _kda()
+    o, f = kda.chunk_fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, None)
+    torch.cuda.synchronize()
+    P = 40000
+    heads = [0, 9, 22, 31]
+    xs = synth.KDAInputs(*(t[:, :P].cpu() for t in (x.q, x.k, x.v, x.g, x.beta)), x.scale, None)
+    res = cref.kda_forward_chains(xs.q, xs.k, xs.v, xs.g, xs.beta, xs.scale, None, None,
+                                  select=[(0, h) for h in heads], n_threads=THREADS)
+    for h, (oc, _) in zip(heads, res):
+        assert_parity(o[0, :P, h], oc, torch.bfloat16, f"o prefix head {h}")
+    cut = 500001
+    sl = lambda t, a, b: t[:, a:b].contiguous()
+    o1, f1 = kda.chunk_fwd(*(sl(t, 0, cut) for t in (x.q, x.k, x.v, x.g, x.beta)), x.scale, None)
+    o2, f2 = kda.chunk_fwd(*(sl(t, cut, None) for t in (x.q, x.k, x.v, x.g, x.beta)), x.scale, f1)
+    torch.cuda.synchronize()
+    assert rel_rms(o2[:, -4096:], o[:, cut:][:, -4096:]) <= 2e-2
+    assert rel_rms(f2, f) <= 2e-2
+    del o1, o2
+    hs = [0, 31]
+    xh = [sl(t[:, :, hs], 0, None) for t in (x.q, x.k, x.v, x.g, x.beta)]
+    oc, fc = kda.chunk_fwd(*xh, x.scale, None, variant="chunk")
+    torch.cuda.synchronize()
+    assert rel_rms(f[:, hs], fc) <= 2e-2
+    assert rel_rms(o[0, -8192:, hs], oc[0, -8192:]) <= 2e-2
