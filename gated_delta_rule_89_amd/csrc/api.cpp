@@ -63,8 +63,10 @@ kda_variant resolve_variant(kda_variant v, int32_t B, int32_t T, int32_t H, int3
         chunks += (len + 31) / 32;
     }
     (void)B;
-    const int64_t per_cu = chunks * H / cu_count();
-    return (longest + 31) / 32 > 2 * per_cu + 16 ? KDA_VARIANT_CHUNK_SCAN : KDA_VARIANT_CHUNK;
+    // Chunks per resident chain if the work were spread evenly; a sequence
+    // much longer than that would leave most of the GPU idle at the end.
+    const int64_t per_slot = chunks * H / (static_cast<int64_t>(cu_count()) * kda::chunk_chains_per_cu());
+    return (longest + 31) / 32 > 2 * per_slot + 16 ? KDA_VARIANT_CHUNK_SCAN : KDA_VARIANT_CHUNK;
 }
 
 size_t workspace_for(kda_variant v, int32_t B, int32_t T, int32_t H, int32_t N, const int32_t* cu_host) {

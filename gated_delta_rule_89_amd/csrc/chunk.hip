@@ -11,7 +11,7 @@
 //   P    = Lower_incl((Lambda q)(k / Lambda)^T)                 C x C
 //   T    = (I + A)^-1 Diag(beta)
 //   W    = T (Lambda k),   U = T v
-//   Delta = U - W S
+//   Delta = U - W S = T (v - K~ S),            K~ = Lambda k
 //   O    = scale (Q~ S + P Delta),             Q~ = Lambda q
 //   S   <- Diag(Lambda_last) S + K-bar^T Delta,  K-bar = (Lambda_last / Lambda) k
 //
@@ -31,8 +31,8 @@
 //    relative to the sub-block start, across sub-blocks relative to the end
 //    of the earlier one, so all factors are <= 1 except the in-block
 //    exp(-Gamma) of the diagonal Gram blocks.  Those two diagonal blocks run
-//    on split bf16 operands (hi + lo, three MFMAs) that keep fp32 range; every
-//    other product runs on fp16 MFMA with fp32 accumulation.  The kernel needs
+//    on fp32 MFMA straight from the gate registers; every other product runs
+//    on fp16 MFMA with fp32 accumulation.  The kernel needs
 //    the sum of g over any 16 consecutive tokens of a channel to stay above
 //    about -85 (exp of the negated sum must be finite in fp32).
 //  * S lives in MFMA accumulators for the whole segment; its fp16 copy and
@@ -42,7 +42,12 @@
 //  * Value-side fp16 operands (S, v, Delta) carry a per-wave power-of-two scale
 //    chosen every chunk from max(|S|, |v|), which keeps them inside fp16 range
 //    and away from subnormals; the scale is exact and is removed in fp32.
+//  * Delta is formed as T (v - K~ S): one product with K~ per state column
+//    tile and one with T, instead of building W = T K~ (which every wave
+//    would need in full).
 //  * The next chunk's inputs are fetched into registers during the state pass.
+//  * Register use is held to 128 VGPRs in the full-mode kernel, so that two
+//    chains share a CU and fill each other's barrier and latency stalls.
 #include "dev_common.h"
 #include "kda_internal.h"
 
@@ -65,16 +70,13 @@ struct ScanItem {
 
 namespace chunkk {
 
-#ifndef KDA_CHUNK_WG_PER_CU
-#define KDA_CHUNK_WG_PER_CU 1  // chains resident per CU; sets the register budget per wave
-#endif
-
 constexpr int C = 32;   // tokens per chunk
 constexpr int SB = 16;  // tokens per sub-block
 constexpr int D = 128;  // head size (d_k = d_v)
 constexpr int QP = 136; // row stride (halves) of [token][channel] tiles
 constexpr int TP = 40;  // row stride (halves) of [x][token] tiles
-constexpr int GP = 17;  // row stride (floats) of 16x16 Gram tiles
+constexpr int GP = 18;  // row stride (floats) of 16x16 Gram tiles
+constexpr int BP = 20;  // row stride (halves) of 16x16 fp16 blocks
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -82,21 +84,27 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
+// MFMA A operands read from LDS ([row][k] tiles with k = 32 channels or 32
+// tokens per block) store each 32-wide k block in operand order: position
+// 8 j + m holds k index 4 j + m (m < 4) or 16 + 4 j + m - 4 (m >= 4), the
+// order in which the B operands built from accumulator registers come.  A
+// lane's 8 k values are then one aligned 16-byte read.
+__device__ __forceinline__ int kpos(int c) { return 8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3); }
+
 // Gram tiles: A00, P00, A11, P11, A10, P10.
 enum { GA00 = 0, GP00 = 1, GA11 = 2, GP11 = 3, GA10 = 4, GP10 = 5 };
 
 // Per-workgroup LDS; NP = channel parts per sub-block (one Gram partial each).
 template <int NP>
 struct alignas(16) Smem {
-    _Float16 qt[C][QP];      // Q~ = Lambda q                 [token][channel]
-    _Float16 kbt[D][TP];     // K-bar^T                       [channel][token]
-    _Float16 ktt[D][TP];     // K~^T = (Lambda k)^T           [channel][token]
+    _Float16 qt[C][QP];      // Q~ = Lambda q                 [token][channel, operand order]
+    _Float16 kt[C][QP];      // K~ = Lambda k                 [token][channel, operand order]
+    _Float16 kbt[D][TP];     // K-bar^T                       [channel][token, operand order]
     _Float16 r0[SB][QP];     // k exp(Gamma_end0 - Gamma), tokens 0..15   [token][channel]
-    _Float16 t[C][TP];       // T = (I + A)^-1 Diag(beta)     [token][token]
-    _Float16 p[C][TP];       // P                             [token][token]
+    _Float16 tb[3][SB][BP];  // T00, T11 = X_JJ Diag(beta_J) and -G10 (raw cross Gram)  [token][token]
+    _Float16 p[C][TP];       // P                             [token][token, operand order]
     uint16_t v[C][QP];       // v tile (bf16 bits)            [token][column]
     float gp[NP][6][SB][GP]; // Gram partial sums, one per channel part
-    float x[2][SB][GP];      // (I + A_II)^-1 for the two diagonal blocks
     float a[2][SB][20];      // A_II^T: column m of Diag(beta) Gram in row m
     float etot[2][D];        // per-channel exp(sum of g over each sub-block)
     float lam[D];            // Lambda_last = exp(Gamma over the chunk)
@@ -105,6 +113,9 @@ struct alignas(16) Smem {
 
 __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma16k16(h4 a, h4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f4 mfmab(b8 a, b8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -165,9 +176,10 @@ __device__ __forceinline__ int value_exponent(float mx, int ex) {
 
 // NW waves; each owns NCT 16-column tiles of the state.  Full mode: state = S
 // (NW * 16 NCT = 128 columns), writes o and the final state.  Map mode: state
-// = [B | M] (256 columns), no o, writes the segment's (B, M).
-template <int NW, int NCT, bool MAP, typename Tout>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4 * KDA_CHUNK_WG_PER_CU)))
+// = [B | M] (256 columns), no o, writes the segment's (B, M).  WPC workgroups
+// share a CU (it sets the register budget per wave).
+template <int NW, int NCT, bool MAP, int WPC, typename Tout>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4 * WPC)))
 void chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
@@ -185,7 +197,7 @@ void chunk_kernel(
     __shared__ Smem<NP> sm;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;      // wave
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave (uniform: scalar register)
     const int l = tid & 63;      // lane
     const int r = l & 15;        // MFMA row / column index
     const int g4 = l >> 4;       // MFMA k group
@@ -269,44 +281,72 @@ void chunk_kernel(
         // ---------------- gate phase 1: cumulative gates, diagonal Grams
         h8 l16[KS], q16[KS], rb16[KS];  // L, Lq, k exp(tot - G) as fp16 (k-step ks, slot m)
         {
+            constexpr float LOG2E = 1.4426950408889634f;
+            // Diagonal Gram operands are referenced to half the sub-block total,
+            // k exp(G - tot/2) and k exp(tot/2 - G) (their products are unchanged).
+            // A wave whose exponents all stay within +-8 (natural units) feeds them
+            // to fp16 MFMA; otherwise it keeps fp32 range on fp32 MFMA.
+            constexpr float FAST_SPAN = 8.f * LOG2E;
             f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+            float La[KS][8], Ra[KS][8], Qa[KS][8];
+            float span = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = CPG * part + 32 * ks + 8 * g4;
-                float kf[8], qf[8];
+                float kf[8], qf[8], G[8], Gt[8];
                 unpack_bf16x8(kw[ks], kf);
                 unpack_bf16x8(qw[ks], qf);
-                b8 lh, ll, qh, ql, rh, rl;
+                // Gamma from the sub-block start, in log2 units; Gt = sub-block total (lane 15)
+#pragma unroll
+                for (int m = 0; m < 8; ++m) G[m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) Gt[m] = __shfl(G[m], 15, 16);
+                float e1[8];
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
-                    const float G = row_scan16(m < 4 ? ga[ks][m] : gb[ks][m - 4]);  // Gamma from the sub-block start
-                    const float e1 = gate_exp(G);            // <= 1
-                    const float e2 = gate_exp(-G);           // >= 1
-                    const float etot = __shfl(e1, 15, 16);   // exp(sum of g over the sub-block)
-                    const float L = kf[m] * e1, R = kf[m] * e2;
+                    e1[m] = __builtin_amdgcn_exp2f(G[m]);                      // exp(G) <= 1
+                    const float e3 = __builtin_amdgcn_exp2f(Gt[m] - G[m]);     // exp(tot - G) <= 1
+                    const float hm = __builtin_amdgcn_exp2f(-0.5f * Gt[m]);    // exp(-tot/2)
+                    span = fmaxf(span, fabsf(G[m] - 0.5f * Gt[m]));
+                    const float L = kf[m] * e1[m], rb = kf[m] * e3;
                     l16[ks][m] = static_cast<_Float16>(L);
-                    rb16[ks][m] = static_cast<_Float16>(R * etot);  // k exp(tot - G) <= 1
-                    if (r == 15) sm.etot[I][ch + m] = etot;
-                    lh[m] = static_cast<__bf16>(L);
-                    ll[m] = static_cast<__bf16>(L - static_cast<float>(lh[m]));
-                    rh[m] = static_cast<__bf16>(R);
-                    rl[m] = static_cast<__bf16>(R - static_cast<float>(rh[m]));
+                    rb16[ks][m] = static_cast<_Float16>(rb);
+                    La[ks][m] = L * hm;
+                    Ra[ks][m] = rb * hm;
                     if (!MAP) {
-                        const float Lq = qf[m] * e1;
+                        const float Lq = qf[m] * e1[m];
                         q16[ks][m] = static_cast<_Float16>(Lq);
-                        qh[m] = static_cast<__bf16>(Lq);
-                        ql[m] = static_cast<__bf16>(Lq - static_cast<float>(qh[m]));
+                        Qa[ks][m] = Lq * hm;
                     }
                 }
-                accA = mfmab(lh, rh, accA);
-                accA = mfmab(lh, rl, accA);
-                accA = mfmab(ll, rh, accA);
-                if (!MAP) {
-                    accP = mfmab(qh, rh, accP);
-                    accP = mfmab(qh, rl, accP);
-                    accP = mfmab(ql, rh, accP);
+                if (r == 15) {  // exp(sum of g over the sub-block)
+                    *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{e1[0], e1[1], e1[2], e1[3]};
+                    *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{e1[4], e1[5], e1[6], e1[7]};
                 }
                 if (I == 0) *reinterpret_cast<h8*>(&sm.r0[r][ch]) = rb16[ks];
+            }
+            if (wave_max_nonneg(span) <= FAST_SPAN) {  // wave-uniform
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    h8 la, ra, qa;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        la[m] = static_cast<_Float16>(La[ks][m]);
+                        ra[m] = static_cast<_Float16>(Ra[ks][m]);
+                        if (!MAP) qa[m] = static_cast<_Float16>(Qa[ks][m]);
+                    }
+                    accA = mfma16(la, ra, accA);
+                    if (!MAP) accP = mfma16(qa, ra, accP);
+                }
+            } else {
+                // MFMA m contracts channel 8 g4 + m (k index g4).
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        accA = mfma4(La[ks][m], Ra[ks][m], accA);
+                        if (!MAP) accP = mfma4(Qa[ks][m], Ra[ks][m], accP);
+                    }
             }
             // Row 4 g4 + i of the Gram tile is token 4 g4 + i of the sub-block: scale A by its beta.
 #pragma unroll
@@ -325,19 +365,34 @@ void chunk_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = CPG * part + 32 * ks + 8 * g4;
+                // exp(sum of g over the other sub-block) as fp16 (<= 1; an underflow
+                // to zero drops terms below 2^-24 of the kept ones).
+                // Sub-block 0: Gamma_r = G, K-bar needs exp(tot1); sub-block 1:
+                // Gamma_r = tot0 + G, so Q~ and K~ take exp(tot0).
                 const f4 oa = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch]);
                 const f4 ob = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch + 4]);
-                h8 qv;
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const float other = m < 4 ? oa[m] : ob[m - 4];  // exp(sum of g over the other sub-block)
-                    // sub-block 0: Gamma_r = G, K-bar needs exp(tot1); sub-block 1: Gamma_r = tot0 + G
-                    const float fq = I ? other : 1.f, fk = I ? 1.f : other;
-                    sm.ktt[ch + m][tok] = static_cast<_Float16>(static_cast<float>(l16[ks][m]) * fq);
-                    sm.kbt[ch + m][tok] = static_cast<_Float16>(static_cast<float>(rb16[ks][m]) * fk);
-                    if (!MAP) qv[m] = static_cast<_Float16>(static_cast<float>(q16[ks][m]) * fq);
+                const h8 of = {static_cast<_Float16>(oa[0]), static_cast<_Float16>(oa[1]),
+                               static_cast<_Float16>(oa[2]), static_cast<_Float16>(oa[3]),
+                               static_cast<_Float16>(ob[0]), static_cast<_Float16>(ob[1]),
+                               static_cast<_Float16>(ob[2]), static_cast<_Float16>(ob[3])};
+                h8 kv = l16[ks], qv = q16[ks], bv = rb16[ks];
+                if (I == 1) {
+                    kv *= of;
+                    if (!MAP) qv *= of;
+                } else {
+                    bv *= of;
                 }
-                if (!MAP) *reinterpret_cast<h8*>(&sm.qt[tok][ch]) = qv;
+                // channels 8 g4 .. 8 g4 + 7 of the block go to two 4-wide runs
+                const int cb = ch & ~31, p0 = cb + (g4 < 2 ? 16 * g4 : 16 * g4 - 28), p1 = p0 + 8;
+                *reinterpret_cast<h4*>(&sm.kt[tok][p0]) = __builtin_shufflevector(kv, kv, 0, 1, 2, 3);
+                *reinterpret_cast<h4*>(&sm.kt[tok][p1]) = __builtin_shufflevector(kv, kv, 4, 5, 6, 7);
+                if (!MAP) {
+                    *reinterpret_cast<h4*>(&sm.qt[tok][p0]) = __builtin_shufflevector(qv, qv, 0, 1, 2, 3);
+                    *reinterpret_cast<h4*>(&sm.qt[tok][p1]) = __builtin_shufflevector(qv, qv, 4, 5, 6, 7);
+                }
+                const int tp = kpos(tok);
+#pragma unroll
+                for (int m = 0; m < 8; ++m) sm.kbt[ch + m][tp] = bv[m];
                 if (I == 1) {
                     const h8 rv = *reinterpret_cast<const h8*>(&sm.r0[r][ch]);
                     a10 = mfma16(l16[ks], rv, a10);
@@ -347,7 +402,7 @@ void chunk_kernel(
             if (I == 1) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    sm.gp[part][GA10][4 * g4 + i][r] = a10[i] * sm.beta[SB + 4 * g4 + i];
+                    sm.gp[part][GA10][4 * g4 + i][r] = a10[i];  // raw (beta is applied in the state pass)
                     if (!MAP) sm.gp[part][GP10][4 * g4 + i][r] = p10[i];
                 }
             }
@@ -373,32 +428,29 @@ void chunk_kernel(
             const int j = r;  // column of the inverse owned by this lane
             // Column j of (I + A_JJ)^-1 by forward substitution, column-oriented:
             // once x_m is final, every later row subtracts A[i][m] x_m (independent
-            // updates).  Columns of A are read one step ahead.
+            // updates).  The parts of A's columns below the diagonal are read up
+            // front (broadcast reads), so the 16 steps wait on LDS only once.
+            int jj = j;
+            asm volatile("" : "+v"(jj));  // keeps the identity column from being hoisted out of the chunk loop
             float xcol[SB];
 #pragma unroll
-            for (int i = 0; i < SB; ++i) xcol[i] = (i == j) ? 1.f : 0.f;
-            f4 cl[4], ncl[4];
+            for (int i = 0; i < SB; ++i) xcol[i] = (i == jj) ? 1.f : 0.f;
+            f4 cl[SB][4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) cl[c] = *reinterpret_cast<const f4*>(&sm.a[J][0][4 * c]);
+            for (int m = 0; m < SB; ++m)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (4 * c + 3 > m) cl[m][c] = *reinterpret_cast<const f4*>(&sm.a[J][m][4 * c]);
 #pragma unroll
             for (int m = 0; m < SB; ++m) {
-                if (m + 1 < SB) {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) ncl[c] = *reinterpret_cast<const f4*>(&sm.a[J][m + 1][4 * c]);
-                }
                 const float xm = xcol[m];
 #pragma unroll
-                for (int i = m + 1; i < SB; ++i) xcol[i] = fmaf(-cl[i >> 2][i & 3], xm, xcol[i]);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) cl[c] = ncl[c];
+                for (int i = m + 1; i < SB; ++i) xcol[i] = fmaf(-cl[m][i >> 2][i & 3], xm, xcol[i]);
             }
             if (g4 == 0) {
                 const float bj = sm.beta[SB * J + j];
 #pragma unroll
-                for (int i = 0; i < SB; ++i) {
-                    sm.x[J][i][j] = xcol[i];
-                    sm.t[SB * J + i][SB * J + j] = static_cast<_Float16>(xcol[i] * bj);
-                }
+                for (int i = 0; i < SB; ++i) sm.tb[J][i][j] = static_cast<_Float16>(xcol[i] * bj);
             }
         } else {
             const int t2 = tid - 128;
@@ -413,46 +465,38 @@ void chunk_kernel(
 #pragma unroll
                         for (int pp = 0; pp < NP; ++pp) val += sm.gp[pp][tile][rr][cc];
                     }
-                    sm.p[R][Cc] = static_cast<_Float16>(val);
+                    sm.p[R][kpos(Cc)] = static_cast<_Float16>(val);
                 }
             }
-            for (int e = t2; e < SB * SB; e += NT2) sm.t[e >> 4][SB + (e & 15)] = static_cast<_Float16>(0.f);
+            for (int e = t2; e < SB * SB; e += NT2) {
+                float val = 0.f;
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) val += sm.gp[pp][GA10][e >> 4][e & 15];
+                sm.tb[2][e >> 4][e & 15] = static_cast<_Float16>(-val);
+            }
         }
         __syncthreads();  // B3
-
-        // ---------------- solve: off-diagonal block X10 = -X11 (A10 X00), fp32 MFMA on wave 0
-        if (w == 0) {
-            f4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int m = 4 * ks + g4;
-                float a = 0.f;
-#pragma unroll
-                for (int pp = 0; pp < NP; ++pp) a += sm.gp[pp][GA10][r][m];
-                y = mfma4(a, sm.x[0][m][r], y);
-            }
-            // y[i] = Y[4 g4 + i][r]; contract X11 Y with k index m = 4 g4 + ks
-            f4 x10 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) x10 = mfma4(sm.x[1][r][4 * g4 + ks], y[ks], x10);
-            const float bj = sm.beta[r];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.t[SB + 4 * g4 + i][r] = static_cast<_Float16>(-x10[i] * bj);
-        }
-        __syncthreads();  // B4
 
         // ---------------- state pass on this wave's columns
         if (c0 + C < t1) fetch(c0 + C);
         {
-            // Exponent for this chunk from max(|S|, |v|) over the wave's columns.
-            float mv = 0.f;
-            if (!mhalf) {
+            // v at token 16 rt + 4 g4 + i, column col + 16 ct + r (accumulator layout).
+            float vv[2][NCT][4];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-                    for (int m = 0; m < 8; ++m)
-                        mv = fmaxf(mv, fabsf(bf16_to_f32(sm.v[8 * g4 + m][col + 16 * ct + r])));
-            }
+                    for (int i = 0; i < 4; ++i)
+                        vv[rt][ct][i] = mhalf ? 0.f : bf16_to_f32(sm.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
+            // Exponent for this chunk from max(|S|, |v|) over the wave's columns.
+            float mv = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(vv[rt][ct][i]));
             float ms = 0.f;
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
@@ -471,7 +515,7 @@ void chunk_kernel(
             }
             const float sig = ldexpf(1.f, ex);
 
-            h8 s16[4][NCT];  // B operand of W S and Q~ S: [channel k-step][column tile]
+            h8 s16[4][NCT];  // B operand of K~ S and Q~ S: [channel k-step][column tile]
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -482,54 +526,51 @@ void chunk_kernel(
                         s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
                     }
 
-            // Delta = T v - W S (scaled), W = T K~ built per channel k-step from K~^T T^T.
-            h8 tf[2];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) tf[rt] = *reinterpret_cast<const h8*>(&sm.t[16 * rt + r][8 * g4]);
-            f4 dl[2][NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                if (mhalf) {
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) dl[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
-                } else {
-                    h8 v16;
-#pragma unroll
-                    for (int m = 0; m < 8; ++m)
-                        v16[m] = static_cast<_Float16>(bf16_to_f32(sm.v[8 * g4 + m][col + 16 * ct + r]) * sig);
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) dl[rt][ct] = mfma16(tf[rt], v16, f4{0.f, 0.f, 0.f, 0.f});
-                }
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                f4 wa[2][2];
-#pragma unroll
-                for (int hx = 0; hx < 2; ++hx) {
-                    const h8 kt = *reinterpret_cast<const h8*>(&sm.ktt[16 * (2 * ks + hx) + r][8 * g4]);
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) wa[hx][rt] = mfma16(kt, tf[rt], f4{0.f, 0.f, 0.f, 0.f});
-                }
+            // X = sigma v - K~ S (fp32), then Delta = T X (scaled units) by blocks:
+            // Delta_0 = T00 X_0 and Delta_1 = T11 (X_1 - G10 Delta_0), which is
+            // T X for T = (I + A)^-1 Diag(beta) with A10 = Diag(beta_1) G10.
+            h8 d16[NCT];  // B operand of P Delta and K-bar^T Delta (k = tokens, permuted)
+            {
+                f4 y[2][NCT];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
-                    h8 wf;
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) y[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const h8 kf8 = *reinterpret_cast<const h8*>(&sm.kt[16 * rt + r][32 * ks + 8 * g4]);
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct) y[rt][ct] = mfma16(kf8, s16[ks][ct], y[rt][ct]);
+                    }
+                }
+                const h4 t00 = *reinterpret_cast<const h4*>(&sm.tb[0][r][4 * g4]);
+                const h4 t11 = *reinterpret_cast<const h4*>(&sm.tb[1][r][4 * g4]);
+                const h4 g10 = *reinterpret_cast<const h4*>(&sm.tb[2][r][4 * g4]);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    h4 x0;
+                    f4 x1;
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        wf[m] = static_cast<_Float16>(-wa[0][rt][m]);
-                        wf[4 + m] = static_cast<_Float16>(-wa[1][rt][m]);
+                        x0[m] = static_cast<_Float16>(fmaf(vv[0][ct][m], sig, -y[0][ct][m]));
+                        x1[m] = fmaf(vv[1][ct][m], sig, -y[1][ct][m]);
                     }
+                    const f4 d0 = mfma16k16(t00, x0, f4{0.f, 0.f, 0.f, 0.f});
+                    h4 d0h;
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) dl[rt][ct] = mfma16(wf, s16[ks][ct], dl[rt][ct]);
+                    for (int m = 0; m < 4; ++m) d0h[m] = static_cast<_Float16>(d0[m]);
+                    const f4 z = mfma16k16(g10, d0h, x1);
+                    h4 zh;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) zh[m] = static_cast<_Float16>(z[m]);
+                    const f4 d1 = mfma16k16(t11, zh, f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        d16[ct][m] = d0h[m];
+                        d16[ct][4 + m] = static_cast<_Float16>(d1[m]);
+                    }
                 }
             }
-            h8 d16[NCT];  // B operand (k = tokens, permuted)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    d16[ct][m] = static_cast<_Float16>(dl[0][ct][m]);
-                    d16[ct][4 + m] = static_cast<_Float16>(dl[1][ct][m]);
-                }
 
             // O = scale (Q~ S + P Delta)
             if (!MAP) {
@@ -540,10 +581,8 @@ void chunk_kernel(
                     h8 qf8[4];
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks)
-                        qf8[ks] = cat(*reinterpret_cast<const h4*>(&sm.qt[16 * rt + r][32 * ks + 4 * g4]),
-                                      *reinterpret_cast<const h4*>(&sm.qt[16 * rt + r][32 * ks + 16 + 4 * g4]));
-                    const h8 pf = cat(*reinterpret_cast<const h4*>(&sm.p[16 * rt + r][4 * g4]),
-                                      *reinterpret_cast<const h4*>(&sm.p[16 * rt + r][16 + 4 * g4]));
+                        qf8[ks] = *reinterpret_cast<const h8*>(&sm.qt[16 * rt + r][32 * ks + 8 * g4]);
+                    const h8 pf = *reinterpret_cast<const h8*>(&sm.p[16 * rt + r][8 * g4]);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) {
                         f4 a = mfma16(pf, d16[ct], f4{0.f, 0.f, 0.f, 0.f});
@@ -566,8 +605,7 @@ void chunk_kernel(
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt) {
                 const f4 lam = *reinterpret_cast<const f4*>(&sm.lam[16 * rt + 4 * g4]);
-                const h8 kb = cat(*reinterpret_cast<const h4*>(&sm.kbt[16 * rt + r][4 * g4]),
-                                  *reinterpret_cast<const h4*>(&sm.kbt[16 * rt + r][16 + 4 * g4]));
+                const h8 kb = *reinterpret_cast<const h8*>(&sm.kbt[16 * rt + r][8 * g4]);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb, d16[ct], S[rt][ct] * lam);
             }
@@ -744,7 +782,15 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(
 namespace {
 
 constexpr int kLptMaxSeqs = 16384;
-constexpr int kWaves = 8;  // waves per chain in the full-mode kernel
+#ifndef KDA_CHUNK_WAVES
+#define KDA_CHUNK_WAVES 8
+#endif
+#ifndef KDA_CHUNK_WPC
+#define KDA_CHUNK_WPC 1
+#endif
+constexpr int kWaves = KDA_CHUNK_WAVES;  // waves per chain in the full-mode kernel
+constexpr int kNct = 128 / (16 * kWaves);  // 16-column state tiles per wave
+constexpr int kWpc = KDA_CHUNK_WPC;      // full-mode chains resident per CU
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -784,6 +830,8 @@ ScanLayout scan_layout(int64_t nseg, int64_t nmap, int N, int H) {
 
 }  // namespace
 
+int chunk_chains_per_cu() { return kWpc; }
+
 int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host) {
     // Long sequences are cut so that about four segments (workgroups) per CU
     // exist over all heads; segments are a whole number of chunks.
@@ -811,12 +859,12 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan) {
     auto launch_full = [&](const ChunkItem* items, int64_t nitems, const float* staged) {
         const dim3 grid(static_cast<uint32_t>(nitems * a.H));
         if (a.out_bf16)
-            hipLaunchKernelGGL((chunk_kernel<kWaves, 1, false, bf16_t>), grid, dim3(kWaves * 64), 0,
+            hipLaunchKernelGGL((chunk_kernel<kWaves, kNct, false, kWpc, bf16_t>), grid, dim3(kWaves * 64), 0,
                                a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
                                staged, static_cast<bf16_t*>(a.o), a.hT);
         else
-            hipLaunchKernelGGL((chunk_kernel<kWaves, 1, false, float>), grid, dim3(kWaves * 64), 0,
+            hipLaunchKernelGGL((chunk_kernel<kWaves, kNct, false, kWpc, float>), grid, dim3(kWaves * 64), 0,
                                a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
                                staged, static_cast<float*>(a.o), a.hT);
@@ -841,7 +889,7 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan) {
     hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T, seg,
                        a.h0 ? 1 : 0, a.hT ? 1 : 0, seg_items, map_items, scan_items);
     if (nmap > 0)
-        hipLaunchKernelGGL((chunk_kernel<8, 2, true, float>), dim3(static_cast<uint32_t>(nmap * a.H)),
+        hipLaunchKernelGGL((chunk_kernel<8, 2, true, 1, float>), dim3(static_cast<uint32_t>(nmap * a.H)),
                            dim3(8 * 64), 0, a.stream, static_cast<const uint16_t*>(a.q),
                            static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.g,
                            a.beta, a.scale, map_items, a.H, static_cast<const float*>(nullptr),

@@ -71,6 +71,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 // Chunked MFMA prefill (bf16 inputs, d_k = d_v = 128).  With scan = true long
 // sequences are cut into segments whose (B, M) maps are composed by a scan.
 // cu_host may be null (then the N sequences are rows of length T).
+int chunk_chains_per_cu();  // full-mode chunk workgroups resident per CU
 int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host);
 size_t chunk_workspace_bytes(int B, int T, int H, int N, const int32_t* cu_host, bool scan);
 hipError_t launch_chunk(const PrefillArgs& a, bool scan);
