@@ -22,19 +22,23 @@
 // state [B | M] from [0 | I] (v drives only the B half).
 //
 // Design on this GPU:
-//  * C = 32 tokens per chunk, two 16-token sub-blocks; a workgroup of NW waves
-//    owns one chain segment (one sequence, one head).  Gate-side work (cumulative
-//    gates, Grams, the triangular solve) is split over the waves by sub-block
-//    and channel part; the state pass is split by state columns (columns of S
+//  * A chunk is NSB sub-blocks of 16 tokens (C = 16 NSB; 64 tokens in the
+//    full-mode kernel, 32 in map mode); a workgroup of NW waves owns one chain
+//    segment (one sequence, one head).  Gate-side work (cumulative gates,
+//    Grams, the triangular solves) is split over the waves by sub-block and
+//    channel part; the state pass is split by state columns (columns of S
 //    are independent), 16 NCT columns per wave.
 //  * Gate exponents stay in range: inside a sub-block every factor is taken
-//    relative to the sub-block start, across sub-blocks relative to the end
-//    of the earlier one, so all factors are <= 1 except the in-block
-//    exp(-Gamma) of the diagonal Gram blocks.  Those two diagonal blocks run
-//    on fp32 MFMA straight from the gate registers; every other product runs
-//    on fp16 MFMA with fp32 accumulation.  The kernel needs
-//    the sum of g over any 16 consecutive tokens of a channel to stay above
-//    about -85 (exp of the negated sum must be finite in fp32).
+//    relative to the sub-block start, across sub-blocks relative to sub-block
+//    ends, so every factor is <= 1 except in the diagonal Gram blocks.  Those
+//    take operands referenced to half the sub-block's gate total: fp16 MFMA
+//    when the wave's exponents stay within +-8, fp32 MFMA otherwise.  Every
+//    other product runs on fp16 MFMA with fp32 accumulation.  The kernel
+//    needs the sum of g over any 16 consecutive tokens of a channel to stay
+//    above about -170 (exp of half its negation must be finite in fp32).
+//  * T is kept as its diagonal blocks T_JJ = (I + A_JJ)^-1 Diag(beta_J) and
+//    the raw cross Grams G_JK (A_JK = Diag(beta_J) G_JK); Delta = T X is then
+//    forward block substitution, Delta_J = T_JJ (X_J - sum_K<J G_JK Delta_K).
 //  * S lives in MFMA accumulators for the whole segment; its fp16 copy and
 //    Delta's are fed back as MFMA operands straight from the accumulator
 //    registers, using a k-order permutation that the gate-side operands read
@@ -42,12 +46,7 @@
 //  * Value-side fp16 operands (S, v, Delta) carry a per-wave power-of-two scale
 //    chosen every chunk from max(|S|, |v|), which keeps them inside fp16 range
 //    and away from subnormals; the scale is exact and is removed in fp32.
-//  * Delta is formed as T (v - K~ S): one product with K~ per state column
-//    tile and one with T, instead of building W = T K~ (which every wave
-//    would need in full).
 //  * The next chunk's inputs are fetched into registers during the state pass.
-//  * Register use is held to 128 VGPRs in the full-mode kernel, so that two
-//    chains share a CU and fill each other's barrier and latency stalls.
 #include "dev_common.h"
 #include "kda_internal.h"
 
@@ -70,13 +69,12 @@ struct ScanItem {
 
 namespace chunkk {
 
-constexpr int C = 32;   // tokens per chunk
-constexpr int SB = 16;  // tokens per sub-block
-constexpr int D = 128;  // head size (d_k = d_v)
-constexpr int QP = 136; // row stride (halves) of [token][channel] tiles
-constexpr int TP = 40;  // row stride (halves) of [x][token] tiles
-constexpr int GP = 18;  // row stride (floats) of 16x16 Gram tiles
-constexpr int BP = 20;  // row stride (halves) of 16x16 fp16 blocks
+constexpr int SB = 16;    // tokens per sub-block
+constexpr int CSEG = 64;  // segment boundaries are multiples of every chunk size
+constexpr int D = 128;    // head size (d_k = d_v)
+constexpr int QP = 136;   // row stride (halves) of [token][channel] tiles
+constexpr int GP = 20;    // row stride (floats) of 16x16 Gram tiles (16-byte rows)
+constexpr int BP = 20;    // row stride (halves) of 16x16 fp16 blocks
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -84,30 +82,37 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-// MFMA A operands read from LDS ([row][k] tiles with k = 32 channels or 32
-// tokens per block) store each 32-wide k block in operand order: position
+// MFMA A operands read from LDS ([row][k] tiles with k = channels or tokens
+// in 32-wide blocks) store each 32-wide k block in operand order: position
 // 8 j + m holds k index 4 j + m (m < 4) or 16 + 4 j + m - 4 (m >= 4), the
 // order in which the B operands built from accumulator registers come.  A
 // lane's 8 k values are then one aligned 16-byte read.
-__device__ __forceinline__ int kpos(int c) { return 8 * ((c & 15) >> 2) + 4 * (c >> 4) + (c & 3); }
+__device__ __forceinline__ int kpos(int c) {
+    return (c & ~31) + 8 * ((c & 15) >> 2) + 4 * ((c >> 4) & 1) + (c & 3);
+}
 
-// Gram tiles: A00, P00, A11, P11, A10, P10.
-enum { GA00 = 0, GP00 = 1, GA11 = 2, GP11 = 3, GA10 = 4, GP10 = 5 };
+// Cross (off-diagonal) sub-block pair (I, J), I > J, in row order.
+__host__ __device__ constexpr int xidx(int I, int J) { return I * (I - 1) / 2 + J; }
 
-// Per-workgroup LDS; NP = channel parts per sub-block (one Gram partial each).
-template <int NP>
+// Per-workgroup LDS for NSB sub-blocks and NP channel parts per sub-block
+// (one Gram partial each).  Gram tiles: 2 J (A_JJ), 2 J + 1 (P_JJ), then
+// 2 NSB + 2 x (G_x) and 2 NSB + 2 x + 1 (P_x) for cross pair x.
+template <int NSB, int NP>
 struct alignas(16) Smem {
-    _Float16 qt[C][QP];      // Q~ = Lambda q                 [token][channel, operand order]
-    _Float16 kt[C][QP];      // K~ = Lambda k                 [token][channel, operand order]
-    _Float16 kbt[D][TP];     // K-bar^T                       [channel][token, operand order]
-    _Float16 r0[SB][QP];     // k exp(Gamma_end0 - Gamma), tokens 0..15   [token][channel]
-    _Float16 tb[3][SB][BP];  // T00, T11 = X_JJ Diag(beta_J) and -G10 (raw cross Gram)  [token][token]
-    _Float16 p[C][TP];       // P                             [token][token, operand order]
-    uint16_t v[C][QP];       // v tile (bf16 bits)            [token][column]
-    float gp[NP][6][SB][GP]; // Gram partial sums, one per channel part
-    float a[2][SB][20];      // A_II^T: column m of Diag(beta) Gram in row m
-    float etot[2][D];        // per-channel exp(sum of g over each sub-block)
-    float lam[D];            // Lambda_last = exp(Gamma over the chunk)
+    static constexpr int C = 16 * NSB;
+    static constexpr int NX = NSB * (NSB - 1) / 2;
+    static constexpr int TP = C + 8;  // row stride (halves) of [x][token] tiles
+    _Float16 qt[C][QP];                // Q~ = Lambda q        [token][channel, operand order]
+    _Float16 kt[C][QP];                // K~ = Lambda k        [token][channel, operand order]
+    _Float16 kbt[D][TP];               // K-bar^T              [channel][token, operand order]
+    _Float16 rbs[NSB - 1][SB][QP];     // k exp(tot_J - G) of sub-blocks 0 .. NSB-2   [token][channel]
+    _Float16 tb[NSB + NX][SB][BP];     // T_JJ, then -G_x (raw cross Grams)           [token][token]
+    _Float16 p[C][TP];                 // P                    [token][token, operand order]
+    uint16_t v[C][QP];                 // v tile (bf16 bits)   [token][column]
+    float gp[NP][2 * NSB + 2 * NX][SB][GP];
+    float a[NSB][SB][20];              // A_JJ^T: column m of Diag(beta) Gram in row m
+    float etot[NSB][D];                // per-channel exp(sum of g over each sub-block)
+    float lam[D];                      // Lambda_last = exp(Gamma over the chunk)
     float beta[C];
 };
 
@@ -152,6 +157,25 @@ __device__ __forceinline__ float wave_max_nonneg(float m) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (a uniform address); the
+// per-lane part of an access goes in a 32-bit vector offset, so no 64-bit
+// per-lane address has to stay live across the chunk loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u4 bload16(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+__device__ __forceinline__ float bload4(__amdgpu_buffer_rsrc_t r, int voff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x, float*) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+}
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x, bf16_t*) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, voff, soff, 0);
+}
+
 __device__ __forceinline__ h8 cat(h4 a, h4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -174,11 +198,11 @@ __device__ __forceinline__ int value_exponent(float mx, int ex) {
     return e < -120 ? -120 : (e > 120 ? 120 : e);
 }
 
-// NW waves; each owns NCT 16-column tiles of the state.  Full mode: state = S
-// (NW * 16 NCT = 128 columns), writes o and the final state.  Map mode: state
-// = [B | M] (256 columns), no o, writes the segment's (B, M).  WPC workgroups
-// share a CU (it sets the register budget per wave).
-template <int NW, int NCT, bool MAP, int WPC, typename Tout>
+// NW waves; each owns NCT 16-column tiles of the state; chunks of NSB
+// sub-blocks.  Full mode: state = S (NW * 16 NCT = 128 columns), writes o and
+// the final state.  Map mode: state = [B | M] (256 columns), no o, writes the
+// segment's (B, M).  WPC workgroups share a CU (it sets the register budget).
+template <int NW, int NSB, int NCT, bool MAP, int WPC, typename Tout>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4 * WPC)))
 void chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -186,23 +210,27 @@ void chunk_kernel(
     const float* __restrict__ beta, float scale, const ChunkItem* __restrict__ items, int H,
     const float* __restrict__ h0, const float* __restrict__ staged, Tout* __restrict__ o,
     float* __restrict__ out_state) {
-    constexpr int NP = NW / 2;      // channel parts per sub-block
-    constexpr int CPG = D / NP;     // channels per gate wave
-    constexpr int KS = CPG / 32;    // 32-channel k-steps per gate wave
-    constexpr int CPW = 16 * NCT;   // state columns per wave
-    constexpr int NT = NW * 64;     // threads
+    constexpr int C = 16 * NSB;         // tokens per chunk
+    constexpr int NP = NW / NSB;        // channel parts per sub-block
+    constexpr int CPG = D / NP;         // channels per gate wave
+    constexpr int KS = CPG / 32;        // 32-channel k-steps per gate wave
+    constexpr int NKB = C / 32;         // 32-token k blocks of a chunk
+    constexpr int CPW = 16 * NCT;       // state columns per wave
+    constexpr int NT = NW * 64;         // threads
     constexpr int VU = (C * D / 8) / NT;  // 16-byte pieces of the v tile per thread
-    static_assert(KS >= 1 && VU >= 1, "unsupported wave count");
+    constexpr int NX = NSB * (NSB - 1) / 2;
+    static_assert(NSB == 2 || NSB == 4, "chunks of 32 or 64 tokens");
+    static_assert(NP >= 1 && NW % NSB == 0 && KS >= 1 && VU >= 1 && NW > NSB, "unsupported wave split");
     static_assert(MAP ? NW * CPW == 2 * D : NW * CPW == D, "state columns must match the mode");
-    __shared__ Smem<NP> sm;
+    __shared__ Smem<NSB, NP> sm;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave (uniform: scalar register)
     const int l = tid & 63;      // lane
     const int r = l & 15;        // MFMA row / column index
     const int g4 = l >> 4;       // MFMA k group
-    const int I = w / NP;        // gate phase: sub-block of this wave
-    const int part = w % NP;     // gate phase: channel part of this wave
+    const int I = w / NP;        // gate phases: sub-block of this wave
+    const int part = w % NP;     // gate phases: channel part of this wave
 
     const ChunkItem it = items[blockIdx.x / H];
     const int h = blockIdx.x % H;
@@ -284,12 +312,10 @@ void chunk_kernel(
             constexpr float LOG2E = 1.4426950408889634f;
             // Diagonal Gram operands are referenced to half the sub-block total,
             // k exp(G - tot/2) and k exp(tot/2 - G) (their products are unchanged).
-            // A wave whose exponents all stay within +-8 (natural units) feeds them
-            // to fp16 MFMA; otherwise it keeps fp32 range on fp32 MFMA.
+            // A k-step whose exponents all stay within +-8 (natural units) over
+            // the wave feeds them to fp16 MFMA; otherwise fp32 MFMA keeps fp32 range.
             constexpr float FAST_SPAN = 8.f * LOG2E;
             f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-            float La[KS][8], Ra[KS][8], Qa[KS][8];
-            float span = 0.f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = CPG * part + 32 * ks + 8 * g4;
@@ -301,7 +327,8 @@ void chunk_kernel(
                 for (int m = 0; m < 8; ++m) G[m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
 #pragma unroll
                 for (int m = 0; m < 8; ++m) Gt[m] = __shfl(G[m], 15, 16);
-                float e1[8];
+                float e1[8], La[8], Ra[8], Qa[8];
+                float span = 0.f;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
                     e1[m] = __builtin_amdgcn_exp2f(G[m]);                      // exp(G) <= 1
@@ -311,42 +338,37 @@ void chunk_kernel(
                     const float L = kf[m] * e1[m], rb = kf[m] * e3;
                     l16[ks][m] = static_cast<_Float16>(L);
                     rb16[ks][m] = static_cast<_Float16>(rb);
-                    La[ks][m] = L * hm;
-                    Ra[ks][m] = rb * hm;
+                    La[m] = L * hm;
+                    Ra[m] = rb * hm;
                     if (!MAP) {
                         const float Lq = qf[m] * e1[m];
                         q16[ks][m] = static_cast<_Float16>(Lq);
-                        Qa[ks][m] = Lq * hm;
+                        Qa[m] = Lq * hm;
+                    }
+                }
+                if (wave_max_nonneg(span) <= FAST_SPAN) {  // wave-uniform
+                    h8 la, ra, qa;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        la[m] = static_cast<_Float16>(La[m]);
+                        ra[m] = static_cast<_Float16>(Ra[m]);
+                        if (!MAP) qa[m] = static_cast<_Float16>(Qa[m]);
+                    }
+                    accA = mfma16(la, ra, accA);
+                    if (!MAP) accP = mfma16(qa, ra, accP);
+                } else {
+                    // MFMA m contracts channel 8 g4 + m (k index g4).
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        accA = mfma4(La[m], Ra[m], accA);
+                        if (!MAP) accP = mfma4(Qa[m], Ra[m], accP);
                     }
                 }
                 if (r == 15) {  // exp(sum of g over the sub-block)
                     *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{e1[0], e1[1], e1[2], e1[3]};
                     *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{e1[4], e1[5], e1[6], e1[7]};
                 }
-                if (I == 0) *reinterpret_cast<h8*>(&sm.r0[r][ch]) = rb16[ks];
-            }
-            if (wave_max_nonneg(span) <= FAST_SPAN) {  // wave-uniform
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    h8 la, ra, qa;
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        la[m] = static_cast<_Float16>(La[ks][m]);
-                        ra[m] = static_cast<_Float16>(Ra[ks][m]);
-                        if (!MAP) qa[m] = static_cast<_Float16>(Qa[ks][m]);
-                    }
-                    accA = mfma16(la, ra, accA);
-                    if (!MAP) accP = mfma16(qa, ra, accP);
-                }
-            } else {
-                // MFMA m contracts channel 8 g4 + m (k index g4).
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        accA = mfma4(La[ks][m], Ra[ks][m], accA);
-                        if (!MAP) accP = mfma4(Qa[ks][m], Ra[ks][m], accP);
-                    }
+                if (I < NSB - 1) *reinterpret_cast<h8*>(&sm.rbs[I][r][ch]) = rb16[ks];
             }
             // Row 4 g4 + i of the Gram tile is token 4 g4 + i of the sub-block: scale A by its beta.
 #pragma unroll
@@ -361,27 +383,45 @@ void chunk_kernel(
 
         // ---------------- gate phase 2: chunk-referenced operands, cross-block Grams, v
         {
-            f4 a10 = {0.f, 0.f, 0.f, 0.f}, p10 = {0.f, 0.f, 0.f, 0.f};
+            f4 ax[NSB - 1], px[NSB - 1];  // cross Grams with sub-blocks J < I
+#pragma unroll
+            for (int J = 0; J < NSB - 1; ++J) ax[J] = px[J] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = CPG * part + 32 * ks + 8 * g4;
-                // exp(sum of g over the other sub-block) as fp16 (<= 1; an underflow
-                // to zero drops terms below 2^-24 of the kept ones).
-                // Sub-block 0: Gamma_r = G, K-bar needs exp(tot1); sub-block 1:
-                // Gamma_r = tot0 + G, so Q~ and K~ take exp(tot0).
-                const f4 oa = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch]);
-                const f4 ob = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch + 4]);
-                const h8 of = {static_cast<_Float16>(oa[0]), static_cast<_Float16>(oa[1]),
-                               static_cast<_Float16>(oa[2]), static_cast<_Float16>(oa[3]),
-                               static_cast<_Float16>(ob[0]), static_cast<_Float16>(ob[1]),
-                               static_cast<_Float16>(ob[2]), static_cast<_Float16>(ob[3])};
-                h8 kv = l16[ks], qv = q16[ks], bv = rb16[ks];
-                if (I == 1) {
-                    kv *= of;
-                    if (!MAP) qv *= of;
-                } else {
-                    bv *= of;
+                // Per-channel exp(sum of g) of every sub-block; products of these
+                // (all <= 1, an fp16 underflow to zero drops terms below 2^-24 of
+                // the kept ones) move the sub-block's factors to chunk reference:
+                // Q~, K~ take those of the sub-blocks before I, K-bar those after.
+                float et[NSB][8];
+#pragma unroll
+                for (int J = 0; J < NSB; ++J) {
+                    const f4 a0 = *reinterpret_cast<const f4*>(&sm.etot[J][ch]);
+                    const f4 a1 = *reinterpret_cast<const f4*>(&sm.etot[J][ch + 4]);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        et[J][m] = a0[m];
+                        et[J][4 + m] = a1[m];
+                    }
                 }
+                h8 fb, fa;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    float pb = 1.f, pa = 1.f;
+#pragma unroll
+                    for (int J = 0; J < NSB; ++J) {
+                        if (J < I) pb *= et[J][m];
+                        if (J > I) pa *= et[J][m];
+                    }
+                    fb[m] = static_cast<_Float16>(pb);
+                    fa[m] = static_cast<_Float16>(pa);
+                }
+                h8 kv = l16[ks], qv = q16[ks], bv = rb16[ks];
+                if (I > 0) {
+                    kv *= fb;
+                    if (!MAP) qv *= fb;
+                }
+                if (I < NSB - 1) bv *= fa;
                 // channels 8 g4 .. 8 g4 + 7 of the block go to two 4-wide runs
                 const int cb = ch & ~31, p0 = cb + (g4 < 2 ? 16 * g4 : 16 * g4 - 28), p1 = p0 + 8;
                 *reinterpret_cast<h4*>(&sm.kt[tok][p0]) = __builtin_shufflevector(kv, kv, 0, 1, 2, 3);
@@ -393,21 +433,47 @@ void chunk_kernel(
                 const int tp = kpos(tok);
 #pragma unroll
                 for (int m = 0; m < 8; ++m) sm.kbt[ch + m][tp] = bv[m];
-                if (I == 1) {
-                    const h8 rv = *reinterpret_cast<const h8*>(&sm.r0[r][ch]);
-                    a10 = mfma16(l16[ks], rv, a10);
-                    if (!MAP) p10 = mfma16(q16[ks], rv, p10);
-                }
-            }
-            if (I == 1) {
+                // Cross Grams G_IJ (J < I): k exp(G) of I against k exp(tot_J - G) of J
+                // times the totals of the sub-blocks strictly between them.
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sm.gp[part][GA10][4 * g4 + i][r] = a10[i];  // raw (beta is applied in the state pass)
-                    if (!MAP) sm.gp[part][GP10][4 * g4 + i][r] = p10[i];
+                for (int J = 0; J < NSB - 1; ++J) {
+                    if (J < I) {
+                        h8 rv = *reinterpret_cast<const h8*>(&sm.rbs[J][r][ch]);
+                        if (J + 1 < I) {
+                            h8 fm;
+#pragma unroll
+                            for (int m = 0; m < 8; ++m) {
+                                float pm = 1.f;
+#pragma unroll
+                                for (int K = 1; K < NSB - 1; ++K)
+                                    if (K > J && K < I) pm *= et[K][m];
+                                fm[m] = static_cast<_Float16>(pm);
+                            }
+                            rv *= fm;
+                        }
+                        ax[J] = mfma16(l16[ks], rv, ax[J]);
+                        if (!MAP) px[J] = mfma16(q16[ks], rv, px[J]);
+                    }
                 }
             }
-            if (tid < D) sm.lam[tid] = sm.etot[0][tid] * sm.etot[1][tid];
-            for (int e = tid; e < 2 * SB * SB; e += NT) {
+#pragma unroll
+            for (int J = 0; J < NSB - 1; ++J) {
+                if (J < I) {
+                    const int x = xidx(I, J);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sm.gp[part][2 * NSB + 2 * x][4 * g4 + i][r] = ax[J][i];  // raw (beta applied in the state pass)
+                        if (!MAP) sm.gp[part][2 * NSB + 2 * x + 1][4 * g4 + i][r] = px[J][i];
+                    }
+                }
+            }
+            if (tid < D) {
+                float lm = 1.f;
+#pragma unroll
+                for (int J = 0; J < NSB; ++J) lm *= sm.etot[J][tid];
+                sm.lam[tid] = lm;
+            }
+            for (int e = tid; e < NSB * SB * SB; e += NT) {
                 const int J = e >> 8, i = (e >> 4) & 15, m = e & 15;
                 float s = 0.f;
 #pragma unroll
@@ -422,8 +488,8 @@ void chunk_kernel(
         }
         __syncthreads();  // B2
 
-        // ---------------- solve: diagonal block inverses (waves 0, 1), P and zero fill (others)
-        if (w < 2) {
+        // ---------------- solve: diagonal block inverses (waves 0 .. NSB-1); P and -G_x (others)
+        if (w < NSB) {
             const int J = w;  // diagonal block
             const int j = r;  // column of the inverse owned by this lane
             // Column j of (I + A_JJ)^-1 by forward substitution, column-oriented:
@@ -453,26 +519,51 @@ void chunk_kernel(
                 for (int i = 0; i < SB; ++i) sm.tb[J][i][j] = static_cast<_Float16>(xcol[i] * bj);
             }
         } else {
-            const int t2 = tid - 128;
-            constexpr int NT2 = NT - 128;
-            if (!MAP) {
-                for (int e = t2; e < C * C; e += NT2) {
-                    const int R = e >> 5, Cc = e & 31;
-                    float val = 0.f;
-                    if (Cc <= R) {
-                        const int tile = R < SB ? GP00 : (Cc >= SB ? GP11 : GP10);
-                        const int rr = R & 15, cc = Cc & 15;
+            // Sums of the channel-part partials, 4 consecutive entries per step:
+            // P (causal blocks, plus the zero blocks inside the 32-token k blocks
+            // that the state pass reads) as fp16 in operand order, and -G_x.
+            const int t2 = tid - 64 * NSB;
+            constexpr int NT2 = NT - 64 * NSB;
+            constexpr int NPB = NSB + NX + NKB;  // P blocks written: diagonal, cross, upper-in-k-block
+            constexpr int NQ = (MAP ? 0 : NPB * 64) + NX * 64;  // 4-entry quads
 #pragma unroll
-                        for (int pp = 0; pp < NP; ++pp) val += sm.gp[pp][tile][rr][cc];
+            for (int q0 = 0; q0 < NQ; q0 += NT2) {
+                const int qi = q0 + t2;
+                if (qi < NQ) {
+                    const int blk = qi >> 6, i = (qi >> 2) & 15, m4 = (qi & 3) * 4;
+                    const bool isp = !MAP && blk < NPB;
+                    int tile = -1, bi = 0, bj = 0;
+                    if (isp) {
+                        if (blk < NSB) { bi = bj = blk; tile = 2 * blk + 1; }
+                        else if (blk < NSB + NX) {
+                            const int x = blk - NSB;
+                            bi = 1; while (xidx(bi + 1, 0) <= x) ++bi;
+                            bj = x - xidx(bi, 0);
+                            tile = 2 * NSB + 2 * x + 1;
+                        } else { bi = 2 * (blk - NSB - NX); bj = bi + 1; }  // upper block of a 32-token k block
+                    } else {
+                        tile = 2 * NSB + 2 * (blk - (MAP ? 0 : NPB));
                     }
-                    sm.p[R][kpos(Cc)] = static_cast<_Float16>(val);
-                }
-            }
-            for (int e = t2; e < SB * SB; e += NT2) {
-                float val = 0.f;
+                    f4 val = {0.f, 0.f, 0.f, 0.f};
+                    if (tile >= 0) {
 #pragma unroll
-                for (int pp = 0; pp < NP; ++pp) val += sm.gp[pp][GA10][e >> 4][e & 15];
-                sm.tb[2][e >> 4][e & 15] = static_cast<_Float16>(-val);
+                        for (int pp = 0; pp < NP; ++pp) val += *reinterpret_cast<const f4*>(&sm.gp[pp][tile][i][m4]);
+                    }
+                    if (isp) {
+                        h4 hv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            hv[e] = static_cast<_Float16>((bi > bj || m4 + e <= i) ? val[e] : 0.f);
+                        const int R = 16 * bi + i;
+                        *reinterpret_cast<h4*>(&sm.p[R][kpos(16 * bj + m4)]) = hv;
+                    } else {
+                        const int x = blk - (MAP ? 0 : NPB);
+                        h4 hv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(-val[e]);
+                        *reinterpret_cast<h4*>(&sm.tb[NSB + x][i][m4]) = hv;
+                    }
+                }
             }
         }
         __syncthreads();  // B3
@@ -481,9 +572,9 @@ void chunk_kernel(
         if (c0 + C < t1) fetch(c0 + C);
         {
             // v at token 16 rt + 4 g4 + i, column col + 16 ct + r (accumulator layout).
-            float vv[2][NCT][4];
+            float vv[NSB][NCT][4];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < NSB; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -492,7 +583,7 @@ void chunk_kernel(
             // Exponent for this chunk from max(|S|, |v|) over the wave's columns.
             float mv = 0.f;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < NSB; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -526,14 +617,13 @@ void chunk_kernel(
                         s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
                     }
 
-            // X = sigma v - K~ S (fp32), then Delta = T X (scaled units) by blocks:
-            // Delta_0 = T00 X_0 and Delta_1 = T11 (X_1 - G10 Delta_0), which is
-            // T X for T = (I + A)^-1 Diag(beta) with A10 = Diag(beta_1) G10.
-            h8 d16[NCT];  // B operand of P Delta and K-bar^T Delta (k = tokens, permuted)
+            // X = sigma v - K~ S (fp32), then Delta = T X (scaled units) by forward
+            // block substitution: Delta_J = T_JJ (X_J - sum_{K<J} G_JK Delta_K).
+            h4 dh[NSB][NCT];  // Delta_J as fp16 (rows 4 g4 + i of sub-block J)
             {
-                f4 y[2][NCT];
+                f4 y[NSB][NCT];
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
+                for (int rt = 0; rt < NSB; ++rt) {
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) y[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -543,49 +633,53 @@ void chunk_kernel(
                         for (int ct = 0; ct < NCT; ++ct) y[rt][ct] = mfma16(kf8, s16[ks][ct], y[rt][ct]);
                     }
                 }
-                const h4 t00 = *reinterpret_cast<const h4*>(&sm.tb[0][r][4 * g4]);
-                const h4 t11 = *reinterpret_cast<const h4*>(&sm.tb[1][r][4 * g4]);
-                const h4 g10 = *reinterpret_cast<const h4*>(&sm.tb[2][r][4 * g4]);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    h4 x0;
-                    f4 x1;
+                for (int J = 0; J < NSB; ++J) {
+                    const h4 tjj = *reinterpret_cast<const h4*>(&sm.tb[J][r][4 * g4]);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        x0[m] = static_cast<_Float16>(fmaf(vv[0][ct][m], sig, -y[0][ct][m]));
-                        x1[m] = fmaf(vv[1][ct][m], sig, -y[1][ct][m]);
-                    }
-                    const f4 d0 = mfma16k16(t00, x0, f4{0.f, 0.f, 0.f, 0.f});
-                    h4 d0h;
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        f4 z;
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) d0h[m] = static_cast<_Float16>(d0[m]);
-                    const f4 z = mfma16k16(g10, d0h, x1);
-                    h4 zh;
+                        for (int m = 0; m < 4; ++m) z[m] = fmaf(vv[J][ct][m], sig, -y[J][ct][m]);
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) zh[m] = static_cast<_Float16>(z[m]);
-                    const f4 d1 = mfma16k16(t11, zh, f4{0.f, 0.f, 0.f, 0.f});
+                        for (int K = 0; K < NSB - 1; ++K) {
+                            if (K < J) {
+                                const h4 gjk = *reinterpret_cast<const h4*>(&sm.tb[NSB + xidx(J, K)][r][4 * g4]);
+                                z = mfma16k16(gjk, dh[K][ct], z);
+                            }
+                        }
+                        h4 zh;
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        d16[ct][m] = d0h[m];
-                        d16[ct][4 + m] = static_cast<_Float16>(d1[m]);
+                        for (int m = 0; m < 4; ++m) zh[m] = static_cast<_Float16>(z[m]);
+                        const f4 d = mfma16k16(tjj, zh, f4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) dh[J][ct][m] = static_cast<_Float16>(d[m]);
                     }
                 }
             }
+            h8 d16[NKB][NCT];  // B operand of P Delta and K-bar^T Delta (k = 32 tokens, permuted)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) d16[kb][ct] = cat(dh[2 * kb][ct], dh[2 * kb + 1][ct]);
 
             // O = scale (Q~ S + P Delta)
             if (!MAP) {
                 const float os = scale * ldexpf(1.f, -ex);
+            const int vlim = valid - 4 * g4;  // rows of this lane group still inside the chunk
                 const int64_t stride = static_cast<int64_t>(H) * D;
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
+                for (int rt = 0; rt < NSB; ++rt) {
                     h8 qf8[4];
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks)
                         qf8[ks] = *reinterpret_cast<const h8*>(&sm.qt[16 * rt + r][32 * ks + 8 * g4]);
-                    const h8 pf = *reinterpret_cast<const h8*>(&sm.p[16 * rt + r][8 * g4]);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) {
-                        f4 a = mfma16(pf, d16[ct], f4{0.f, 0.f, 0.f, 0.f});
+                        f4 a = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kb = 0; kb <= rt / 2; ++kb)  // P is causal: k blocks up to this row's
+                            a = mfma16(*reinterpret_cast<const h8*>(&sm.p[16 * rt + r][32 * kb + 8 * g4]), d16[kb][ct], a);
 #pragma unroll
                         for (int ks = 0; ks < 4; ++ks) a = mfma16(qf8[ks], s16[ks][ct], a);
                         Tout* op = o + ((c0 + 16 * rt + 4 * g4) * H + h) * D + col + 16 * ct + r;
@@ -595,7 +689,7 @@ void chunk_kernel(
                         } else {
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                if (16 * rt + 4 * g4 + i < valid) st(op, i * stride, a[i] * os);
+                                if (16 * rt + i < vlim) st(op, i * stride, a[i] * os);
                         }
                     }
                 }
@@ -605,9 +699,14 @@ void chunk_kernel(
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt) {
                 const f4 lam = *reinterpret_cast<const f4*>(&sm.lam[16 * rt + 4 * g4]);
-                const h8 kb = *reinterpret_cast<const h8*>(&sm.kbt[16 * rt + r][8 * g4]);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb, d16[ct], S[rt][ct] * lam);
+                for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= lam;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const h8 kb8 = *reinterpret_cast<const h8*>(&sm.kbt[16 * rt + r][32 * kb + 8 * g4]);
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb8, d16[kb][ct], S[rt][ct]);
+                }
             }
         }
     }
@@ -625,6 +724,482 @@ void chunk_kernel(
                 for (int i = 0; i < 4; ++i)
                     dst[(16 * rt + 4 * g4 + i) * ld + colg + 16 * ct + r] = S[rt][ct][i] * un;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Full-mode kernel with wave roles: 32-token chunks (two sub-blocks); waves
+// 0-3 run the state pass of chunk c on 32 state columns each while waves
+// 4-11 prepare chunk c+1 (cumulative gates, Grams, the diagonal solves, P and
+// the cross Grams) into the other half of double-buffered operand tiles.
+// Each SIMD then holds one MFMA/LDS-heavy state wave and two VALU-heavy gate
+// waves of the same chain, and every A operand is read from LDS by 4 waves.
+namespace ws {
+constexpr int C = 32, NSB = 2, NX = 1, TP = C + 8;
+constexpr int NSW = 4;   // state waves
+constexpr int NGW = 8;   // gate waves
+constexpr int NW = NSW + NGW;
+constexpr int NCT = 2;   // 16-column tiles per state wave
+constexpr int NP = NGW / NSB;  // channel parts per sub-block (gate waves per sub-block)
+constexpr int CPG = D / NP, KS = CPG / 32;
+constexpr int GT = NGW * 64;            // gate threads
+constexpr int VU = (C * D / 8) / GT;    // 16-byte pieces of the v tile per gate thread
+
+struct alignas(16) Tiles {               // operands of one chunk's state pass
+    _Float16 qt[C][QP];                  // Q~   [token][channel, operand order]
+    _Float16 kt[C][QP];                  // K~   [token][channel, operand order]
+    _Float16 kbt[D][TP];                 // K-bar^T [channel][token, operand order]
+    _Float16 tb[NSB + NX][SB][BP];       // T00, T11, -G10
+    _Float16 p[C][TP];                   // P    [token][token, operand order]
+    uint16_t v[C][QP];                   // v tile (bf16 bits) [token][column]
+    float lam[D];                        // Lambda_last
+};
+struct alignas(16) Smem {
+    Tiles tl[2];
+    _Float16 rbs[SB][QP];                // k exp(tot_0 - G), sub-block 0 [token][channel]
+    float gp[NP][2 * NSB + 2 * NX][SB][GP];
+    float a[NSB][SB][20];                // A_JJ^T
+    float etot[NSB][D];
+    float beta[C];
+};
+}  // namespace ws
+
+template <typename Tout>
+__global__ __launch_bounds__(ws::NW * 64) __attribute__((amdgpu_waves_per_eu(ws::NW / 4)))
+void chunk_ws_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, float scale, const ChunkItem* __restrict__ items, int H,
+    const float* __restrict__ h0, const float* __restrict__ staged, Tout* __restrict__ o,
+    float* __restrict__ out_state) {
+    using namespace ws;
+    __shared__ ws::Smem sm;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, r = l & 15, g4 = l >> 4;
+    const bool gate = w >= NSW;  // wave-uniform role
+
+    const ChunkItem it = items[blockIdx.x / H];
+    const int h = blockIdx.x % H;
+    const int64_t t0 = it.t0, t1 = it.t1;
+    const int nch = static_cast<int>((t1 - t0 + C - 1) / C);
+
+    // ---- state waves: S[16 rt + 4 g4 + i][col + 16 ct + r] * 2^ex in S[rt][ct][i]
+    const int col = 32 * (w & 3);
+    f4 S[8][NCT];
+    int ex = 0;
+    h8 d16[NCT];      // fp16 Delta (B operand of P Delta, K-bar^T Delta), chunk-local
+    if (!gate) {
+        const float* src = nullptr;
+        if (it.sin >= 0 && h0) src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
+        else if (it.sin <= -2) src = staged + (static_cast<int64_t>(-it.sin - 2) * H + h) * D * D;
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+        if (src) {
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
+        }
+    }
+
+    // ---- gate waves: sub-block I, channel part `part`; raw inputs fetched ahead
+    const int gw = w - NSW;
+    const int I = gw / NP, part = gw % NP;
+    const int gtid = tid - NSW * 64;
+    const int tok = SB * I + r;
+    u4 kw[KS], qw[KS], vp[VU];
+    f4 ga[KS], gb[KS];
+    float bt = 0.f;
+    const int rowe = H * D;  // elements per token row
+    auto fetch_gate = [&](int64_t cs) {  // k, q, g, beta of this lane's token
+        const int vld = static_cast<int>(t1 - cs < C ? t1 - cs : C);
+        const bool in = tok < vld;
+        const int64_t cb = (cs * H + h) * D;
+        const auto rk = rsrc(k + cb, static_cast<uint32_t>(vld) * rowe * 2);
+        const auto rq = rsrc(q + cb, static_cast<uint32_t>(vld) * rowe * 2);
+        const auto rg = rsrc(g + cb, static_cast<uint32_t>(vld) * rowe * 4);
+        const auto rb = rsrc(beta + cs * H + h, static_cast<uint32_t>(vld) * H * 4);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
+            kw[ks] = qw[ks] = u4{0, 0, 0, 0};
+            ga[ks] = gb[ks] = f4{0.f, 0.f, 0.f, 0.f};
+            if (in) {
+                kw[ks] = bload16(rk, 2 * off);
+                qw[ks] = bload16(rq, 2 * off);
+                const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
+                ga[ks] = f4{__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]), __uint_as_float(a0[3])};
+                gb[ks] = f4{__uint_as_float(a1[0]), __uint_as_float(a1[1]), __uint_as_float(a1[2]), __uint_as_float(a1[3])};
+            }
+        }
+        bt = in ? bload4(rb, 4 * tok * H) : 0.f;
+    };
+    auto fetch_v = [&](int64_t cs) {
+        const int vld = static_cast<int>(t1 - cs < C ? t1 - cs : C);
+        const auto rv = rsrc(v + (cs * H + h) * D, static_cast<uint32_t>(vld) * rowe * 2);
+#pragma unroll
+        for (int j = 0; j < VU; ++j) {
+            const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
+            vp[j] = u4{0, 0, 0, 0};
+            if (vt < vld) vp[j] = bload16(rv, 2 * (vt * rowe + vc));
+        }
+    };
+    if (gate && nch > 0) {
+        fetch_gate(t0);
+        fetch_v(t0);
+    }
+    h8 l16[KS], q16[KS], rb16[KS];  // gate registers carried from phase 1 to phase 2
+
+    // The two roles run separate loops with the same trip count and exactly
+    // three barriers per iteration (the barriers pair up across the roles).
+    if (gate) {
+        for (int c = -1; c < nch; ++c) {
+            const bool gwork = c + 1 < nch;   // prepare chunk c + 1
+            const int64_t c0 = t0 + static_cast<int64_t>(c) * C;
+            const Tiles& cur = sm.tl[c & 1];
+            Tiles& nxt = sm.tl[(c + 1) & 1];
+
+            if (gwork) {
+                constexpr float LOG2E = 1.4426950408889634f;
+                constexpr float FAST_SPAN = 8.f * LOG2E;
+                f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int ch = CPG * part + 32 * ks + 8 * g4;
+                    float kf[8], qf[8], G[8], Gt[8];
+                    unpack_bf16x8(kw[ks], kf);
+                    unpack_bf16x8(qw[ks], qf);
+    #pragma unroll
+                    for (int m = 0; m < 8; ++m) G[m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
+    #pragma unroll
+                    for (int m = 0; m < 8; ++m) Gt[m] = __shfl(G[m], 15, 16);
+                    float e1[8], La[8], Ra[8], Qa[8];
+                    float span = 0.f;
+    #pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        e1[m] = __builtin_amdgcn_exp2f(G[m]);
+                        const float e3 = __builtin_amdgcn_exp2f(Gt[m] - G[m]);
+                        const float hm = __builtin_amdgcn_exp2f(-0.5f * Gt[m]);
+                        span = fmaxf(span, fabsf(G[m] - 0.5f * Gt[m]));
+                        const float L = kf[m] * e1[m], rb = kf[m] * e3, Lq = qf[m] * e1[m];
+                        l16[ks][m] = static_cast<_Float16>(L);
+                        rb16[ks][m] = static_cast<_Float16>(rb);
+                        q16[ks][m] = static_cast<_Float16>(Lq);
+                        La[m] = L * hm;
+                        Ra[m] = rb * hm;
+                        Qa[m] = Lq * hm;
+                    }
+                    if (wave_max_nonneg(span) <= FAST_SPAN) {
+                        h8 la, ra, qa;
+    #pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            la[m] = static_cast<_Float16>(La[m]);
+                            ra[m] = static_cast<_Float16>(Ra[m]);
+                            qa[m] = static_cast<_Float16>(Qa[m]);
+                        }
+                        accA = mfma16(la, ra, accA);
+                        accP = mfma16(qa, ra, accP);
+                    } else {
+    #pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            accA = mfma4(La[m], Ra[m], accA);
+                            accP = mfma4(Qa[m], Ra[m], accP);
+                        }
+                    }
+                    if (r == 15) {
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{e1[0], e1[1], e1[2], e1[3]};
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{e1[4], e1[5], e1[6], e1[7]};
+                    }
+                    if (I == 0) *reinterpret_cast<h8*>(&sm.rbs[r][ch]) = rb16[ks];
+                }
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float bi = __shfl(bt, (l & 48) | (4 * g4 + i));
+                    sm.gp[part][2 * I][4 * g4 + i][r] = accA[i] * bi;
+                    sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
+                }
+                if (part == 0 && g4 == 0) sm.beta[tok] = bt;
+                if (c + 2 < nch) fetch_gate(t0 + static_cast<int64_t>(c + 2) * C);
+        }
+            __syncthreads();
+            if (gwork) {
+                f4 a10 = {0.f, 0.f, 0.f, 0.f}, p10 = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int ch = CPG * part + 32 * ks + 8 * g4;
+                    const f4 oa = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch]);
+                    const f4 ob = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch + 4]);
+                    const h8 of = {static_cast<_Float16>(oa[0]), static_cast<_Float16>(oa[1]),
+                                   static_cast<_Float16>(oa[2]), static_cast<_Float16>(oa[3]),
+                                   static_cast<_Float16>(ob[0]), static_cast<_Float16>(ob[1]),
+                                   static_cast<_Float16>(ob[2]), static_cast<_Float16>(ob[3])};
+                    h8 kv = l16[ks], qv = q16[ks], bv = rb16[ks];
+                    if (I == 1) {
+                        kv *= of;
+                        qv *= of;
+                    } else {
+                        bv *= of;
+                    }
+                    const int cb = ch & ~31, p0 = cb + (g4 < 2 ? 16 * g4 : 16 * g4 - 28), p1 = p0 + 8;
+                    *reinterpret_cast<h4*>(&nxt.kt[tok][p0]) = __builtin_shufflevector(kv, kv, 0, 1, 2, 3);
+                    *reinterpret_cast<h4*>(&nxt.kt[tok][p1]) = __builtin_shufflevector(kv, kv, 4, 5, 6, 7);
+                    *reinterpret_cast<h4*>(&nxt.qt[tok][p0]) = __builtin_shufflevector(qv, qv, 0, 1, 2, 3);
+                    *reinterpret_cast<h4*>(&nxt.qt[tok][p1]) = __builtin_shufflevector(qv, qv, 4, 5, 6, 7);
+                    const int tp = kpos(tok);
+    #pragma unroll
+                    for (int m = 0; m < 8; ++m) nxt.kbt[ch + m][tp] = bv[m];
+                    if (I == 1) {
+                        const h8 rv = *reinterpret_cast<const h8*>(&sm.rbs[r][ch]);
+                        a10 = mfma16(l16[ks], rv, a10);
+                        p10 = mfma16(q16[ks], rv, p10);
+                    }
+                }
+                if (I == 1) {
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sm.gp[part][2 * NSB][4 * g4 + i][r] = a10[i];
+                        sm.gp[part][2 * NSB + 1][4 * g4 + i][r] = p10[i];
+                    }
+                }
+                if (gtid < D) nxt.lam[gtid] = sm.etot[0][gtid] * sm.etot[1][gtid];
+                for (int e = gtid; e < NSB * SB * SB; e += GT) {
+                    const int J = e >> 8, i = (e >> 4) & 15, m = e & 15;
+                    float s = 0.f;
+    #pragma unroll
+                    for (int pp = 0; pp < NP; ++pp) s += sm.gp[pp][2 * J][i][m];
+                    sm.a[J][m][i] = s;
+                }
+    #pragma unroll
+                for (int j = 0; j < VU; ++j) {
+                    const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
+                    *reinterpret_cast<u4*>(&nxt.v[vt][vc]) = vp[j];
+                }
+                if (c + 2 < nch) fetch_v(t0 + static_cast<int64_t>(c + 2) * C);
+        }
+            __syncthreads();
+            if (gwork) {
+                if (gw < NSB) {
+                    const int J = gw, j = r;
+                    int jj = j;
+                    asm volatile("" : "+v"(jj));
+                    float xcol[SB];
+    #pragma unroll
+                    for (int i = 0; i < SB; ++i) xcol[i] = (i == jj) ? 1.f : 0.f;
+                    // columns of A read 2 steps ahead
+                    constexpr int PD = 2;
+                    f4 cl[PD][4];
+    #pragma unroll
+                    for (int m = 0; m < PD; ++m)
+    #pragma unroll
+                        for (int cc = 0; cc < 4; ++cc)
+                            if (4 * cc + 3 > m) cl[m][cc] = *reinterpret_cast<const f4*>(&sm.a[J][m][4 * cc]);
+    #pragma unroll
+                    for (int m = 0; m < SB; ++m) {
+                        const float xm = xcol[m];
+    #pragma unroll
+                        for (int i = m + 1; i < SB; ++i) xcol[i] = fmaf(-cl[m % PD][i >> 2][i & 3], xm, xcol[i]);
+                        if (m + PD < SB) {
+    #pragma unroll
+                            for (int cc = 0; cc < 4; ++cc)
+                                if (4 * cc + 3 > m + PD) cl[m % PD][cc] = *reinterpret_cast<const f4*>(&sm.a[J][m + PD][4 * cc]);
+                        }
+                    }
+                    if (g4 == 0) {
+                        const float bj = sm.beta[SB * J + j];
+    #pragma unroll
+                        for (int i = 0; i < SB; ++i) nxt.tb[J][i][j] = static_cast<_Float16>(xcol[i] * bj);
+                    }
+                } else {
+                    // One 16 x 16 block per wave (gate waves 2-6): P00, P11, P10, P01 (zero)
+                    // and -G10, 4 consecutive entries per lane.
+                    const int blk = gw - NSB;  // wave-uniform
+                    if (blk < 5) {
+                        const int i = (l >> 2) & 15, m4 = (l & 3) * 4;
+                        const int tile = blk == 0 ? 1 : blk == 1 ? 3 : blk == 2 ? 5 : blk == 4 ? 4 : -1;
+                        f4 val = {0.f, 0.f, 0.f, 0.f};
+                        if (tile >= 0) {
+#pragma unroll
+                            for (int pp = 0; pp < NP; ++pp) val += *reinterpret_cast<const f4*>(&sm.gp[pp][tile][i][m4]);
+                        }
+                        h4 hv;
+                        if (blk == 4) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(-val[e]);
+                            *reinterpret_cast<h4*>(&nxt.tb[2][i][m4]) = hv;
+                        } else {
+                            const int bi = (blk == 1 || blk == 2) ? 1 : 0, bj = (blk == 1 || blk == 3) ? 1 : 0;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                hv[e] = static_cast<_Float16>((bi > bj || m4 + e <= i) ? val[e] : 0.f);
+                            *reinterpret_cast<h4*>(&nxt.p[16 * bi + i][kpos(16 * bj + m4)]) = hv;
+                        }
+                    }
+                }
+        }
+            __syncthreads();
+        }
+    } else {
+        for (int c = -1; c < nch; ++c) {
+            const bool swork = c >= 0;        // run chunk c
+            const int64_t c0 = t0 + static_cast<int64_t>(c) * C;
+            const Tiles& cur = sm.tl[c & 1];
+            Tiles& nxt = sm.tl[(c + 1) & 1];
+            const int valid = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
+            if (swork) {
+                float vv[NSB][NCT][4];
+    #pragma unroll
+                for (int rt = 0; rt < NSB; ++rt)
+    #pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            vv[rt][ct][i] = bf16_to_f32(cur.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
+                float mv = 0.f, ms = 0.f;
+    #pragma unroll
+                for (int rt = 0; rt < NSB; ++rt)
+    #pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(vv[rt][ct][i]));
+    #pragma unroll
+                for (int rt = 0; rt < 8; ++rt)
+    #pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[rt][ct][i]));
+                const int nex = value_exponent(wave_max_nonneg(fmaxf(ms * ldexpf(1.f, -ex), mv)), ex);
+                if (nex != ex) {
+                    const float f = ldexpf(1.f, nex - ex);
+    #pragma unroll
+                    for (int rt = 0; rt < 8; ++rt)
+    #pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= f;
+                    ex = nex;
+                }
+                const float sig = ldexpf(1.f, ex);
+                h8 s16[4][NCT];  // fp16 S (B operand of K~ S); rebuilt for Q~ S in the next interval
+    #pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+    #pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+    #pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            s16[ks][ct][m] = static_cast<_Float16>(S[2 * ks][ct][m]);
+                            s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
+                        }
+                f4 y[NSB][NCT];
+    #pragma unroll
+                for (int rt = 0; rt < NSB; ++rt) {
+    #pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) y[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const h8 kf8 = *reinterpret_cast<const h8*>(&cur.kt[16 * rt + r][32 * ks + 8 * g4]);
+    #pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct) y[rt][ct] = mfma16(kf8, s16[ks][ct], y[rt][ct]);
+                    }
+                }
+                const h4 t00 = *reinterpret_cast<const h4*>(&cur.tb[0][r][4 * g4]);
+                const h4 t11 = *reinterpret_cast<const h4*>(&cur.tb[1][r][4 * g4]);
+                const h4 g10 = *reinterpret_cast<const h4*>(&cur.tb[2][r][4 * g4]);
+    #pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    h4 x0;
+                    f4 x1;
+    #pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        x0[m] = static_cast<_Float16>(fmaf(vv[0][ct][m], sig, -y[0][ct][m]));
+                        x1[m] = fmaf(vv[1][ct][m], sig, -y[1][ct][m]);
+                    }
+                    const f4 d0 = mfma16k16(t00, x0, f4{0.f, 0.f, 0.f, 0.f});
+                    h4 d0h;
+    #pragma unroll
+                    for (int m = 0; m < 4; ++m) d0h[m] = static_cast<_Float16>(d0[m]);
+                    const f4 z = mfma16k16(g10, d0h, x1);
+                    h4 zh;
+    #pragma unroll
+                    for (int m = 0; m < 4; ++m) zh[m] = static_cast<_Float16>(z[m]);
+                    const f4 d1 = mfma16k16(t11, zh, f4{0.f, 0.f, 0.f, 0.f});
+    #pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        d16[ct][m] = d0h[m];
+                        d16[ct][4 + m] = static_cast<_Float16>(d1[m]);
+                    }
+                }
+        }
+            __syncthreads();
+            if (swork) {
+                const float os = scale * ldexpf(1.f, -ex);
+            const int vlim = valid - 4 * g4;  // rows of this lane group still inside the chunk
+                h8 s16[4][NCT];
+    #pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+    #pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+    #pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            s16[ks][ct][m] = static_cast<_Float16>(S[2 * ks][ct][m]);
+                            s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
+                        }
+                const auto ro = rsrc(o + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * sizeof(Tout));
+                const int vo = static_cast<int>(((4 * g4) * rowe + col + r) * sizeof(Tout));
+    #pragma unroll
+                for (int rt = 0; rt < NSB; ++rt) {
+                    h8 qf8[4];
+    #pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+                        qf8[ks] = *reinterpret_cast<const h8*>(&cur.qt[16 * rt + r][32 * ks + 8 * g4]);
+                    const h8 pf = *reinterpret_cast<const h8*>(&cur.p[16 * rt + r][8 * g4]);
+    #pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        f4 a = mfma16(pf, d16[ct], f4{0.f, 0.f, 0.f, 0.f});
+    #pragma unroll
+                        for (int ks = 0; ks < 4; ++ks) a = mfma16(qf8[ks], s16[ks][ct], a);
+                        const int voc = vo + static_cast<int>(16 * ct * sizeof(Tout));
+                        if (valid == C) {
+    #pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                bstore(ro, voc, static_cast<int>((16 * rt + i) * rowe * sizeof(Tout)), a[i] * os, o);
+                        } else {
+    #pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (16 * rt + i < vlim)
+                                    bstore(ro, voc, static_cast<int>((16 * rt + i) * rowe * sizeof(Tout)), a[i] * os, o);
+                        }
+                    }
+                }
+        }
+            __syncthreads();
+            if (swork) {
+    #pragma unroll
+                for (int rt = 0; rt < 8; ++rt) {
+                    const f4 lam = *reinterpret_cast<const f4*>(&cur.lam[16 * rt + 4 * g4]);
+                    const h8 kb8 = *reinterpret_cast<const h8*>(&cur.kbt[16 * rt + r][8 * g4]);
+    #pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb8, d16[ct], S[rt][ct] * lam);
+                }
+        }
+            __syncthreads();
+        }
+        if (it.sout >= 0 && out_state) {
+            const float un = ldexpf(1.f, -ex);
+            float* dst = out_state + (static_cast<int64_t>(it.sout) * H + h) * D * D;
+    #pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+    #pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dst[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] = S[rt][ct][i] * un;
+        }
+    }
+
+
 }
 
 // Initial states of every segment, staged in the workspace: S_0 = h0 (or
@@ -791,6 +1366,13 @@ constexpr int kLptMaxSeqs = 16384;
 constexpr int kWaves = KDA_CHUNK_WAVES;  // waves per chain in the full-mode kernel
 constexpr int kNct = 128 / (16 * kWaves);  // 16-column state tiles per wave
 constexpr int kWpc = KDA_CHUNK_WPC;      // full-mode chains resident per CU
+#ifndef KDA_CHUNK_WS
+#define KDA_CHUNK_WS 1
+#endif
+#ifndef KDA_CHUNK_NSB
+#define KDA_CHUNK_NSB 4
+#endif
+constexpr int kNsb = KDA_CHUNK_NSB;      // 16-token sub-blocks per chunk in the full-mode kernel
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -840,8 +1422,8 @@ int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host) {
     for (int n = 0; n < N; ++n) total += cu_host ? cu_host[n + 1] - cu_host[n] : T;
     const int64_t target_items = 4 * 256 / (H > 0 ? H : 1) + 1;
     int64_t seg = (total + target_items - 1) / target_items;
-    seg = (seg + chunkk::C - 1) / chunkk::C * chunkk::C;
-    if (seg < 16 * chunkk::C) seg = 16 * chunkk::C;
+    seg = (seg + chunkk::CSEG - 1) / chunkk::CSEG * chunkk::CSEG;
+    if (seg < 8 * chunkk::CSEG) seg = 8 * chunkk::CSEG;
     return static_cast<int>(seg > (1 << 30) ? (1 << 30) : seg);
 }
 
@@ -858,13 +1440,26 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan) {
     char* ws = static_cast<char*>(a.ws);
     auto launch_full = [&](const ChunkItem* items, int64_t nitems, const float* staged) {
         const dim3 grid(static_cast<uint32_t>(nitems * a.H));
+#if KDA_CHUNK_WS
         if (a.out_bf16)
-            hipLaunchKernelGGL((chunk_kernel<kWaves, kNct, false, kWpc, bf16_t>), grid, dim3(kWaves * 64), 0,
+            hipLaunchKernelGGL((chunk_ws_kernel<bf16_t>), grid, dim3(ws::NW * 64), 0, a.stream,
+                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
+                               staged, static_cast<bf16_t*>(a.o), a.hT);
+        else
+            hipLaunchKernelGGL((chunk_ws_kernel<float>), grid, dim3(ws::NW * 64), 0, a.stream,
+                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                               static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
+                               staged, static_cast<float*>(a.o), a.hT);
+        return;
+#endif
+        if (a.out_bf16)
+            hipLaunchKernelGGL((chunk_kernel<kWaves, kNsb, kNct, false, kWpc, bf16_t>), grid, dim3(kWaves * 64), 0,
                                a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
                                staged, static_cast<bf16_t*>(a.o), a.hT);
         else
-            hipLaunchKernelGGL((chunk_kernel<kWaves, kNct, false, kWpc, float>), grid, dim3(kWaves * 64), 0,
+            hipLaunchKernelGGL((chunk_kernel<kWaves, kNsb, kNct, false, kWpc, float>), grid, dim3(kWaves * 64), 0,
                                a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
                                staged, static_cast<float*>(a.o), a.hT);
@@ -889,7 +1484,7 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan) {
     hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T, seg,
                        a.h0 ? 1 : 0, a.hT ? 1 : 0, seg_items, map_items, scan_items);
     if (nmap > 0)
-        hipLaunchKernelGGL((chunk_kernel<8, 2, true, 1, float>), dim3(static_cast<uint32_t>(nmap * a.H)),
+        hipLaunchKernelGGL((chunk_kernel<8, 2, 2, true, 1, float>), dim3(static_cast<uint32_t>(nmap * a.H)),
                            dim3(8 * 64), 0, a.stream, static_cast<const uint16_t*>(a.q),
                            static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.g,
                            a.beta, a.scale, map_items, a.H, static_cast<const float*>(nullptr),
