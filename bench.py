@@ -80,44 +80,53 @@ def cpu_baseline(x, budget_s=12.0):
     dv = x.v.shape[-1]
     chains = chain_list(B, T, x.cu_seqlens)
 
-    def run(sel, cap):
+    def run(sel, lo, hi):
+        """Oracle over tokens [lo, hi) of each selected chain (from the chain's
+        initial state: a timing sample, not a continuation)."""
         parts = [[], [], [], [], []]
         h0s, starts, lens = [], [], []
         row = 0
         for n, h in sel:
             b, t0, t1 = chains[n]
-            t1 = min(t1, t0 + cap)
+            a0, a1 = min(t0 + lo, t1), min(t0 + hi, t1)
+            if a1 <= a0:
+                continue
             for i, src in enumerate((x.q, x.k, x.v, x.g, x.beta)):
-                parts[i].append(src[b, t0:t1, h].to("cpu", torch.float32).numpy())
+                parts[i].append(src[b, a0:a1, h].to("cpu", torch.float32).numpy())
             if x.h0 is not None:
                 h0s.append(x.h0[n, h].to("cpu", torch.float64).numpy())
             starts.append(row)
-            lens.append(t1 - t0)
-            row += t1 - t0
+            lens.append(a1 - a0)
+            row += a1 - a0
+        if not row:
+            return 0, 0.0
         arrs = [np.concatenate(p) for p in parts]
         t_0 = time.perf_counter()
         cref.run_packed(starts, lens, dk, dv, x.scale, *arrs,
                         np.stack(h0s) if h0s else None, True, threads)
         return row, time.perf_counter() - t_0
 
-    # calibrate on short prefixes of one chain per thread
+    # Batches of (sequence, head) chains in order, each over a 4096-token
+    # window (about 1M head-tokens of host arrays per batch, one OpenMP run
+    # each), until the runs add up to the budget; after the first window of
+    # every chain, later windows of the same chains follow.
     order = [(n, h) for n in range(len(chains)) for h in range(H)]
-    sel = order[:max(threads, 1)]
-    ht, dt = run(sel, 256)
-    target = int(ht / max(dt, 1e-6) * budget_s)
-    # whole chains in order, each cut to at most target/threads tokens, until the target
-    cap = max(256, target // max(threads, 1))
-    sel, acc = [], 0
-    for n, h in order:
-        if acc >= target:
+    longest = max(t1 - t0 for _, t0, t1 in chains)
+    win, per_batch = 4096, 16 * max(threads, 1)
+    ht, dt, batches = 0, 0.0, 0
+    for lo in range(0, max(longest, 1), win):
+        for i in range(0, len(order), per_batch):
+            if dt >= budget_s:
+                break
+            n_ht, n_dt = run(order[i:i + per_batch], lo, lo + win)
+            ht += n_ht
+            dt += n_dt
+            batches += n_ht > 0
+        if dt >= budget_s:
             break
-        b, t0, t1 = chains[n]
-        sel.append((n, h))
-        acc += min(t1 - t0, cap)
-    ht, dt = run(sel, cap)
     return {"value": ht / dt / H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(sel)} (sequence, head) chains, first <= {cap} tokens each "
-                      f"({ht} head-tokens, {dt:.1f} s); fp64 C recurrence, OpenMP over chains; "
+            "sample": f"{batches} batches of up to {per_batch} (sequence, head) chains over {win}-token "
+                      f"windows ({ht} head-tokens, {dt:.1f} s); fp64 C recurrence, OpenMP over chains; "
                       f"tokens/s = head-tokens/s / H"}
 
 

@@ -346,7 +346,7 @@ void chunk_kernel(
                         Qa[m] = Lq * hm;
                     }
                 }
-                if (wave_max_nonneg(span) <= FAST_SPAN) {  // wave-uniform
+                if (!__any(span > FAST_SPAN)) {  // wave-uniform
                     h8 la, ra, qa;
 #pragma unroll
                     for (int m = 0; m < 8; ++m) {
@@ -370,11 +370,9 @@ void chunk_kernel(
                 }
                 if (I < NSB - 1) *reinterpret_cast<h8*>(&sm.rbs[I][r][ch]) = rb16[ks];
             }
-            // Row 4 g4 + i of the Gram tile is token 4 g4 + i of the sub-block: scale A by its beta.
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float bi = __shfl(bt, (l & 48) | (4 * g4 + i));
-                sm.gp[part][2 * I][4 * g4 + i][r] = accA[i] * bi;
+                sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
                 if (!MAP) sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
             }
             if (part == 0 && g4 == 0) sm.beta[tok] = bt;
@@ -478,7 +476,7 @@ void chunk_kernel(
                 float s = 0.f;
 #pragma unroll
                 for (int pp = 0; pp < NP; ++pp) s += sm.gp[pp][2 * J][i][m];
-                sm.a[J][m][i] = s;  // stored by column
+                sm.a[J][m][i] = s * sm.beta[SB * J + i];  // stored by column
             }
 #pragma unroll
             for (int j = 0; j < VU; ++j) {
@@ -884,7 +882,7 @@ void chunk_ws_kernel(
                     for (int m = 0; m < 8; ++m) {
                         e1[m] = __builtin_amdgcn_exp2f(G[m]);
                         const float e3 = __builtin_amdgcn_exp2f(Gt[m] - G[m]);
-                        const float hm = __builtin_amdgcn_exp2f(-0.5f * Gt[m]);
+                        const float hm = __builtin_amdgcn_exp2f(-0.5f * Gt[m]);    // exp(-tot/2)
                         span = fmaxf(span, fabsf(G[m] - 0.5f * Gt[m]));
                         const float L = kf[m] * e1[m], rb = kf[m] * e3, Lq = qf[m] * e1[m];
                         l16[ks][m] = static_cast<_Float16>(L);
@@ -894,7 +892,7 @@ void chunk_ws_kernel(
                         Ra[m] = rb * hm;
                         Qa[m] = Lq * hm;
                     }
-                    if (wave_max_nonneg(span) <= FAST_SPAN) {
+                    if (!__any(span > FAST_SPAN)) {
                         h8 la, ra, qa;
     #pragma unroll
                         for (int m = 0; m < 8; ++m) {
@@ -919,8 +917,7 @@ void chunk_ws_kernel(
                 }
     #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float bi = __shfl(bt, (l & 48) | (4 * g4 + i));
-                    sm.gp[part][2 * I][4 * g4 + i][r] = accA[i] * bi;
+                    sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
                     sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
                 }
                 if (part == 0 && g4 == 0) sm.beta[tok] = bt;
@@ -972,7 +969,7 @@ void chunk_ws_kernel(
                     float s = 0.f;
     #pragma unroll
                     for (int pp = 0; pp < NP; ++pp) s += sm.gp[pp][2 * J][i][m];
-                    sm.a[J][m][i] = s;
+                    sm.a[J][m][i] = s * sm.beta[SB * J + i];
                 }
     #pragma unroll
                 for (int j = 0; j < VU; ++j) {
