@@ -50,18 +50,28 @@ def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=4):
     return state, state + other
 
 
+def code_sha256(path):
+    """sha256 of a C/HIP source with comments and whitespace removed, so that
+    only changes to the code itself count as a change of the kernel."""
+    import hashlib
+    import re
+    src = open(path, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return hashlib.sha256(re.sub(r"\s+", "", src).encode()).hexdigest()
+
+
 def measured_traffic(key, workload_label):
     """HBM bytes per launch from the committed rocprofv3 counter record
-    (profiles/hbm_traffic.json), or None when the kernel source has changed
+    (profiles/hbm_traffic.json), or None when the kernel code has changed
     since the counters were taken or the workload differs."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         rec = json.load(open(path))["kernels"][key]
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        digest = code_sha256(os.path.join(ROOT, rec["source"]))
     except (OSError, KeyError, ValueError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"] or rec["workload"] != workload_label:
+    if digest != rec["code_sha256"] or rec["workload"] != workload_label:
         return None
     return rec["traffic_bytes"]
 

@@ -35,7 +35,7 @@
 //    when the wave's exponents stay within +-8, fp32 MFMA otherwise.  Every
 //    other product runs on fp16 MFMA with fp32 accumulation.  The kernel
 //    needs the sum of g over any 16 consecutive tokens of a channel to stay
-//    above about -170 (exp of half its negation must be finite in fp32).
+//    above about -85 (k exp(G) is formed in fp32 before the rescaling).
 //  * T is kept as its diagonal blocks T_JJ = (I + A_JJ)^-1 Diag(beta_J) and
 //    the raw cross Grams G_JK (A_JK = Diag(beta_J) G_JK); Delta = T X is then
 //    forward block substitution, Delta_J = T_JJ (X_J - sum_K<J G_JK Delta_K).
