@@ -70,7 +70,7 @@ kda_variant resolve_variant(kda_variant v, int32_t B, int32_t T, int32_t H, int3
 }
 
 size_t workspace_for(kda_variant v, int32_t B, int32_t T, int32_t H, int32_t N, const int32_t* cu_host) {
-    if (v == KDA_VARIANT_CHUNK || v == KDA_VARIANT_CHUNK_SCAN)
+    if (v == KDA_VARIANT_CHUNK || v == KDA_VARIANT_CHUNK_SCAN || v == KDA_VARIANT_CHUNK64)
         return kda::chunk_workspace_bytes(B, T, H, N, cu_host, v == KDA_VARIANT_CHUNK_SCAN);
     return 0;
 }
@@ -108,7 +108,7 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
                                     int32_t N, const int32_t* cu_seqlens_host, kda_dtype in_dtype,
                                     kda_variant variant) {
     if (B < 0 || T < 0 || H < 0 || N < 0 || !head_size_ok(d_k) || !head_size_ok(d_v) ||
-        !dtype_ok(in_dtype) || variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK_SCAN)
+        !dtype_ok(in_dtype) || variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK64)
         return 0;
     if (cu_seqlens_host ? (B != 1 || !seqlens_ok(cu_seqlens_host, N, T)) : N != B) return 0;
     const kda_variant v = resolve_variant(variant, B, T, H, d_k, d_v, N, in_dtype, cu_seqlens_host);
@@ -125,7 +125,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
     if (B < 0 || T < 0 || H < 0 || N < 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_SHAPE;
     if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDA_ERR_UNSUPPORTED;
-    if (variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK_SCAN) return KDA_ERR_UNSUPPORTED;
+    if (variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK64) return KDA_ERR_UNSUPPORTED;
     if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr)) return KDA_ERR_NULL;
     if (cu_seqlens) {
         if (B != 1) return KDA_ERR_SHAPE;
@@ -152,7 +152,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if (static_cast<int64_t>(N) * H * 8 > INT32_MAX || H > 65535) return KDA_ERR_SHAPE;
 
     const kda_variant var = resolve_variant(variant, B, T, H, d_k, d_v, N, in_dtype, cu_seqlens_host);
-    if ((var == KDA_VARIANT_CHUNK || var == KDA_VARIANT_CHUNK_SCAN) && !chunk_supported(d_k, d_v, in_dtype))
+    if ((var == KDA_VARIANT_CHUNK || var == KDA_VARIANT_CHUNK_SCAN || var == KDA_VARIANT_CHUNK64) &&
+        !chunk_supported(d_k, d_v, in_dtype))
         return KDA_ERR_UNSUPPORTED;
 
     for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(o),
@@ -209,8 +210,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     hipError_t e = hipErrorInvalidValue;
     switch (var) {
         case KDA_VARIANT_RECURRENT: e = kda::launch_recurrent(a); break;
-        case KDA_VARIANT_CHUNK: e = kda::launch_chunk(a, false); break;
-        case KDA_VARIANT_CHUNK_SCAN: e = kda::launch_chunk(a, true); break;
+        case KDA_VARIANT_CHUNK: e = kda::launch_chunk(a, false, false); break;
+        case KDA_VARIANT_CHUNK_SCAN: e = kda::launch_chunk(a, true, false); break;
+        case KDA_VARIANT_CHUNK64: e = kda::launch_chunk(a, false, true); break;
         default: return KDA_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

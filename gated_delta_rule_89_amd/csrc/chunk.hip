@@ -1354,22 +1354,7 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(
 namespace {
 
 constexpr int kLptMaxSeqs = 16384;
-#ifndef KDA_CHUNK_WAVES
-#define KDA_CHUNK_WAVES 8
-#endif
-#ifndef KDA_CHUNK_WPC
-#define KDA_CHUNK_WPC 1
-#endif
-constexpr int kWaves = KDA_CHUNK_WAVES;  // waves per chain in the full-mode kernel
-constexpr int kNct = 128 / (16 * kWaves);  // 16-column state tiles per wave
-constexpr int kWpc = KDA_CHUNK_WPC;      // full-mode chains resident per CU
-#ifndef KDA_CHUNK_WS
-#define KDA_CHUNK_WS 1
-#endif
-#ifndef KDA_CHUNK_NSB
-#define KDA_CHUNK_NSB 4
-#endif
-constexpr int kNsb = KDA_CHUNK_NSB;      // 16-token sub-blocks per chunk in the full-mode kernel
+constexpr int kWpc = 1;  // full-mode chains resident per CU (LDS bound)
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -1412,12 +1397,14 @@ ScanLayout scan_layout(int64_t nseg, int64_t nmap, int N, int H) {
 int chunk_chains_per_cu() { return kWpc; }
 
 int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host) {
-    // Long sequences are cut so that about four segments (workgroups) per CU
-    // exist over all heads; segments are a whole number of chunks.
+    // Long sequences are cut so that four segments (workgroups) per CU of a
+    // 256-CU part exist over all heads: a whole number of rounds of resident
+    // workgroups.  Segments are a whole number of chunks.
     (void)B;
     int64_t total = 0;
     for (int n = 0; n < N; ++n) total += cu_host ? cu_host[n + 1] - cu_host[n] : T;
-    const int64_t target_items = 4 * 256 / (H > 0 ? H : 1) + 1;
+    int64_t target_items = 4 * 256 / (H > 0 ? H : 1);
+    if (target_items < 1) target_items = 1;
     int64_t seg = (total + target_items - 1) / target_items;
     seg = (seg + chunkk::CSEG - 1) / chunkk::CSEG * chunkk::CSEG;
     if (seg < 8 * chunkk::CSEG) seg = 8 * chunkk::CSEG;
@@ -1432,12 +1419,24 @@ size_t chunk_workspace_bytes(int B, int T, int H, int N, const int32_t* cu_host,
     return scan_layout(nseg, nmap, N, H).total;
 }
 
-hipError_t launch_chunk(const PrefillArgs& a, bool scan) {
+hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
     using namespace chunkk;
     char* ws = static_cast<char*>(a.ws);
     auto launch_full = [&](const ChunkItem* items, int64_t nitems, const float* staged) {
         const dim3 grid(static_cast<uint32_t>(nitems * a.H));
-#if KDA_CHUNK_WS
+        if (c64) {  // single-role kernel, 64-token chunks
+            if (a.out_bf16)
+                hipLaunchKernelGGL((chunk_kernel<8, 4, 1, false, 1, bf16_t>), grid, dim3(8 * 64), 0, a.stream,
+                                   static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                                   static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
+                                   staged, static_cast<bf16_t*>(a.o), a.hT);
+            else
+                hipLaunchKernelGGL((chunk_kernel<8, 4, 1, false, 1, float>), grid, dim3(8 * 64), 0, a.stream,
+                                   static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                                   static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
+                                   staged, static_cast<float*>(a.o), a.hT);
+            return;
+        }
         if (a.out_bf16)
             hipLaunchKernelGGL((chunk_ws_kernel<bf16_t>), grid, dim3(ws::NW * 64), 0, a.stream,
                                static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
@@ -1446,18 +1445,6 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan) {
         else
             hipLaunchKernelGGL((chunk_ws_kernel<float>), grid, dim3(ws::NW * 64), 0, a.stream,
                                static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                               static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
-                               staged, static_cast<float*>(a.o), a.hT);
-        return;
-#endif
-        if (a.out_bf16)
-            hipLaunchKernelGGL((chunk_kernel<kWaves, kNsb, kNct, false, kWpc, bf16_t>), grid, dim3(kWaves * 64), 0,
-                               a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                               static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
-                               staged, static_cast<bf16_t*>(a.o), a.hT);
-        else
-            hipLaunchKernelGGL((chunk_kernel<kWaves, kNsb, kNct, false, kWpc, float>), grid, dim3(kWaves * 64), 0,
-                               a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                                static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
                                staged, static_cast<float*>(a.o), a.hT);
     };

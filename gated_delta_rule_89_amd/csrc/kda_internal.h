@@ -74,6 +74,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 int chunk_chains_per_cu();  // full-mode chunk workgroups resident per CU
 int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host);
 size_t chunk_workspace_bytes(int B, int T, int H, int N, const int32_t* cu_host, bool scan);
-hipError_t launch_chunk(const PrefillArgs& a, bool scan);
+// scan: segment-scan path; c64: single-role kernel on 64-token chunks.
+hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64);
 
 }  // namespace kda

@@ -68,18 +68,25 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 /* Prefill implementations.  AUTO picks the fastest one that supports the
  * arguments; the others exist to compare paths against each other.
  *  RECURRENT  token-sequential fused recurrent kernel, any supported shape;
- *  CHUNK      chunkwise kernel on fp16/bf16 MFMA, 32-token chunks, one
- *             workgroup per (sequence, head) (bf16 inputs, d_k = d_v = 128);
+ *  CHUNK      chunkwise kernel on fp16 MFMA, 32-token chunks, one workgroup
+ *             of 12 waves per (sequence, head): 8 waves prepare the next
+ *             chunk's gate-side operands while 4 run the state pass (bf16
+ *             inputs, d_k = d_v = 128);
  *  CHUNK_SCAN CHUNK on segments of long sequences: each segment's affine
  *             state map is computed in parallel, composed by a scan, and the
  *             segments then run in parallel from their initial states (same
  *             inputs as CHUNK).  AUTO takes it when the longest sequence
- *             would otherwise dominate the run time. */
+ *             would otherwise dominate the run time.
+ *  CHUNK64    chunkwise kernel on 64-token chunks (four 16-token
+ *             sub-blocks), 8 waves per (sequence, head) doing the gate-side
+ *             and then the state work of each chunk; same inputs as CHUNK.
+ *             Never chosen by AUTO. */
 typedef enum kda_variant {
     KDA_VARIANT_AUTO = 0,
     KDA_VARIANT_RECURRENT = 1,
     KDA_VARIANT_CHUNK = 2,
-    KDA_VARIANT_CHUNK_SCAN = 3
+    KDA_VARIANT_CHUNK_SCAN = 3,
+    KDA_VARIANT_CHUNK64 = 4
 } kda_variant;
 
 /* ABI version (KDA_ABI_VERSION of the built library). */

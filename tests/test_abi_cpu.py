@@ -117,6 +117,7 @@ def test_workspace_size_grows_with_segments():
     scan = ws(1, 100100, 4, 128, 128, 2, cu, BF16, 3)
     assert 0 < plain < 4096 and scan > 4 * 128 * 128 * 4
     assert ws(1, 100100, 4, 128, 128, 2, cu, BF16, 1) == 0
+    assert ws(1, 100100, 4, 128, 128, 2, cu, BF16, 4) == plain     # CHUNK64: item list only
 
 
 def decode(q=None, k=None, v=None, g=None, beta=None, state=None, N=4, H=2, dk=16, dv=16,

@@ -41,7 +41,8 @@ def run_prefill(x, variant="auto", **kw):
     return o, f
 
 
-VARIANTS = ["auto", "recurrent", "chunk", "chunk_scan"]
+VARIANTS = ["auto", "recurrent", "chunk", "chunk_scan", "chunk64"]
+CHUNKED = ["chunk", "chunk64"]  # the two chunkwise kernels (32- and 64-token chunks)
 
 
 @pytest.mark.parametrize("variant", ["auto", "recurrent"])
@@ -211,34 +212,37 @@ def test_run_to_run_determinism():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_chunk_rejects_fp32_and_small_heads():
-    say("chunk variant: fp32 inputs / d=16 are unsupported")
+@pytest.mark.parametrize("variant", CHUNKED)
+def test_chunk_rejects_fp32_and_small_heads(variant):
+    say(f"{variant} variant: fp32 inputs / d=16 are unsupported")
     x = synth.make_inputs("tiny")
     with pytest.raises(_kda().KDAError) as e:
-        run_prefill(x, "chunk")
+        run_prefill(x, variant)
     assert e.value.code == 4
 
 
-@pytest.mark.parametrize("T", [1, 17, 31, 32, 33, 64, 100])
-def test_chunk_ragged_lengths(T):
-    say(f"chunk T={T} H=3 (partial chunks)")
+@pytest.mark.parametrize("variant", CHUNKED)
+@pytest.mark.parametrize("T", [1, 17, 31, 32, 33, 63, 64, 65, 100, 129])
+def test_chunk_ragged_lengths(T, variant):
+    say(f"{variant} T={T} H=3 (partial chunks)")
     x = synth.make_inputs("prefill", T=T, H=3, seed=7)
-    o, f = run_prefill(x, "chunk")
+    o, f = run_prefill(x, variant)
     o_ref, f_ref = ref.kda_forward(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0)
     assert_parity(o, o_ref, torch.bfloat16, "o")
     assert_parity(f, f_ref, torch.bfloat16, "final")
 
 
+@pytest.mark.parametrize("variant", CHUNKED)
 @pytest.mark.parametrize("mu,sigma", [(4.0, 1.0), (-4.0, 0.5), (8.0, 2.0)])
-def test_chunk_gate_range(mu, sigma):
+def test_chunk_gate_range(mu, sigma, variant):
     """Strong and weak decay: g = -softplus(sigma N(0,1) + mu), floored at -5.2
     so that a 16-token sum stays above -84 (the documented range of the
     chunked kernel); mu = 8 puts many sub-blocks near that floor."""
-    say(f"chunk gate range g=-softplus({sigma} N + {mu}) T=300 H=2")
+    say(f"{variant} gate range g=-softplus({sigma} N + {mu}) T=300 H=2")
     x = synth.make_inputs("prefill", T=300, H=2, seed=11)
     gen = torch.Generator().manual_seed(5)
     x.g = (-torch.nn.functional.softplus(sigma * torch.randn(x.g.shape, generator=gen) + mu)).clamp(min=-5.2)
-    o, f = run_prefill(x, "chunk")
+    o, f = run_prefill(x, variant)
     o_ref, f_ref = oracle_prefill(x)
     eo = assert_parity(o, o_ref, torch.bfloat16, "o")
     ef = assert_parity(f, f_ref, torch.bfloat16, "final")
