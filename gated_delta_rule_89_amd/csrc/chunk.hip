@@ -47,6 +47,8 @@
 //    chosen every chunk from max(|S|, |v|), which keeps them inside fp16 range
 //    and away from subnormals; the scale is exact and is removed in fp32.
 //  * The next chunk's inputs are fetched into registers during the state pass.
+#include <utility>
+
 #include "dev_common.h"
 #include "kda_internal.h"
 
@@ -133,6 +135,27 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
 template <int N>
 __device__ __forceinline__ float row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | N, 0xf, 0xf, true));
+}
+
+// Value of lane M of the same 16-lane DPP row, in every lane of the row.
+template <int M>
+__device__ __forceinline__ float row_bcast16(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 | M, 0xf, 0xf, true));
+}
+
+// One step of a column-oriented substitution with rows across the 16 lanes
+// of a DPP row: x_i -= a_i x_M for four columns, a_i = A[i][M] of this lane's row.
+template <int M>
+__device__ __forceinline__ void subst_step(float (&x)[4], const f4 (&arow)[4]) {
+    float xb[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) xb[qq] = row_bcast16<M>(x[qq]);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) x[qq] = fmaf(-arow[M >> 2][M & 3], xb[qq], x[qq]);
+}
+template <int... M>
+__device__ __forceinline__ void subst_all(float (&x)[4], const f4 (&arow)[4], std::integer_sequence<int, M...>) {
+    (subst_step<M>(x, arow), ...);
 }
 
 // Inclusive prefix sum over the 16 lanes of a DPP row.
@@ -755,7 +778,7 @@ struct alignas(16) Smem {
     Tiles tl[2];
     _Float16 rbs[SB][QP];                // k exp(tot_0 - G), sub-block 0 [token][channel]
     float gp[NP][2 * NSB + 2 * NX][SB][GP];
-    float a[NSB][SB][20];                // A_JJ^T
+    float a[NSB][SB][20];                // A_JJ = Diag(beta) G_JJ, strictly lower, by row
     float etot[NSB][D];
     float beta[C];
 };
@@ -781,30 +804,16 @@ void chunk_ws_kernel(
     const int h = blockIdx.x % H;
     const int64_t t0 = it.t0, t1 = it.t1;
     const int nch = static_cast<int>((t1 - t0 + C - 1) / C);
+    const int rowe = H * D;  // elements per token row
 
-    // ---- state waves: S[16 rt + 4 g4 + i][col + 16 ct + r] * 2^ex in S[rt][ct][i]
-    const int col = 32 * (w & 3);
-    f4 S[8][NCT];
-    int ex = 0;
-    h8 d16[NCT];      // fp16 Delta (B operand of P Delta, K-bar^T Delta), chunk-local
-    if (!gate) {
-        const float* src = nullptr;
-        if (it.sin >= 0 && h0) src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
-        else if (it.sin <= -2) src = staged + (static_cast<int64_t>(-it.sin - 2) * H + h) * D * D;
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
-        if (src) {
-#pragma unroll
-            for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
-        }
-    }
-
+    // The two roles run separate loops with the same trip count and exactly
+    // three barriers per iteration (the barriers pair up across the roles).
+    // Each role's memory traffic stays inside its own branch, and every
+    // iteration issues the same loads (past the end of the sequence they fall
+    // outside the buffer range and read zeros): the compiler can then count
+    // outstanding loads exactly and never waits for the prefetch of chunk
+    // c + 2 before it is consumed.
+    if (gate) {
     // ---- gate waves: sub-block I, channel part `part`; raw inputs fetched ahead
     const int gw = w - NSW;
     const int I = gw / NP, part = gw % NP;
@@ -813,49 +822,42 @@ void chunk_ws_kernel(
     u4 kw[KS], qw[KS], vp[VU];
     f4 ga[KS], gb[KS];
     float bt = 0.f;
-    const int rowe = H * D;  // elements per token row
+    // Tokens at or past the end of the sequence lie outside the buffer range
+    // of the chunk (valid tokens x row bytes), so their loads return zeros.
+    auto valid_at = [&](int64_t cs) {
+        const int64_t n = t1 - cs;
+        return static_cast<uint32_t>(n < 0 ? 0 : n < C ? n : C);
+    };
     auto fetch_gate = [&](int64_t cs) {  // k, q, g, beta of this lane's token
-        const int vld = static_cast<int>(t1 - cs < C ? t1 - cs : C);
-        const bool in = tok < vld;
+        const uint32_t vld = valid_at(cs);
         const int64_t cb = (cs * H + h) * D;
-        const auto rk = rsrc(k + cb, static_cast<uint32_t>(vld) * rowe * 2);
-        const auto rq = rsrc(q + cb, static_cast<uint32_t>(vld) * rowe * 2);
-        const auto rg = rsrc(g + cb, static_cast<uint32_t>(vld) * rowe * 4);
-        const auto rb = rsrc(beta + cs * H + h, static_cast<uint32_t>(vld) * H * 4);
+        const auto rk = rsrc(k + cb, vld * rowe * 2);
+        const auto rq = rsrc(q + cb, vld * rowe * 2);
+        const auto rg = rsrc(g + cb, vld * rowe * 4);
+        const auto rb = rsrc(beta + cs * H + h, vld * H * 4);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
-            kw[ks] = qw[ks] = u4{0, 0, 0, 0};
-            ga[ks] = gb[ks] = f4{0.f, 0.f, 0.f, 0.f};
-            if (in) {
-                kw[ks] = bload16(rk, 2 * off);
-                qw[ks] = bload16(rq, 2 * off);
-                const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
-                ga[ks] = f4{__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]), __uint_as_float(a0[3])};
-                gb[ks] = f4{__uint_as_float(a1[0]), __uint_as_float(a1[1]), __uint_as_float(a1[2]), __uint_as_float(a1[3])};
-            }
+            kw[ks] = bload16(rk, 2 * off);
+            qw[ks] = bload16(rq, 2 * off);
+            const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
+            ga[ks] = f4{__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]), __uint_as_float(a0[3])};
+            gb[ks] = f4{__uint_as_float(a1[0]), __uint_as_float(a1[1]), __uint_as_float(a1[2]), __uint_as_float(a1[3])};
         }
-        bt = in ? bload4(rb, 4 * tok * H) : 0.f;
+        bt = bload4(rb, 4 * tok * H);
     };
     auto fetch_v = [&](int64_t cs) {
-        const int vld = static_cast<int>(t1 - cs < C ? t1 - cs : C);
-        const auto rv = rsrc(v + (cs * H + h) * D, static_cast<uint32_t>(vld) * rowe * 2);
+        const auto rv = rsrc(v + (cs * H + h) * D, valid_at(cs) * rowe * 2);
 #pragma unroll
         for (int j = 0; j < VU; ++j) {
             const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
-            vp[j] = u4{0, 0, 0, 0};
-            if (vt < vld) vp[j] = bload16(rv, 2 * (vt * rowe + vc));
+            vp[j] = bload16(rv, 2 * (vt * rowe + vc));
         }
     };
-    if (gate && nch > 0) {
-        fetch_gate(t0);
-        fetch_v(t0);
-    }
+    fetch_gate(t0);
+    fetch_v(t0);
     h8 l16[KS], q16[KS], rb16[KS];  // gate registers carried from phase 1 to phase 2
 
-    // The two roles run separate loops with the same trip count and exactly
-    // three barriers per iteration (the barriers pair up across the roles).
-    if (gate) {
         for (int c = -1; c < nch; ++c) {
             const bool gwork = c + 1 < nch;   // prepare chunk c + 1
             const int64_t c0 = t0 + static_cast<int64_t>(c) * C;
@@ -921,8 +923,8 @@ void chunk_ws_kernel(
                     sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
                 }
                 if (part == 0 && g4 == 0) sm.beta[tok] = bt;
-                if (c + 2 < nch) fetch_gate(t0 + static_cast<int64_t>(c + 2) * C);
-        }
+            }
+            fetch_gate(t0 + static_cast<int64_t>(c + 2) * C);
             __syncthreads();
             if (gwork) {
                 f4 a10 = {0.f, 0.f, 0.f, 0.f}, p10 = {0.f, 0.f, 0.f, 0.f};
@@ -969,48 +971,36 @@ void chunk_ws_kernel(
                     float s = 0.f;
     #pragma unroll
                     for (int pp = 0; pp < NP; ++pp) s += sm.gp[pp][2 * J][i][m];
-                    sm.a[J][m][i] = s * sm.beta[SB * J + i];
+                    sm.a[J][i][m] = m < i ? s * sm.beta[SB * J + i] : 0.f;  // A_JJ, strictly lower
                 }
     #pragma unroll
                 for (int j = 0; j < VU; ++j) {
                     const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
                     *reinterpret_cast<u4*>(&nxt.v[vt][vc]) = vp[j];
                 }
-                if (c + 2 < nch) fetch_v(t0 + static_cast<int64_t>(c + 2) * C);
-        }
+            }
+            fetch_v(t0 + static_cast<int64_t>(c + 2) * C);
             __syncthreads();
             if (gwork) {
                 if (gw < NSB) {
-                    const int J = gw, j = r;
-                    int jj = j;
-                    asm volatile("" : "+v"(jj));
-                    float xcol[SB];
-    #pragma unroll
-                    for (int i = 0; i < SB; ++i) xcol[i] = (i == jj) ? 1.f : 0.f;
-                    // columns of A read 2 steps ahead
-                    constexpr int PD = 2;
-                    f4 cl[PD][4];
-    #pragma unroll
-                    for (int m = 0; m < PD; ++m)
-    #pragma unroll
-                        for (int cc = 0; cc < 4; ++cc)
-                            if (4 * cc + 3 > m) cl[m][cc] = *reinterpret_cast<const f4*>(&sm.a[J][m][4 * cc]);
-    #pragma unroll
-                    for (int m = 0; m < SB; ++m) {
-                        const float xm = xcol[m];
-    #pragma unroll
-                        for (int i = m + 1; i < SB; ++i) xcol[i] = fmaf(-cl[m % PD][i >> 2][i & 3], xm, xcol[i]);
-                        if (m + PD < SB) {
-    #pragma unroll
-                            for (int cc = 0; cc < 4; ++cc)
-                                if (4 * cc + 3 > m + PD) cl[m % PD][cc] = *reinterpret_cast<const f4*>(&sm.a[J][m + PD][4 * cc]);
-                        }
-                    }
-                    if (g4 == 0) {
-                        const float bj = sm.beta[SB * J + j];
-    #pragma unroll
-                        for (int i = 0; i < SB; ++i) nxt.tb[J][i][j] = static_cast<_Float16>(xcol[i] * bj);
-                    }
+                    // Column-oriented substitution for T = (I + A_JJ)^-1: lane
+                    // (i, g4) holds row i of columns 4 g4 .. 4 g4 + 3 and row i of
+                    // A (zero on and above the diagonal).  Step m broadcasts x_m of
+                    // each column across its 16-lane row (DPP) and updates every
+                    // row at once: x_i -= A[i][m] x_m.
+                    const int J = gw;
+                    f4 arow[4];
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) arow[cc] = *reinterpret_cast<const f4*>(&sm.a[J][r][4 * cc]);
+                    const f4 bcol = *reinterpret_cast<const f4*>(&sm.beta[SB * J + 4 * g4]);
+                    float x[4];
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) x[qq] = (r == 4 * g4 + qq) ? 1.f : 0.f;
+                    subst_all(x, arow, std::make_integer_sequence<int, SB>{});
+                    h4 tv;
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) tv[qq] = static_cast<_Float16>(x[qq] * bcol[qq]);
+                    *reinterpret_cast<h4*>(&nxt.tb[J][r][4 * g4]) = tv;
                 } else {
                     // One 16 x 16 block per wave (gate waves 2-6): P00, P11, P10, P01 (zero)
                     // and -G10, 4 consecutive entries per lane.
@@ -1041,6 +1031,28 @@ void chunk_ws_kernel(
             __syncthreads();
         }
     } else {
+    // ---- state waves: S[16 rt + 4 g4 + i][col + 16 ct + r] * 2^ex in S[rt][ct][i]
+    const int col = 32 * (w & 3);
+    f4 S[8][NCT];
+    int ex = 0;
+    h8 d16[NCT];      // fp16 Delta (B operand of P Delta, K-bar^T Delta), chunk-local
+    {
+        const float* src = nullptr;
+        if (it.sin >= 0 && h0) src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
+        else if (it.sin <= -2) src = staged + (static_cast<int64_t>(-it.sin - 2) * H + h) * D * D;
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+        if (src) {
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
+        }
+    }
         for (int c = -1; c < nch; ++c) {
             const bool swork = c >= 0;        // run chunk c
             const int64_t c0 = t0 + static_cast<int64_t>(c) * C;
