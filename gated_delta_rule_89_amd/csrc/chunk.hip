@@ -112,7 +112,7 @@ struct alignas(16) Smem {
     _Float16 p[C][TP];                 // P                    [token][token, operand order]
     uint16_t v[C][QP];                 // v tile (bf16 bits)   [token][column]
     float gp[NP][2 * NSB + 2 * NX][SB][GP];
-    float a[NSB][SB][20];              // A_JJ^T: column m of Diag(beta) Gram in row m
+    float a[NSB][SB][20];              // A_JJ = Diag(beta) G_JJ, strictly lower, by row
     float etot[NSB][D];                // per-channel exp(sum of g over each sub-block)
     float lam[D];                      // Lambda_last = exp(Gamma over the chunk)
     float beta[C];
@@ -293,38 +293,41 @@ void chunk_kernel(
 
     // Raw inputs of the next chunk, fetched one chunk ahead: k, q, g of this
     // lane's token and channels (gate layout), its beta, and pieces of the v
-    // tile (staging layout).
+    // tile (staging layout).  Every chunk issues the same buffer loads; tokens
+    // at or past the end of the sequence lie outside the buffer range (valid
+    // tokens x row bytes) and read zeros, so the compiler counts outstanding
+    // loads exactly and waits only for the ones it consumes.
     const int tok = SB * I + r;
+    const int rowe = H * D;  // elements per token row
     u4 kw[KS], qw[KS], vp[VU];
     f4 ga[KS], gb[KS];
     float bt;
     auto fetch = [&](int64_t cs) {
-        const int vld = static_cast<int>(t1 - cs < C ? t1 - cs : C);
-        const bool in = tok < vld;
-        const int64_t rowq = ((cs + tok) * H + h) * D;
+        const int64_t nv = t1 - cs;
+        const uint32_t vld = static_cast<uint32_t>(nv < 0 ? 0 : nv < C ? nv : C);
+        const int64_t cb = (cs * H + h) * D;
+        const auto rk = rsrc(k + cb, vld * rowe * 2);
+        const auto rq = rsrc(q + cb, vld * rowe * 2);
+        const auto rg = rsrc(g + cb, vld * rowe * 4);
+        const auto rb = rsrc(beta + cs * H + h, vld * H * 4);
+        const auto rv = rsrc(v + cb, vld * rowe * 2);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int ch = CPG * part + 32 * ks + 8 * g4;
-            kw[ks] = u4{0, 0, 0, 0};
-            qw[ks] = u4{0, 0, 0, 0};
-            ga[ks] = f4{0.f, 0.f, 0.f, 0.f};
-            gb[ks] = f4{0.f, 0.f, 0.f, 0.f};
-            if (in) {
-                kw[ks] = *reinterpret_cast<const u4*>(k + rowq + ch);
-                if (!MAP) qw[ks] = *reinterpret_cast<const u4*>(q + rowq + ch);
-                ga[ks] = *reinterpret_cast<const f4*>(g + rowq + ch);
-                gb[ks] = *reinterpret_cast<const f4*>(g + rowq + ch + 4);
-            }
+            const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
+            kw[ks] = bload16(rk, 2 * off);
+            qw[ks] = MAP ? u4{0, 0, 0, 0} : bload16(rq, 2 * off);
+            const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
+            ga[ks] = f4{__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]), __uint_as_float(a0[3])};
+            gb[ks] = f4{__uint_as_float(a1[0]), __uint_as_float(a1[1]), __uint_as_float(a1[2]), __uint_as_float(a1[3])};
         }
-        bt = in ? beta[(cs + tok) * H + h] : 0.f;
+        bt = bload4(rb, 4 * tok * H);
 #pragma unroll
         for (int j = 0; j < VU; ++j) {
             const int e = tid + NT * j, vt = e >> 4, vc = (e & 15) * 8;
-            vp[j] = u4{0, 0, 0, 0};
-            if (vt < vld) vp[j] = *reinterpret_cast<const u4*>(v + ((cs + vt) * H + h) * D + vc);
+            vp[j] = bload16(rv, 2 * (vt * rowe + vc));
         }
     };
-    if (t0 < t1) fetch(t0);
+    fetch(t0);
 
     for (int64_t c0 = t0; c0 < t1; c0 += C) {
         const int valid = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
@@ -349,25 +352,27 @@ void chunk_kernel(
 #pragma unroll
                 for (int m = 0; m < 8; ++m) G[m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
 #pragma unroll
-                for (int m = 0; m < 8; ++m) Gt[m] = __shfl(G[m], 15, 16);
-                float e1[8], La[8], Ra[8], Qa[8];
+                for (int m = 0; m < 8; ++m) Gt[m] = row_bcast16<15>(G[m]);
+                // a = exp(G - tot/2), 1/a, and the channel's exp(tot/2) (a at the
+                // last token): exp(G) = a exp(tot/2), exp(tot - G) = exp(tot/2) / a.
+                float La[8], Ra[8], Qa[8], hh[8];
                 float span = 0.f;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
-                    e1[m] = __builtin_amdgcn_exp2f(G[m]);                      // exp(G) <= 1
-                    const float e3 = __builtin_amdgcn_exp2f(Gt[m] - G[m]);     // exp(tot - G) <= 1
-                    const float hm = __builtin_amdgcn_exp2f(-0.5f * Gt[m]);    // exp(-tot/2)
-                    span = fmaxf(span, fabsf(G[m] - 0.5f * Gt[m]));
-                    const float L = kf[m] * e1[m], rb = kf[m] * e3;
-                    l16[ks][m] = static_cast<_Float16>(L);
-                    rb16[ks][m] = static_cast<_Float16>(rb);
-                    La[m] = L * hm;
-                    Ra[m] = rb * hm;
-                    if (!MAP) {
-                        const float Lq = qf[m] * e1[m];
-                        q16[ks][m] = static_cast<_Float16>(Lq);
-                        Qa[m] = Lq * hm;
-                    }
+                    const float xa = fmaf(-0.5f, Gt[m], G[m]);
+                    span = fmaxf(span, fabsf(xa));
+                    const float a = __builtin_amdgcn_exp2f(xa);
+                    const float ia = __builtin_amdgcn_exp2f(-xa);
+                    La[m] = kf[m] * a;
+                    Ra[m] = kf[m] * ia;
+                    if (!MAP) Qa[m] = qf[m] * a;
+                    hh[m] = row_bcast16<15>(a);
+                }
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G) <= |k|
+                    rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
+                    if (!MAP) q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);
                 }
                 if (!__any(span > FAST_SPAN)) {  // wave-uniform
                     h8 la, ra, qa;
@@ -387,9 +392,11 @@ void chunk_kernel(
                         if (!MAP) accP = mfma4(Qa[m], Ra[m], accP);
                     }
                 }
-                if (r == 15) {  // exp(sum of g over the sub-block)
-                    *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{e1[0], e1[1], e1[2], e1[3]};
-                    *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{e1[4], e1[5], e1[6], e1[7]};
+                if (r == 15) {  // exp(sum of g over the sub-block) = exp(tot/2)^2
+                    *reinterpret_cast<f4*>(&sm.etot[I][ch]) =
+                        f4{hh[0] * hh[0], hh[1] * hh[1], hh[2] * hh[2], hh[3] * hh[3]};
+                    *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) =
+                        f4{hh[4] * hh[4], hh[5] * hh[5], hh[6] * hh[6], hh[7] * hh[7]};
                 }
                 if (I < NSB - 1) *reinterpret_cast<h8*>(&sm.rbs[I][r][ch]) = rb16[ks];
             }
@@ -499,7 +506,7 @@ void chunk_kernel(
                 float s = 0.f;
 #pragma unroll
                 for (int pp = 0; pp < NP; ++pp) s += sm.gp[pp][2 * J][i][m];
-                sm.a[J][m][i] = s * sm.beta[SB * J + i];  // stored by column
+                sm.a[J][i][m] = m < i ? s * sm.beta[SB * J + i] : 0.f;  // A_JJ by row, strictly lower
             }
 #pragma unroll
             for (int j = 0; j < VU; ++j) {
@@ -511,34 +518,21 @@ void chunk_kernel(
 
         // ---------------- solve: diagonal block inverses (waves 0 .. NSB-1); P and -G_x (others)
         if (w < NSB) {
+            // T_JJ = (I + A_JJ)^-1 Diag(beta_J) by column-oriented substitution:
+            // lane (i, g4) holds row i of columns 4 g4 .. 4 g4 + 3 and row i of A.
             const int J = w;  // diagonal block
-            const int j = r;  // column of the inverse owned by this lane
-            // Column j of (I + A_JJ)^-1 by forward substitution, column-oriented:
-            // once x_m is final, every later row subtracts A[i][m] x_m (independent
-            // updates).  The parts of A's columns below the diagonal are read up
-            // front (broadcast reads), so the 16 steps wait on LDS only once.
-            int jj = j;
-            asm volatile("" : "+v"(jj));  // keeps the identity column from being hoisted out of the chunk loop
-            float xcol[SB];
+            f4 arow[4];
 #pragma unroll
-            for (int i = 0; i < SB; ++i) xcol[i] = (i == jj) ? 1.f : 0.f;
-            f4 cl[SB][4];
+            for (int c = 0; c < 4; ++c) arow[c] = *reinterpret_cast<const f4*>(&sm.a[J][r][4 * c]);
+            const f4 bcol = *reinterpret_cast<const f4*>(&sm.beta[SB * J + 4 * g4]);
+            float x[4];
 #pragma unroll
-            for (int m = 0; m < SB; ++m)
+            for (int qq = 0; qq < 4; ++qq) x[qq] = (r == 4 * g4 + qq) ? 1.f : 0.f;
+            subst_all(x, arow, std::make_integer_sequence<int, SB>{});
+            h4 tv;
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if (4 * c + 3 > m) cl[m][c] = *reinterpret_cast<const f4*>(&sm.a[J][m][4 * c]);
-#pragma unroll
-            for (int m = 0; m < SB; ++m) {
-                const float xm = xcol[m];
-#pragma unroll
-                for (int i = m + 1; i < SB; ++i) xcol[i] = fmaf(-cl[m][i >> 2][i & 3], xm, xcol[i]);
-            }
-            if (g4 == 0) {
-                const float bj = sm.beta[SB * J + j];
-#pragma unroll
-                for (int i = 0; i < SB; ++i) sm.tb[J][i][j] = static_cast<_Float16>(xcol[i] * bj);
-            }
+            for (int qq = 0; qq < 4; ++qq) tv[qq] = static_cast<_Float16>(x[qq] * bcol[qq]);
+            *reinterpret_cast<h4*>(&sm.tb[J][r][4 * g4]) = tv;
         } else {
             // Sums of the channel-part partials, 4 consecutive entries per step:
             // P (causal blocks, plus the zero blocks inside the 32-token k blocks
@@ -590,7 +584,7 @@ void chunk_kernel(
         __syncthreads();  // B3
 
         // ---------------- state pass on this wave's columns
-        if (c0 + C < t1) fetch(c0 + C);
+        fetch(c0 + C);
         {
             // v at token 16 rt + 4 g4 + i, column col + 16 ct + r (accumulator layout).
             float vv[NSB][NCT][4];
@@ -877,22 +871,28 @@ void chunk_ws_kernel(
     #pragma unroll
                     for (int m = 0; m < 8; ++m) G[m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
     #pragma unroll
-                    for (int m = 0; m < 8; ++m) Gt[m] = __shfl(G[m], 15, 16);
-                    float e1[8], La[8], Ra[8], Qa[8];
+                    for (int m = 0; m < 8; ++m) Gt[m] = row_bcast16<15>(G[m]);
+                    // Factors referenced to half the sub-block total: a = exp(G - tot/2),
+                    // 1/a, and the channel's exp(tot/2), which is a at the last token.
+                    // exp(G) = a exp(tot/2) and exp(tot - G) = exp(tot/2) / a.
+                    float xa[8], La[8], Ra[8], Qa[8], hh[8];
                     float span = 0.f;
     #pragma unroll
                     for (int m = 0; m < 8; ++m) {
-                        e1[m] = __builtin_amdgcn_exp2f(G[m]);
-                        const float e3 = __builtin_amdgcn_exp2f(Gt[m] - G[m]);
-                        const float hm = __builtin_amdgcn_exp2f(-0.5f * Gt[m]);    // exp(-tot/2)
-                        span = fmaxf(span, fabsf(G[m] - 0.5f * Gt[m]));
-                        const float L = kf[m] * e1[m], rb = kf[m] * e3, Lq = qf[m] * e1[m];
-                        l16[ks][m] = static_cast<_Float16>(L);
-                        rb16[ks][m] = static_cast<_Float16>(rb);
-                        q16[ks][m] = static_cast<_Float16>(Lq);
-                        La[m] = L * hm;
-                        Ra[m] = rb * hm;
-                        Qa[m] = Lq * hm;
+                        xa[m] = fmaf(-0.5f, Gt[m], G[m]);
+                        span = fmaxf(span, fabsf(xa[m]));
+                        const float a = __builtin_amdgcn_exp2f(xa[m]);
+                        const float ia = __builtin_amdgcn_exp2f(-xa[m]);
+                        La[m] = kf[m] * a;
+                        Ra[m] = kf[m] * ia;
+                        Qa[m] = qf[m] * a;
+                        hh[m] = row_bcast16<15>(a);
+                    }
+    #pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G)
+                        rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
+                        q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);   // q exp(G)
                     }
                     if (!__any(span > FAST_SPAN)) {
                         h8 la, ra, qa;
@@ -911,9 +911,11 @@ void chunk_ws_kernel(
                             accP = mfma4(Qa[m], Ra[m], accP);
                         }
                     }
-                    if (r == 15) {
-                        *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{e1[0], e1[1], e1[2], e1[3]};
-                        *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{e1[4], e1[5], e1[6], e1[7]};
+                    if (r == 15) {  // exp(tot) = exp(tot/2)^2
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch]) =
+                            f4{hh[0] * hh[0], hh[1] * hh[1], hh[2] * hh[2], hh[3] * hh[3]};
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) =
+                            f4{hh[4] * hh[4], hh[5] * hh[5], hh[6] * hh[6], hh[7] * hh[7]};
                     }
                     if (I == 0) *reinterpret_cast<h8*>(&sm.rbs[r][ch]) = rb16[ks];
                 }
@@ -1053,54 +1055,60 @@ void chunk_ws_kernel(
                     for (int i = 0; i < 4; ++i) S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
         }
     }
+        // Operands of the next chunk's state pass, prepared right after the
+        // previous S update (its v tile is in LDS by then): v, the scale
+        // exponent, and fp16 S (B operand of both K~ S and Q~ S).
+        float vv[NSB][NCT][4];
+        h8 s16[4][NCT];
+        float sig = 1.f;
+        auto prepare = [&](const Tiles& t) {
+    #pragma unroll
+            for (int rt = 0; rt < NSB; ++rt)
+    #pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        vv[rt][ct][i] = bf16_to_f32(t.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
+            float mv = 0.f, ms = 0.f;
+    #pragma unroll
+            for (int rt = 0; rt < NSB; ++rt)
+    #pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(vv[rt][ct][i]));
+    #pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+    #pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[rt][ct][i]));
+            const int nex = value_exponent(wave_max_nonneg(fmaxf(ms * ldexpf(1.f, -ex), mv)), ex);
+            if (nex != ex) {
+                const float f = ldexpf(1.f, nex - ex);
+    #pragma unroll
+                for (int rt = 0; rt < 8; ++rt)
+    #pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= f;
+                ex = nex;
+            }
+            sig = ldexpf(1.f, ex);
+    #pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+    #pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+    #pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        s16[ks][ct][m] = static_cast<_Float16>(S[2 * ks][ct][m]);
+                        s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
+                    }
+        };
         for (int c = -1; c < nch; ++c) {
             const bool swork = c >= 0;        // run chunk c
             const int64_t c0 = t0 + static_cast<int64_t>(c) * C;
             const Tiles& cur = sm.tl[c & 1];
-            Tiles& nxt = sm.tl[(c + 1) & 1];
+            const Tiles& nxt = sm.tl[(c + 1) & 1];
             const int valid = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
             if (swork) {
-                float vv[NSB][NCT][4];
-    #pragma unroll
-                for (int rt = 0; rt < NSB; ++rt)
-    #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-    #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            vv[rt][ct][i] = bf16_to_f32(cur.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
-                float mv = 0.f, ms = 0.f;
-    #pragma unroll
-                for (int rt = 0; rt < NSB; ++rt)
-    #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-    #pragma unroll
-                        for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(vv[rt][ct][i]));
-    #pragma unroll
-                for (int rt = 0; rt < 8; ++rt)
-    #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-    #pragma unroll
-                        for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[rt][ct][i]));
-                const int nex = value_exponent(wave_max_nonneg(fmaxf(ms * ldexpf(1.f, -ex), mv)), ex);
-                if (nex != ex) {
-                    const float f = ldexpf(1.f, nex - ex);
-    #pragma unroll
-                    for (int rt = 0; rt < 8; ++rt)
-    #pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= f;
-                    ex = nex;
-                }
-                const float sig = ldexpf(1.f, ex);
-                h8 s16[4][NCT];  // fp16 S (B operand of K~ S); rebuilt for Q~ S in the next interval
-    #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-    #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-    #pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            s16[ks][ct][m] = static_cast<_Float16>(S[2 * ks][ct][m]);
-                            s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
-                        }
                 f4 y[NSB][NCT];
     #pragma unroll
                 for (int rt = 0; rt < NSB; ++rt) {
@@ -1140,21 +1148,9 @@ void chunk_ws_kernel(
                         d16[ct][4 + m] = static_cast<_Float16>(d1[m]);
                     }
                 }
-        }
-            __syncthreads();
-            if (swork) {
+                // o of chunk c, right after its Delta
                 const float os = scale * ldexpf(1.f, -ex);
-            const int vlim = valid - 4 * g4;  // rows of this lane group still inside the chunk
-                h8 s16[4][NCT];
-    #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-    #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-    #pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            s16[ks][ct][m] = static_cast<_Float16>(S[2 * ks][ct][m]);
-                            s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
-                        }
+                const int vlim = valid - 4 * g4;  // rows of this lane group still inside the chunk
                 const auto ro = rsrc(o + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * sizeof(Tout));
                 const int vo = static_cast<int>(((4 * g4) * rowe + col + r) * sizeof(Tout));
     #pragma unroll
@@ -1182,7 +1178,7 @@ void chunk_ws_kernel(
                         }
                     }
                 }
-        }
+            }
             __syncthreads();
             if (swork) {
     #pragma unroll
@@ -1192,7 +1188,9 @@ void chunk_ws_kernel(
     #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb8, d16[ct], S[rt][ct] * lam);
                 }
-        }
+            }
+            __syncthreads();
+            if (c + 1 < nch) prepare(nxt);  // v of chunk c + 1 was staged in interval 2
             __syncthreads();
         }
         if (it.sout >= 0 && out_state) {
