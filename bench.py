@@ -12,6 +12,8 @@ as state/total HBM GB/s.  Inputs are generated on the device before the
 timed region.  The roofline entry is for the prefill kernel: algorithmic
 bytes per launch / average launch time from HIP events on the launch stream.
 The CPU baseline is the C oracle on a bounded sample of the same workload.
+Entry points outside the hot path (a short run of tokens per sequence with
+the state in place) are timed after the steps and reported under "extras".
 
     python bench.py [--steps K] [--warmup W] [--workload varlen|long|prefill]
 """
@@ -48,6 +50,28 @@ def decode_alg_bytes(N, H, dk, dv, in_bytes=2, out_bytes=4):
     state = N * H * dk * dv * 4 * 2
     other = N * H * ((2 * dk + dv) * in_bytes + dk * 4 + 4 + dv * out_bytes)
     return state, state + other
+
+
+def steps_alg_bytes(N, T, H, dk, dv, in_bytes=2, out_bytes=4):
+    """A run of T tokens per sequence with the state in place: the state is
+    read and written once, the per-token vectors once."""
+    state = N * H * dk * dv * 4 * 2
+    return state + N * T * H * ((2 * dk + dv) * in_bytes + dk * 4 + 4 + dv * out_bytes)
+
+
+def time_launches(fn, stream, reps, warmup=2):
+    """Average milliseconds of fn() between HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
 
 
 def code_sha256(path):
@@ -149,6 +173,8 @@ def main():
     ap.add_argument("--variant", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the entry points outside the timed step (short runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device copy first (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -256,6 +282,20 @@ def main():
                           "total_gbs": tb / (dm * 1e-3) / 1e9,
                           "frac": tb / (dm * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "config": f"{N3} sequences x {H3} heads, d=128"}
+    if not args.no_extras:
+        # Outside the timed step: a short run of 8 tokens per sequence with the
+        # state in place (speculative verification), through kda_fused_recurrent_fwd.
+        vx = synth.make_inputs("verify", device=dev)
+        Nv, Tv, Hv, dkv = vx.q.shape
+        vst = vx.h0.clone()
+        vo = torch.empty(Nv, Tv, Hv, vx.v.shape[-1], device=dev)
+        vm = time_launches(lambda: kda.fused_recurrent_fwd(vx.q, vx.k, vx.v, vx.g, vx.beta,
+                                                           vx.scale, vst, o=vo), stream, 10)
+        vb = steps_alg_bytes(Nv, Tv, Hv, dkv, vx.v.shape[-1])
+        line["extras"] = {"fused_recurrent": {
+            "us_per_launch": vm * 1e3, "gbs": vb / (vm * 1e-3) / 1e9,
+            "frac": vb / (vm * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": vb,
+            "config": f"{Nv} sequences x {Tv} tokens x {Hv} heads, d={dkv}, state in place"}}
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(x)

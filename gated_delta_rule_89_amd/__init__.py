@@ -7,6 +7,9 @@ include/kda.h); this package is a thin binding over it:
         -> (o, final_state)          chunked prefill, varlen via cu_seqlens
     decode_step(q, k, v, g, beta, scale, state) -> o
                                      one token per sequence, state in place
+    fused_recurrent_fwd(q, k, v, g, beta, scale, state) -> o
+                                     a short run of tokens per sequence
+                                     (T <= 64), state in place
 """
-from ._lib import (KDAError, abi_version, chunk_fwd, decode_step, lib, status_str,  # noqa: F401
-                   workspace_size)
+from ._lib import (KDAError, abi_version, chunk_fwd, decode_step, fused_recurrent_fwd,  # noqa: F401
+                   lib, status_str, workspace_size)

@@ -23,7 +23,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
 F32, BF16 = 0, 1
 VARIANTS = {"auto": 0, "recurrent": 1, "chunk": 2, "chunk_scan": 3, "chunk64": 4}
 EXPORTS = ("kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_size",
-           "kda_chunk_fwd", "kda_decode_step")
+           "kda_chunk_fwd", "kda_decode_step", "kda_fused_recurrent_fwd")
+FUSED_RECURRENT_MAX_T = 64
 
 
 class KDAError(RuntimeError):
@@ -49,6 +50,9 @@ def _load() -> ctypes.CDLL:
     lib.kda_decode_step.argtypes = [P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, I32,
                                     ctypes.c_int, ctypes.c_int, P, P]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_fused_recurrent_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, I32,
+                                            I32, ctypes.c_int, ctypes.c_int, P, P]
+    lib.kda_fused_recurrent_fwd.restype = ctypes.c_int
     return lib
 
 
@@ -171,5 +175,24 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     code = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
                                _ptr(state), N, H, dk, dv, _dt(q.dtype), _dt(o.dtype), _ptr(o),
                                _stream(q.device))
+    _check(code)
+    return o
+
+
+def fused_recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                        beta: torch.Tensor, scale: float, state: torch.Tensor,
+                        out_dtype: torch.dtype = torch.float32, o: Optional[torch.Tensor] = None):
+    """kda_fused_recurrent_fwd: q, k, g [N, T, H, dk]; v [N, T, H, dv];
+    beta [N, T, H]; state [N, H, dk, dv] fp32, updated in place after the
+    run of T tokens.  Returns o [N, T, H, dv]."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state)):
+        _dev(t, name)
+    N, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty(N, T, H, dv, dtype=out_dtype, device=q.device)
+    code = lib.kda_fused_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                                       _ptr(state), N, T, H, dk, dv, _dt(q.dtype), _dt(o.dtype),
+                                       _ptr(o), _stream(q.device))
     _check(code)
     return o

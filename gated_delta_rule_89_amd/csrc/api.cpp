@@ -256,8 +256,54 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
     a.in_bf16 = in_dtype == KDA_BF16;
     a.out_bf16 = out_dtype == KDA_BF16;
     a.o = o;
+    a.T = 1;
     a.stream = static_cast<hipStream_t>(stream);
     return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_fused_recurrent_fwd(const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, float scale, float* state, int32_t N,
+                                   int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                   kda_dtype in_dtype, kda_dtype out_dtype, void* o,
+                                   void* stream) {
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
+    if (N < 0 || T < 0 || H < 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_SHAPE;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (T > KDA_FUSED_RECURRENT_MAX_T) return KDA_ERR_UNSUPPORTED;
+    if (N == 0 || H == 0 || T == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_NULL;
+    if (static_cast<int64_t>(N) * H > INT32_MAX) return KDA_ERR_SHAPE;
+    for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(state), static_cast<const void*>(o)})
+        if (!aligned(p, 16)) return KDA_ERR_ALIGN;
+    if (!aligned(beta, 4)) return KDA_ERR_ALIGN;
+    const size_t nh = static_cast<size_t>(N) * H, nth = nh * static_cast<size_t>(T);
+    const Range in_r[] = {range(q, nth * d_k * esize(in_dtype)), range(k, nth * d_k * esize(in_dtype)),
+                          range(v, nth * d_v * esize(in_dtype)), range(g, nth * d_k * 4),
+                          range(beta, nth * 4)};
+    const Range s_r = range(state, nh * d_k * d_v * 4);
+    const Range o_r = range(o, nth * d_v * esize(out_dtype));
+    for (const Range& r : in_r)
+        if (overlap(o_r, r) || overlap(s_r, r)) return KDA_ERR_ALIAS;
+    if (overlap(o_r, s_r)) return KDA_ERR_ALIAS;
+
+    DecodeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.scale = scale;
+    a.state = state;
+    a.N = N;
+    a.H = H;
+    a.dk = d_k;
+    a.dv = d_v;
+    a.T = T;
+    a.in_bf16 = in_dtype == KDA_BF16;
+    a.out_bf16 = out_dtype == KDA_BF16;
+    a.o = o;
+    a.stream = static_cast<hipStream_t>(stream);
+    return kda::launch_steps(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // extern "C"

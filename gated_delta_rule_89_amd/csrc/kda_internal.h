@@ -37,6 +37,7 @@ struct DecodeArgs {
     float scale;
     float* state;
     int N, H, dk, dv;
+    int T;            // tokens per sequence (1 for a decode step)
     bool in_bf16, out_bf16;
     void* o;
     hipStream_t stream;
@@ -67,6 +68,7 @@ hipError_t dispatch_head_sizes(int dk, int dv, F&& f) {
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);
 hipError_t launch_recurrent(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_steps(const DecodeArgs& a);
 
 // Chunked MFMA prefill (bf16 inputs, d_k = d_v = 128).  With scan = true long
 // sequences are cut into segments whose (B, M) maps are composed by a scan.

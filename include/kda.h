@@ -157,6 +157,35 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
                            int32_t d_k, int32_t d_v, kda_dtype in_dtype, kda_dtype out_dtype,
                            void* o, void* stream);
 
+/* Longest run kda_fused_recurrent_fwd accepts. */
+#define KDA_FUSED_RECURRENT_MAX_T 64
+
+/* T consecutive tokens for each of N independent sequences, state updated in
+ * place: the fused recurrent mode of "Understanding Kimi Delta Attention"
+ * (section "Two execution modes": token by token with the state resident)
+ * over a short run, as when a draft of several tokens is verified or a short
+ * prompt is appended to a cached state.  The result equals T calls of
+ * kda_decode_step, one per token in order, but the state is read and
+ * written once for the whole run.
+ *
+ *  q, k        [N, T, H, d_k]  in_dtype
+ *  v           [N, T, H, d_v]  in_dtype
+ *  g           [N, T, H, d_k]  fp32, log forget gate
+ *  beta        [N, T, H]       fp32
+ *  scale       read-out scale
+ *  state       [N, H, d_k, d_v] fp32, read and overwritten with the state
+ *              after token T-1
+ *  o           [N, T, H, d_v]  out_dtype, written for every token; must not
+ *              overlap any input or the state.
+ * 0 <= T <= KDA_FUSED_RECURRENT_MAX_T (longer runs return
+ * KDA_ERR_UNSUPPORTED: kda_chunk_fwd is the path for them).  N = 0, H = 0 or
+ * T = 0 is a successful no-op. */
+kda_status kda_fused_recurrent_fwd(const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, float scale, float* state, int32_t N,
+                                   int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                   kda_dtype in_dtype, kda_dtype out_dtype, void* o,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

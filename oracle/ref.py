@@ -88,3 +88,13 @@ def kda_decode(q, k, v, g, beta, scale, state, dtype=np.float64):
     o, final = kda_forward(q[:, None], k[:, None], v[:, None], g[:, None], beta[:, None],
                            scale, s, None, dtype)
     return o[:, 0], final
+
+
+def kda_fused_recurrent(q, k, v, g, beta, scale, state, dtype=np.float64):
+    """A run of T tokens for each of N independent sequences from a given
+    state: q, k, g [N, T, H, dk]; v [N, T, H, dv]; beta [N, T, H];
+    state [N, H, dk, dv].  Returns (o [N, T, H, dv], state after the run).
+    Row n of the batch is one chain, so this is the sequential recurrence
+    above with the rows as sequences (the fused recurrent mode of the first
+    page run over several tokens)."""
+    return kda_forward(q, k, v, g, beta, scale, state, None, dtype)

@@ -2,7 +2,7 @@
 
 This module is shared by the oracle tests, the GPU parity tests and the
 benchmark.  It draws random tensors of the shapes and distributions of the
-five workloads below and holds none of the operator's arithmetic: the L2
+six workloads below and holds none of the operator's arithmetic: the L2
 normalisation of q/k, the sigmoid for beta and the softplus for the log-gate
 are the upstream projections that feed the operator (q/k normalisation and the
 sigmoid update gate: "kimi delta attn from first principles", sections "three
@@ -14,6 +14,8 @@ Workloads (names used everywhere in the repository):
   prefill B=1, T=4096, H=8, d=128, bf16 q/k/v, g=-softplus(N(0,2)-2),
           h0 ~ N(0, 0.02)
   decode  256 sequences x H=32, one token each, d=128, state ~ N(0, 0.02)
+  verify  256 sequences x H=32, a run of 8 tokens each (a speculative draft
+          checked against a cached state), d=128, state ~ N(0, 0.02)
   varlen  64 packed sequences, lengths log-uniform in [512, 32768] with an
           exact total of 262144 tokens, H=32, per-sequence h0 ~ N(0, 0.02)
   long    B=1, T=1048576, H=32, g=-softplus(N(0,2)-3), zero h0
@@ -55,6 +57,7 @@ class Workload:
     seed: int
     n_seqs: int = 1
     decode: bool = False
+    steps: int = 1         # tokens per sequence of a state-in-place run
 
     @property
     def scale(self) -> float:
@@ -68,6 +71,9 @@ WORKLOADS = {
                         g_mu=-2.0, g_sigma=2.0, h0_std=0.02, seed=2),
     "decode": Workload("decode", H=32, dk=128, dv=128, T=256, in_dtype=torch.bfloat16,
                        g_mu=-2.0, g_sigma=2.0, h0_std=0.02, seed=3, n_seqs=256, decode=True),
+    "verify": Workload("verify", H=32, dk=128, dv=128, T=256, in_dtype=torch.bfloat16,
+                       g_mu=-2.0, g_sigma=2.0, h0_std=0.02, seed=6, n_seqs=256, decode=True,
+                       steps=8),
     "varlen": Workload("varlen", H=32, dk=128, dv=128, T=262144, in_dtype=torch.bfloat16,
                        g_mu=-2.0, g_sigma=2.0, h0_std=0.02, seed=4, n_seqs=64),
     "long": Workload("long", H=32, dk=128, dv=128, T=1048576, in_dtype=torch.bfloat16,
@@ -109,7 +115,8 @@ def cu_seqlens_from_lengths(lens) -> np.ndarray:
 @dataclass
 class KDAInputs:
     """One batch of operator inputs.  q/k/v/g/beta are [B, T, H, d] ([B, T, H]
-    for beta); for decode B is the number of sequences and T is 1."""
+    for beta); for decode and verify B is the number of sequences and T the
+    tokens per sequence (1 for decode)."""
     q: torch.Tensor
     k: torch.Tensor
     v: torch.Tensor
@@ -176,10 +183,13 @@ def make_inputs(name: str, device="cpu", T: Optional[int] = None, H: Optional[in
     seed = w.seed if seed is None else seed
     if w.decode:
         N = w.n_seqs if n_seqs is None else n_seqs
-        q, k, v, beta, g = draw_tokens(N, H, w.dk, w.dv, w.in_dtype, w.g_mu, w.g_sigma, seed, device)
+        S = w.steps if T is None else T  # tokens per sequence
+        q, k, v, beta, g = draw_tokens(N * S, H, w.dk, w.dv, w.in_dtype, w.g_mu, w.g_sigma, seed,
+                                       device)
         h0 = draw_state(N, H, w.dk, w.dv, w.h0_std, seed, device)
-        return KDAInputs(q[:, None], k[:, None], v[:, None], g[:, None], beta[:, None], w.scale,
-                         h0, None, {"workload": name, "N": N, "H": H})
+        q, k, v, g = (x.view(N, S, H, x.shape[-1]) for x in (q, k, v, g))
+        return KDAInputs(q, k, v, g, beta.view(N, S, H), w.scale, h0, None,
+                         {"workload": name, "N": N, "T": S, "H": H})
     cu = None
     if lens is not None:
         cu = cu_seqlens_from_lengths(lens)

@@ -142,3 +142,30 @@ def test_decode_validation():
     assert decode(o=addr(5)) == ALIAS                 # o over the state
     assert decode(state=addr(2)) == ALIAS             # state over v
     assert decode(N=0) == OK                          # no-op, nothing launched
+
+
+def steps(q=None, k=None, v=None, g=None, beta=None, state=None, N=4, T=5, H=2, dk=16, dv=16,
+          ind=F32, outd=F32, o=None):
+    q = addr(0) if q is None else q
+    k = addr(1) if k is None else k
+    v = addr(2) if v is None else v
+    g = addr(3) if g is None else g
+    beta = addr(4) if beta is None else beta
+    state = addr(5) if state is None else state
+    o = addr(6) if o is None else o
+    return kda.lib.kda_fused_recurrent_fwd(q, k, v, g, beta, 0.25, state, N, T, H, dk, dv,
+                                           ind, outd, o, None)
+
+
+def test_fused_recurrent_validation():
+    assert steps(outd=9) == DTYPE
+    assert steps(T=-1) == SHAPE
+    assert steps(dv=24) == UNSUP
+    assert steps(T=_lib.FUSED_RECURRENT_MAX_T + 1) == UNSUP   # long runs belong to kda_chunk_fwd
+    assert steps(beta=P(0)) == NULL
+    assert steps(v=addr(2, 8)) == ALIGN
+    assert steps(beta=addr(4, 1)) == ALIGN
+    # o spans N*T*H*dv*4 bytes: one ending inside q's range overlaps it
+    assert steps(o=addr(0, 64)) == ALIAS
+    assert steps(state=addr(6, 4 * 5 * 2 * 16 * 4 - 16)) == ALIAS   # state starts inside o
+    assert steps(T=0) == OK and steps(N=0) == OK                      # no-ops

@@ -137,6 +137,77 @@ def test_decode_head_sizes(dk, dv, ind):
     assert max_abs(o, o_ref) <= 1e-4 and max_abs(st, s_ref) <= 1e-4
 
 
+def test_fused_recurrent_verify_workload_full():
+    say("fused recurrent N=256 T=8 H=32 d=128 bf16 (verify workload)")
+    x = synth.make_inputs("verify")
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    st = xd.h0.clone()
+    o = _kda().fused_recurrent_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, st)
+    torch.cuda.synchronize()
+    o_ref, s_ref = cref.kda_forward(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0, None,
+                                    n_threads=THREADS)
+    e1, e2 = max_abs(o, o_ref), max_abs(st, s_ref)
+    say(f"  o max-abs {e1:.2e}  state max-abs {e2:.2e}")
+    assert e1 <= 1e-4 and e2 <= 1e-4   # fp32 arithmetic on exact inputs
+
+
+@pytest.mark.parametrize("dk,dv,ind,T", [(16, 16, torch.float32, 1), (64, 128, torch.bfloat16, 5),
+                                          (128, 32, torch.float32, 64), (32, 64, torch.bfloat16, 17),
+                                          (128, 128, torch.bfloat16, 3)])
+def test_fused_recurrent_shapes(dk, dv, ind, T):
+    say(f"fused recurrent dk={dk} dv={dv} {ind} T={T}")
+    rng = np.random.default_rng(dk + dv + T)
+    N, H = 5, 3
+    q = torch.tensor(rng.standard_normal((N, T, H, dk)), dtype=torch.float32).to(ind)
+    k = torch.nn.functional.normalize(torch.tensor(rng.standard_normal((N, T, H, dk))),
+                                      dim=-1).to(ind)
+    v = torch.tensor(rng.standard_normal((N, T, H, dv)), dtype=torch.float32).to(ind)
+    g = -torch.rand(N, T, H, dk, generator=torch.Generator().manual_seed(1))
+    beta = torch.rand(N, T, H, generator=torch.Generator().manual_seed(2))
+    s0 = torch.randn(N, H, dk, dv, generator=torch.Generator().manual_seed(3))
+    dev = torch.device("cuda")
+    st = s0.to(dev)
+    o = _kda().fused_recurrent_fwd(q.to(dev), k.to(dev), v.to(dev), g.to(dev), beta.to(dev),
+                                   0.7, st, out_dtype=ind)
+    torch.cuda.synchronize()
+    o_ref, s_ref = ref.kda_fused_recurrent(q, k, v, g, beta, 0.7, s0)
+    assert max_abs(st, s_ref) <= 1e-4
+    if ind == torch.float32:
+        assert max_abs(o, o_ref) <= 1e-4
+    else:  # bf16 output: one rounding of each value
+        assert rel_rms(o, o_ref) <= 2e-2 and max_abs(o, o_ref) <= 8e-3 * float(np.abs(o_ref).max())
+
+
+def test_fused_recurrent_equals_decode_steps():
+    say("fused recurrent T=6 == six decode steps (N=64, H=4, d=128, bf16)")
+    x = synth.make_inputs("verify", n_seqs=64, H=4, T=6)
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    kda = _kda()
+    s1 = xd.h0.clone()
+    o = kda.fused_recurrent_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, s1)
+    s2 = xd.h0.clone()
+    od = [kda.decode_step(xd.q[:, t].contiguous(), xd.k[:, t].contiguous(), xd.v[:, t].contiguous(),
+                          xd.g[:, t].contiguous(), xd.beta[:, t].contiguous(), x.scale, s2)
+          for t in range(6)]
+    torch.cuda.synchronize()
+    assert max_abs(o, torch.stack(od, 1)) <= 1e-5 and max_abs(s1, s2) <= 1e-5
+
+
+def test_fused_recurrent_empty_and_rejects_long_runs():
+    say("fused recurrent T=0 no-op; T=65 rejected")
+    kda = _kda()
+    dev = torch.device("cuda")
+    st = torch.ones(2, 1, 16, 16, device=dev)
+    z = torch.zeros(2, 0, 1, 16, device=dev)
+    o = kda.fused_recurrent_fwd(z, z, z, z, torch.zeros(2, 0, 1, device=dev), 1.0, st)
+    assert o.shape == (2, 0, 1, 16) and bool((st == 1).all())
+    x = torch.zeros(2, 65, 1, 16, device=dev)
+    with pytest.raises(kda.KDAError):
+        kda.fused_recurrent_fwd(x, x, x, x, torch.zeros(2, 65, 1, device=dev), 1.0, st)
+
+
 def test_prefill_then_decode_equals_prefill():
     say("prefill T-1 then decode == prefill T (H=4, T=300)")
     x = synth.make_inputs("prefill", T=300, H=4)

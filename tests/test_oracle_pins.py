@@ -195,3 +195,23 @@ def test_decode_is_one_step_of_forward():
     od, fd = ref.kda_decode(q[:, -1], k[:, -1], v[:, -1], g[:, -1], beta[:, -1], 0.5, f1)
     assert np.max(np.abs(od[0] - o[0, -1])) < 1e-13
     assert np.max(np.abs(fd - f)) < 1e-13
+
+
+def test_fused_recurrent_is_successive_decode_steps():
+    """A run of T tokens from a state equals T single-token steps in order,
+    with each row of the batch its own chain (rows must not mix)."""
+    rng = np.random.default_rng(9)
+    N, T, H, dk, dv = 3, 5, 2, 6, 4
+    q, k, v = (rng.standard_normal((N, T, H, d)) for d in (dk, dk, dv))
+    g = -rng.random((N, T, H, dk))
+    beta = rng.random((N, T, H))
+    s0 = rng.standard_normal((N, H, dk, dv))
+    o, f = ref.kda_fused_recurrent(q, k, v, g, beta, 0.5, s0)
+    s = s0.copy()
+    for t in range(T):
+        od, s = ref.kda_decode(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], 0.5, s)
+        assert np.max(np.abs(od - o[:, t])) < 1e-13
+    assert np.max(np.abs(s - f)) < 1e-13
+    # each row from its own state: row 1 alone gives the same result
+    o1, f1 = ref.kda_fused_recurrent(q[1:2], k[1:2], v[1:2], g[1:2], beta[1:2], 0.5, s0[1:2])
+    assert np.max(np.abs(o1[0] - o[1])) < 1e-13 and np.max(np.abs(f1[0] - f[1])) < 1e-13
