@@ -296,6 +296,28 @@ def main():
             "us_per_launch": vm * 1e3, "gbs": vb / (vm * 1e-3) / 1e9,
             "frac": vb / (vm * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": vb,
             "config": f"{Nv} sequences x {Tv} tokens x {Hv} heads, d={dkv}, state in place"}}
+        if args.workload == "varlen":
+            # The same prefill with the state of every sequence kept each 4096 tokens
+            # (kda_chunk_fwd_snapshots), against the plain prefill timed above.
+            iv = 4096
+            lens = [T] * N if x.cu_seqlens is None else list(int(a) for a in
+                                                             (x.cu_seqlens[1:] - x.cu_seqlens[:-1]))
+            nsn = int(kda.snapshot_rows(lens, iv)[-1])
+            snb = torch.empty(nsn, H, dk, dv, device=dev)
+            sws = torch.empty(max(1, kda.snapshots_workspace_size(B, T, H, dk, dv, N, iv, x.q.dtype,
+                                                                  args.variant, cu_host)),
+                              dtype=torch.uint8, device=dev)
+            sm = time_launches(lambda: kda.chunk_fwd_snapshots(
+                x.q, x.k, x.v, x.g, x.beta, x.scale, iv, initial_state=x.h0, cu_seqlens=cu_dev,
+                cu_seqlens_host=cu_host, o=o, final_state=fin, snapshots=snb, workspace=sws,
+                variant=args.variant),
+                stream, 5)
+            sb = alg_b + nsn * H * dk * dv * 4
+            line["extras"]["snapshots"] = {
+                "ms_per_launch": sm, "plain_ms": pre_avg, "overhead": sm / pre_avg - 1.0,
+                "snapshots": nsn, "gbs": sb / (sm * 1e-3) / 1e9,
+                "frac": sb / (sm * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": sb,
+                "config": f"{args.workload} prefill with the state every {iv} tokens"}
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(x)

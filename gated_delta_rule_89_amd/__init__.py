@@ -7,9 +7,12 @@ include/kda.h); this package is a thin binding over it:
         -> (o, final_state)          chunked prefill, varlen via cu_seqlens
     decode_step(q, k, v, g, beta, scale, state) -> o
                                      one token per sequence, state in place
+    chunk_fwd_snapshots(q, k, v, g, beta, scale, interval, ...)
+        -> (o, final_state, snapshots) states every `interval` tokens
     fused_recurrent_fwd(q, k, v, g, beta, scale, state) -> o
                                      a short run of tokens per sequence
                                      (T <= 64), state in place
 """
-from ._lib import (KDAError, abi_version, chunk_fwd, decode_step, fused_recurrent_fwd,  # noqa: F401
-                   lib, status_str, workspace_size)
+from ._lib import (KDAError, abi_version, chunk_fwd, chunk_fwd_snapshots, decode_step,  # noqa: F401
+                   fused_recurrent_fwd, lib, snapshot_rows, snapshots_workspace_size, status_str,
+                   workspace_size)

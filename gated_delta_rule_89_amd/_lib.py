@@ -23,7 +23,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
 F32, BF16 = 0, 1
 VARIANTS = {"auto": 0, "recurrent": 1, "chunk": 2, "chunk_scan": 3, "chunk64": 4}
 EXPORTS = ("kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_size",
-           "kda_chunk_fwd", "kda_decode_step", "kda_fused_recurrent_fwd")
+           "kda_chunk_fwd", "kda_decode_step", "kda_fused_recurrent_fwd",
+           "kda_chunk_fwd_snapshots_workspace_size", "kda_chunk_fwd_snapshots")
 FUSED_RECURRENT_MAX_T = 64
 
 
@@ -53,6 +54,12 @@ def _load() -> ctypes.CDLL:
     lib.kda_fused_recurrent_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, I32,
                                             I32, ctypes.c_int, ctypes.c_int, P, P]
     lib.kda_fused_recurrent_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_snapshots_workspace_size.argtypes = [I32] * 6 + [P, ctypes.c_int, ctypes.c_int, I32]
+    lib.kda_chunk_fwd_snapshots_workspace_size.restype = SZ
+    lib.kda_chunk_fwd_snapshots.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P,
+                                            I32, I32, I32, I32, I32, I32, ctypes.c_int, ctypes.c_int,
+                                            P, P, I32, P, P, SZ, ctypes.c_int, P]
+    lib.kda_chunk_fwd_snapshots.restype = ctypes.c_int
     return lib
 
 
@@ -103,6 +110,29 @@ def workspace_size(B, T, H, dk, dv, N, in_dtype=torch.bfloat16, variant="auto",
                                                 VARIANTS[variant]))
 
 
+def snapshots_workspace_size(B, T, H, dk, dv, N, interval, in_dtype=torch.bfloat16,
+                             variant="auto", cu_seqlens_host=None) -> int:
+    """Workspace bytes kda_chunk_fwd_snapshots needs for these sizes."""
+    ptr = None if cu_seqlens_host is None else ctypes.c_void_p(cu_seqlens_host.data_ptr())
+    return int(lib.kda_chunk_fwd_snapshots_workspace_size(B, T, H, dk, dv, N, ptr, _dt(in_dtype),
+                                                          VARIANTS[variant], int(interval)))
+
+
+def snapshot_rows(lengths, interval: int) -> np.ndarray:
+    """Row of every sequence's first snapshot and, last, the total: an
+    exclusive prefix sum of floor(length / interval)."""
+    cnt = np.asarray(lengths, dtype=np.int64) // int(interval)
+    return np.concatenate([[0], np.cumsum(cnt)]).astype(np.int64)
+
+
+def chunk_fwd_snapshots(q, k, v, g, beta, scale, snapshot_interval: int, **kw):
+    """kda_chunk_fwd_snapshots: chunk_fwd that also returns the state of every
+    sequence after each `snapshot_interval` tokens (a multiple of 64).
+    Returns (o, final_state, snapshots [total, H, dk, dv]); sequence n's
+    snapshots are rows snapshot_rows(lengths, interval)[n] onwards."""
+    return chunk_fwd(q, k, v, g, beta, scale, snapshot_interval=snapshot_interval, **kw)
+
+
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
               beta: torch.Tensor, scale: float, initial_state: Optional[torch.Tensor] = None,
               cu_seqlens: Union[None, torch.Tensor, np.ndarray, Sequence[int]] = None,
@@ -110,13 +140,16 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               variant: str = "auto", o: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None,
-              cu_seqlens_host: Optional[torch.Tensor] = None):
+              cu_seqlens_host: Optional[torch.Tensor] = None,
+              snapshot_interval: Optional[int] = None,
+              snapshots: Optional[torch.Tensor] = None):
     """kda_chunk_fwd on torch tensors.  q, k, g: [B, T, H, dk]; v: [B, T, H, dv];
     beta: [B, T, H]; initial_state [N, H, dk, dv] fp32 or None; cu_seqlens int32
     [N+1] (device tensor, CPU tensor, numpy array or list) or None.  A caller
     holding both copies passes the device tensor as cu_seqlens and an int32 CPU
     tensor as cu_seqlens_host, and no copy is made.
-    Returns (o [B, T, H, dv], final_state [N, H, dk, dv] or None)."""
+    Returns (o [B, T, H, dv], final_state [N, H, dk, dv] or None), and with
+    snapshot_interval also the snapshots (kda_chunk_fwd_snapshots)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         _dev(t, name)
     B, T, H, dk = q.shape
@@ -148,6 +181,24 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
     if not output_final_state:
         final_state = None
+    if snapshot_interval is not None:
+        lens = np.diff(cu_host.numpy()) if cu_host is not None else np.full(N, T)
+        total = int(snapshot_rows(lens, snapshot_interval)[-1]) if snapshot_interval > 0 else 0
+        if snapshots is None:
+            snapshots = torch.empty(total, H, dk, dv, dtype=torch.float32, device=dev)
+        cu_ptr = None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr())
+        ws_bytes = snapshots_workspace_size(B, T, H, dk, dv, N, snapshot_interval, q.dtype, variant,
+                                            cu_host)
+        if workspace is None and ws_bytes > 0:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        code = lib.kda_chunk_fwd_snapshots(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
+            _ptr(cu_dev), cu_ptr, B, T, H, dk, dv, N, _dt(q.dtype), _dt(o.dtype), _ptr(o),
+            _ptr(final_state), int(snapshot_interval), _ptr(snapshots) if snapshots.numel() else None,
+            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+            VARIANTS[variant], _stream(dev))
+        _check(code)
+        return o, final_state, snapshots
     ws_bytes = workspace_size(B, T, H, dk, dv, N, q.dtype, variant, cu_host)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

@@ -75,6 +75,15 @@ size_t workspace_for(kda_variant v, int32_t B, int32_t T, int32_t H, int32_t N, 
     return 0;
 }
 
+size_t align256_(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Snapshots over all sequences: floor(length / interval) each.
+int64_t snapshot_count(const int32_t* cu_host, int32_t N, int32_t T, int32_t interval) {
+    int64_t c = 0;
+    for (int32_t n = 0; n < N; ++n) c += (cu_host ? cu_host[n + 1] - cu_host[n] : T) / interval;
+    return c;
+}
+
 bool seqlens_ok(const int32_t* cu_host, int32_t N, int32_t T) {
     if (cu_host[0] != 0 || cu_host[N] != T) return false;
     for (int32_t i = 0; i < N; ++i)
@@ -115,14 +124,21 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
     return workspace_for(v, B, T, H, N, cu_seqlens_host);
 }
 
-kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, float scale, const float* initial_state,
-                         const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t B,
-                         int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
-                         kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* final_state,
-                         void* workspace, size_t workspace_bytes, kda_variant variant,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// kda_chunk_fwd and kda_chunk_fwd_snapshots; snap_mode selects the latter.
+kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, float scale, const float* initial_state,
+                          const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t B,
+                          int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
+                          kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* final_state,
+                          void* workspace, size_t workspace_bytes, kda_variant variant,
+                          void* stream, bool snap_mode, int32_t snap_interval, float* snapshots) {
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
+    if (snap_mode && snap_interval <= 0) return KDA_ERR_SHAPE;
+    if (snap_mode && snap_interval % 64 != 0) return KDA_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || H < 0 || N < 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_SHAPE;
     if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDA_ERR_UNSUPPORTED;
     if (variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK64) return KDA_ERR_UNSUPPORTED;
@@ -163,7 +179,12 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if (!aligned(beta, 4) || !aligned(cu_seqlens, 4) || !aligned(workspace, 256))
         return KDA_ERR_ALIGN;
 
-    const size_t ws_need = workspace_for(var, B, T, H, N, cu_seqlens_host);
+    const int64_t nsnap = snap_mode ? snapshot_count(cu_seqlens_host, N, T, snap_interval) : 0;
+    if (nsnap > 0 && !snapshots) return KDA_ERR_NULL;
+    if (!aligned(snapshots, 16)) return KDA_ERR_ALIGN;
+    if (nsnap > INT32_MAX / 2) return KDA_ERR_SHAPE;
+    const size_t ws_plain = workspace_for(var, B, T, H, N, cu_seqlens_host);
+    const size_t ws_need = nsnap > 0 ? align256_(ws_plain) + align256_(static_cast<size_t>(N) * 4) : ws_plain;
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need)) return KDA_ERR_WORKSPACE;
 
     const size_t th = static_cast<size_t>(tokens) * H;
@@ -182,6 +203,12 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
         if (!same_state && overlap(f_r, r)) return KDA_ERR_ALIAS;
     }
     if (overlap(o_r, f_r) || overlap(o_r, w_r) || overlap(f_r, w_r)) return KDA_ERR_ALIAS;
+    if (nsnap > 0) {
+        const Range s_r = range(snapshots, static_cast<size_t>(nsnap) * H * d_k * d_v * 4);
+        for (const Range& r : in_r)
+            if (overlap(s_r, r)) return KDA_ERR_ALIAS;
+        if (overlap(s_r, o_r) || overlap(s_r, f_r) || overlap(s_r, w_r)) return KDA_ERR_ALIAS;
+    }
 
     PrefillArgs a{};
     a.q = q;
@@ -206,6 +233,14 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     a.ws = workspace;
     a.ws_bytes = workspace_bytes;
     a.stream = static_cast<hipStream_t>(stream);
+    if (nsnap > 0) {
+        int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256_(ws_plain));
+        a.snaps = snapshots;
+        a.snap_interval = snap_interval;
+        a.snap_base = base;
+        if (kda::launch_snap_base(cu_seqlens, N, T, snap_interval, base, a.stream) != hipSuccess)
+            return KDA_ERR_HIP;
+    }
 
     hipError_t e = hipErrorInvalidValue;
     switch (var) {
@@ -216,6 +251,51 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
         default: return KDA_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, float scale, const float* initial_state,
+                         const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t B,
+                         int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
+                         kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, kda_variant variant,
+                         void* stream) {
+    return chunk_fwd_impl(q, k, v, g, beta, scale, initial_state, cu_seqlens, cu_seqlens_host, B, T,
+                          H, d_k, d_v, N, in_dtype, out_dtype, o, final_state, workspace,
+                          workspace_bytes, variant, stream, false, 0, nullptr);
+}
+
+size_t kda_chunk_fwd_snapshots_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                              int32_t d_v, int32_t N,
+                                              const int32_t* cu_seqlens_host, kda_dtype in_dtype,
+                                              kda_variant variant, int32_t snap_interval) {
+    if (snap_interval <= 0 || snap_interval % 64 != 0) return 0;
+    if (B < 0 || T < 0 || H < 0 || N < 0 || !head_size_ok(d_k) || !head_size_ok(d_v) ||
+        !dtype_ok(in_dtype) || variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK64)
+        return 0;
+    if (cu_seqlens_host ? (B != 1 || !seqlens_ok(cu_seqlens_host, N, T)) : N != B) return 0;
+    const kda_variant v = resolve_variant(variant, B, T, H, d_k, d_v, N, in_dtype, cu_seqlens_host);
+    const size_t plain = workspace_for(v, B, T, H, N, cu_seqlens_host);
+    if (static_cast<int64_t>(B) * T == 0 || snapshot_count(cu_seqlens_host, N, T, snap_interval) == 0)
+        return plain;
+    return align256_(plain) + align256_(static_cast<size_t>(N) * 4);
+}
+
+kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, float scale, const float* initial_state,
+                                   const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                   int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                   int32_t N, kda_dtype in_dtype, kda_dtype out_dtype, void* o,
+                                   float* final_state, int32_t snap_interval, float* snapshots,
+                                   void* workspace, size_t workspace_bytes, kda_variant variant,
+                                   void* stream) {
+    return chunk_fwd_impl(q, k, v, g, beta, scale, initial_state, cu_seqlens, cu_seqlens_host, B, T,
+                          H, d_k, d_v, N, in_dtype, out_dtype, o, final_state, workspace,
+                          workspace_bytes, variant, stream, true, snap_interval, snapshots);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const float* g,

@@ -59,6 +59,9 @@ struct ChunkItem {
     int64_t t0, t1;
     int32_t sin;   // initial state: >= 0 row of h0, <= -2 row (-sin - 2) of the staged states, -1 zero
     int32_t sout;  // final state (or map slot in map mode): >= 0 row of the output, -1 none
+    int64_t p0;    // tokens of the sequence before t0
+    int32_t snap;  // row of the sequence's first state snapshot, -1 none
+    int32_t pad_;
 };
 
 // Scan over the segment maps of one sequence (all heads).
@@ -221,18 +224,47 @@ __device__ __forceinline__ int value_exponent(float mx, int ex) {
     return e < -120 ? -120 : (e > 120 ? 120 : e);
 }
 
+// State snapshots: the state after every `interval` tokens of a sequence
+// (a multiple of 64, so every snapshot falls on a chunk boundary).  Snapshot j
+// of a sequence holds the state after tokens 0 .. (j + 1) interval - 1.
+struct SnapCursor {
+    int64_t next;  // sequence position of the next snapshot
+    int64_t row;   // its row in the snapshot output
+    __device__ void init(const ChunkItem& it, int interval) {
+        next = (it.p0 / interval + 1) * interval;
+        row = it.snap + it.p0 / interval;
+    }
+};
+
+// Writes the state columns a wave holds (S[rt][ct][i] at row 16 rt + 4 g4 + i,
+// column col + 16 ct + r, scaled by un) to a row-major d_k x d_v fp32 matrix.
+// Buffer stores: one lane offset, the rest in scalar offsets (few registers).
+template <int NCT>
+__device__ __forceinline__ void store_state(float* __restrict__ dst, const f4 (&S)[8][NCT], float un,
+                                            int g4, int r, int col) {
+    const auto rd = rsrc(dst, D * D * 4);
+    int vo = ((4 * g4) * D + col + r) * 4;
+    asm volatile("" : "+v"(vo));  // computed here, not held in a register across the chunk loop
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bstore(rd, vo, ((16 * rt + i) * D + 16 * ct) * 4, S[rt][ct][i] * un, dst);
+}
+
 // NW waves; each owns NCT 16-column tiles of the state; chunks of NSB
 // sub-blocks.  Full mode: state = S (NW * 16 NCT = 128 columns), writes o and
 // the final state.  Map mode: state = [B | M] (256 columns), no o, writes the
 // segment's (B, M).  WPC workgroups share a CU (it sets the register budget).
-template <int NW, int NSB, int NCT, bool MAP, int WPC, typename Tout>
+template <int NW, int NSB, int NCT, bool MAP, int WPC, typename Tout, bool SNAP = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4 * WPC)))
 void chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, const ChunkItem* __restrict__ items, int H,
     const float* __restrict__ h0, const float* __restrict__ staged, Tout* __restrict__ o,
-    float* __restrict__ out_state) {
+    float* __restrict__ out_state, float* __restrict__ snaps, int interval) {
     constexpr int C = 16 * NSB;         // tokens per chunk
     constexpr int NP = NW / NSB;        // channel parts per sub-block
     constexpr int CPG = D / NP;         // channels per gate wave
@@ -328,6 +360,9 @@ void chunk_kernel(
         }
     };
     fetch(t0);
+    const bool snapping = SNAP && !MAP && snaps != nullptr && it.snap >= 0;
+    SnapCursor sc{};
+    if (snapping) sc.init(it, interval);
 
     for (int64_t c0 = t0; c0 < t1; c0 += C) {
         const int valid = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
@@ -724,6 +759,11 @@ void chunk_kernel(
                 }
             }
         }
+        if (snapping && it.p0 + ((c0 + C < t1 ? c0 + C : t1) - t0) == sc.next) {
+            store_state<NCT>(snaps + (sc.row * H + h) * D * D, S, ldexpf(1.f, -ex), g4, r, col);
+            sc.next += interval;
+            ++sc.row;
+        }
     }
 
     // Final state (full mode) or this segment's (B, M) (map mode, rows of 256).
@@ -778,14 +818,14 @@ struct alignas(16) Smem {
 };
 }  // namespace ws
 
-template <typename Tout>
+template <typename Tout, bool SNAP>
 __global__ __launch_bounds__(ws::NW * 64) __attribute__((amdgpu_waves_per_eu(ws::NW / 4)))
 void chunk_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, const ChunkItem* __restrict__ items, int H,
     const float* __restrict__ h0, const float* __restrict__ staged, Tout* __restrict__ o,
-    float* __restrict__ out_state) {
+    float* __restrict__ out_state, float* __restrict__ snaps, int interval) {
     using namespace ws;
     __shared__ ws::Smem sm;
 
@@ -1102,6 +1142,9 @@ void chunk_ws_kernel(
                         s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
                     }
         };
+        const bool snapping = SNAP && snaps != nullptr && it.snap >= 0;
+        SnapCursor sc{};
+        if (snapping) sc.init(it, interval);
         for (int c = -1; c < nch; ++c) {
             const bool swork = c >= 0;        // run chunk c
             const int64_t c0 = t0 + static_cast<int64_t>(c) * C;
@@ -1187,6 +1230,11 @@ void chunk_ws_kernel(
                     const h8 kb8 = *reinterpret_cast<const h8*>(&cur.kbt[16 * rt + r][8 * g4]);
     #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb8, d16[ct], S[rt][ct] * lam);
+                }
+                if (snapping && it.p0 + (c0 + valid - t0) == sc.next) {
+                    store_state<NCT>(snaps + (sc.row * H + h) * D * D, S, ldexpf(1.f, -ex), g4, r, col);
+                    sc.next += interval;
+                    ++sc.row;
                 }
             }
             __syncthreads();
@@ -1294,7 +1342,8 @@ __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
 // dispatcher hands workgroups out in index order, so launching long chains
 // first gives a longest-processing-time schedule.  One item per sequence.
 __global__ void plan_sequences_kernel(const int32_t* __restrict__ cu, int N, int T, int lpt,
-                                      int has_h0, int has_hT, ChunkItem* __restrict__ items) {
+                                      int has_h0, int has_hT, const int32_t* __restrict__ snap_base,
+                                      ChunkItem* __restrict__ items) {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     if (n >= N) return;
     const int64_t a = cu ? cu[n] : static_cast<int64_t>(n) * T;
@@ -1308,7 +1357,7 @@ __global__ void plan_sequences_kernel(const int32_t* __restrict__ cu, int N, int
             rank += (lm > len) || (lm == len && m < n);
         }
     }
-    items[rank] = ChunkItem{a, b, has_h0 ? n : -1, has_hT ? n : -1};
+    items[rank] = ChunkItem{a, b, has_h0 ? n : -1, has_hT ? n : -1, 0, snap_base ? snap_base[n] : -1, 0};
 }
 
 // Segments of every sequence (seg tokens each, the last one shorter), the
@@ -1316,8 +1365,8 @@ __global__ void plan_sequences_kernel(const int32_t* __restrict__ cu, int N, int
 // A single workgroup walks the sequences in blocks of 256 with a block scan.
 __global__ __launch_bounds__(256) void plan_segments_kernel(
     const int32_t* __restrict__ cu, int N, int T, int seg, int has_h0, int has_hT,
-    ChunkItem* __restrict__ seg_items, ChunkItem* __restrict__ map_items,
-    ScanItem* __restrict__ scan_items) {
+    const int32_t* __restrict__ snap_base, ChunkItem* __restrict__ seg_items,
+    ChunkItem* __restrict__ map_items, ScanItem* __restrict__ scan_items) {
     __shared__ int sc[256];
     __shared__ int base;
     if (threadIdx.x == 0) base = 0;
@@ -1348,8 +1397,10 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(
                 const int64_t sb = sa + seg < b ? sa + seg : b;
                 const int sin = -2 - (segs_before + gi);  // staged by the scan
                 const int sout = gi == G - 1 ? (has_hT ? n : -1) : -1;
-                seg_items[segs_before + gi] = ChunkItem{sa, sb, sin, sout};
-                if (gi < G - 1) map_items[maps_before + gi] = ChunkItem{sa, sb, -1, maps_before + gi};
+                seg_items[segs_before + gi] =
+                    ChunkItem{sa, sb, sin, sout, sa - a, snap_base ? snap_base[n] : -1, 0};
+                if (gi < G - 1)
+                    map_items[maps_before + gi] = ChunkItem{sa, sb, -1, maps_before + gi, sa - a, -1, 0};
             }
             scan_items[n] = ScanItem{maps_before, G - 1, has_h0 ? n : -1, segs_before};
         }
@@ -1367,6 +1418,36 @@ constexpr int kLptMaxSeqs = 16384;
 constexpr int kWpc = 1;  // full-mode chains resident per CU (LDS bound)
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Row of every sequence's first snapshot: an exclusive prefix sum of
+// floor(length / interval) over the sequences, one workgroup in blocks of 256.
+__global__ __launch_bounds__(256) void snap_base_kernel(const int32_t* __restrict__ cu, int N, int T,
+                                                        int interval, int32_t* __restrict__ base_out) {
+    __shared__ int sc[256];
+    __shared__ int base;
+    if (threadIdx.x == 0) base = 0;
+    __syncthreads();
+    for (int n0 = 0; n0 < N; n0 += 256) {
+        const int n = n0 + threadIdx.x;
+        int cnt = 0;
+        if (n < N) {
+            const int64_t len = cu ? cu[n + 1] - cu[n] : T;
+            cnt = static_cast<int>(len / interval);
+        }
+        sc[threadIdx.x] = cnt;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
+            const int x = threadIdx.x >= off ? sc[threadIdx.x - off] : 0;
+            __syncthreads();
+            sc[threadIdx.x] += x;
+            __syncthreads();
+        }
+        if (n < N) base_out[n] = base + sc[threadIdx.x] - cnt;
+        __syncthreads();
+        if (threadIdx.x == 255) base += sc[255];
+        __syncthreads();
+    }
+}
 
 // Host mirror of the segment plan (same formula as plan_segments_kernel).
 void count_segments(const int32_t* cu_host, int N, int T, int seg, int64_t* nseg, int64_t* nmap) {
@@ -1406,6 +1487,12 @@ ScanLayout scan_layout(int64_t nseg, int64_t nmap, int N, int H) {
 
 int chunk_chains_per_cu() { return kWpc; }
 
+hipError_t launch_snap_base(const int32_t* cu, int N, int T, int interval, int32_t* out,
+                            hipStream_t stream) {
+    hipLaunchKernelGGL(snap_base_kernel, dim3(1), dim3(256), 0, stream, cu, N, T, interval, out);
+    return hipGetLastError();
+}
+
 int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host) {
     // Long sequences are cut so that four segments (workgroups) per CU of a
     // 256-CU part exist over all heads: a whole number of rounds of resident
@@ -1434,35 +1521,35 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
     char* ws = static_cast<char*>(a.ws);
     auto launch_full = [&](const ChunkItem* items, int64_t nitems, const float* staged) {
         const dim3 grid(static_cast<uint32_t>(nitems * a.H));
+        const auto q = static_cast<const uint16_t*>(a.q);
+        const auto k = static_cast<const uint16_t*>(a.k);
+        const auto v = static_cast<const uint16_t*>(a.v);
+        auto go = [&](auto kernel, int threads, auto* o) {
+            hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, a.stream, q, k, v, a.g, a.beta, a.scale,
+                               items, a.H, a.h0, staged, o, a.hT, a.snaps, a.snap_interval);
+        };
+        bf16_t* ob = static_cast<bf16_t*>(a.o);
+        float* of = static_cast<float*>(a.o);
+        const bool sn = a.snaps != nullptr;
         if (c64) {  // single-role kernel, 64-token chunks
             if (a.out_bf16)
-                hipLaunchKernelGGL((chunk_kernel<8, 4, 1, false, 1, bf16_t>), grid, dim3(8 * 64), 0, a.stream,
-                                   static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                                   static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
-                                   staged, static_cast<bf16_t*>(a.o), a.hT);
+                sn ? go(chunk_kernel<8, 4, 1, false, 1, bf16_t, true>, 8 * 64, ob)
+                   : go(chunk_kernel<8, 4, 1, false, 1, bf16_t, false>, 8 * 64, ob);
             else
-                hipLaunchKernelGGL((chunk_kernel<8, 4, 1, false, 1, float>), grid, dim3(8 * 64), 0, a.stream,
-                                   static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                                   static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
-                                   staged, static_cast<float*>(a.o), a.hT);
+                sn ? go(chunk_kernel<8, 4, 1, false, 1, float, true>, 8 * 64, of)
+                   : go(chunk_kernel<8, 4, 1, false, 1, float, false>, 8 * 64, of);
             return;
         }
         if (a.out_bf16)
-            hipLaunchKernelGGL((chunk_ws_kernel<bf16_t>), grid, dim3(ws::NW * 64), 0, a.stream,
-                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                               static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
-                               staged, static_cast<bf16_t*>(a.o), a.hT);
+            sn ? go(chunk_ws_kernel<bf16_t, true>, ws::NW * 64, ob) : go(chunk_ws_kernel<bf16_t, false>, ws::NW * 64, ob);
         else
-            hipLaunchKernelGGL((chunk_ws_kernel<float>), grid, dim3(ws::NW * 64), 0, a.stream,
-                               static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                               static_cast<const uint16_t*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
-                               staged, static_cast<float*>(a.o), a.hT);
+            sn ? go(chunk_ws_kernel<float, true>, ws::NW * 64, of) : go(chunk_ws_kernel<float, false>, ws::NW * 64, of);
     };
     if (!scan) {
         ChunkItem* items = reinterpret_cast<ChunkItem*>(ws);
         const int lpt = (a.cu && a.N > 1 && a.N <= kLptMaxSeqs) ? 1 : 0;
         hipLaunchKernelGGL(plan_sequences_kernel, dim3((a.N + 255) / 256), dim3(256), 0, a.stream,
-                           a.cu, a.N, a.T, lpt, a.h0 ? 1 : 0, a.hT ? 1 : 0, items);
+                           a.cu, a.N, a.T, lpt, a.h0 ? 1 : 0, a.hT ? 1 : 0, a.snap_base, items);
         launch_full(items, a.N, nullptr);
         return hipGetLastError();
     }
@@ -1476,13 +1563,14 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
     float* maps = reinterpret_cast<float*>(ws + L.maps);
     float* staged = reinterpret_cast<float*>(ws + L.staged);
     hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T, seg,
-                       a.h0 ? 1 : 0, a.hT ? 1 : 0, seg_items, map_items, scan_items);
+                       a.h0 ? 1 : 0, a.hT ? 1 : 0, a.snap_base, seg_items, map_items, scan_items);
     if (nmap > 0)
         hipLaunchKernelGGL((chunk_kernel<8, 2, 2, true, 1, float>), dim3(static_cast<uint32_t>(nmap * a.H)),
                            dim3(8 * 64), 0, a.stream, static_cast<const uint16_t*>(a.q),
                            static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.g,
                            a.beta, a.scale, map_items, a.H, static_cast<const float*>(nullptr),
-                           static_cast<const float*>(nullptr), static_cast<float*>(nullptr), maps);
+                           static_cast<const float*>(nullptr), static_cast<float*>(nullptr), maps,
+                           static_cast<float*>(nullptr), 0);
     hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<uint32_t>(a.N) * a.H), dim3(256), 0,
                        a.stream, scan_items, a.H, a.h0, maps, staged);
     launch_full(seg_items, nseg, staged);

@@ -23,6 +23,9 @@ struct PrefillArgs {
     bool in_bf16, out_bf16;
     void* o;
     float* hT;           // [N, H, dk, dv] or nullptr
+    float* snaps;        // [total snapshots, H, dk, dv] or nullptr
+    int snap_interval;   // tokens between snapshots (multiple of 64) when snaps
+    const int32_t* snap_base;  // device [N]: row of each sequence's first snapshot
     void* ws;
     size_t ws_bytes;
     hipStream_t stream;
@@ -73,7 +76,9 @@ hipError_t launch_steps(const DecodeArgs& a);
 // Chunked MFMA prefill (bf16 inputs, d_k = d_v = 128).  With scan = true long
 // sequences are cut into segments whose (B, M) maps are composed by a scan.
 // cu_host may be null (then the N sequences are rows of length T).
-int chunk_chains_per_cu();  // full-mode chunk workgroups resident per CU
+int chunk_chains_per_cu();
+hipError_t launch_snap_base(const int32_t* cu, int N, int T, int interval, int32_t* out,
+                            hipStream_t stream);  // full-mode chunk workgroups resident per CU
 int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host);
 size_t chunk_workspace_bytes(int B, int T, int H, int N, const int32_t* cu_host, bool scan);
 // scan: segment-scan path; c64: single-role kernel on 64-token chunks.

@@ -19,7 +19,8 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float scale,
     const float* __restrict__ h0, const int32_t* __restrict__ cu, int T, int H,
-    Tout* __restrict__ o, float* __restrict__ hT) {
+    Tout* __restrict__ o, float* __restrict__ hT, float* __restrict__ snaps, int interval,
+    const int32_t* __restrict__ snap_base) {
     constexpr int R = DK / 8;  // rows per lane
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -57,6 +58,7 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(
         nb = beta[t * H + h];
     };
     if (t0 < t1) fetch(t0);
+    int64_t next_snap = interval, snap_row = snaps ? snap_base[n] : 0;
     for (int64_t t = t0; t < t1; ++t) {
         float kk[R], qq[R], gg[R];
 #pragma unroll
@@ -87,6 +89,13 @@ __global__ __launch_bounds__(64 * WAVES) void recurrent_kernel(
         r += __shfl_xor(r, 16);
         r += __shfl_xor(r, 32);
         if (rg == 0) st(o, (t * H + h) * DV + j, scale * r);
+        if (snaps && t + 1 - t0 == next_snap) {  // state after `interval` more tokens
+            float* dst = snaps + (snap_row * H + h) * DK * DV;
+#pragma unroll
+            for (int i = 0; i < R; ++i) dst[static_cast<int64_t>(rg * R + i) * DV + j] = s[i];
+            next_snap += interval;
+            ++snap_row;
+        }
     }
     if (hT) {
 #pragma unroll
@@ -101,7 +110,7 @@ static hipError_t launch_recurrent_t(const PrefillArgs& a) {
     hipLaunchKernelGGL((recurrent_kernel<DK, DV, WAVES, Tin, Tout>), grid, dim3(64 * WAVES), 0,
                        a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                        static_cast<const Tin*>(a.v), a.g, a.beta, a.scale, a.h0, a.cu, a.T, a.H,
-                       static_cast<Tout*>(a.o), a.hT);
+                       static_cast<Tout*>(a.o), a.hT, a.snaps, a.snap_interval, a.snap_base);
     return hipGetLastError();
 }
 

@@ -139,6 +139,43 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          void* workspace, size_t workspace_bytes, kda_variant variant,
                          void* stream);
 
+/* Bytes of device workspace kda_chunk_fwd_snapshots needs (the same
+ * arguments as kda_chunk_fwd_workspace_size plus the snapshot interval);
+ * 0 for arguments it would reject. */
+size_t kda_chunk_fwd_snapshots_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k,
+                                              int32_t d_v, int32_t N,
+                                              const int32_t* cu_seqlens_host, kda_dtype in_dtype,
+                                              kda_variant variant, int32_t snap_interval);
+
+/* kda_chunk_fwd that also writes the state of every sequence after each
+ * `snap_interval` tokens: states kept at prefix boundaries so that a later
+ * request sharing the prefix can resume from them (the concept page "Kimi
+ * Delta Attention (KDA)", section "KV Caching Challenges & vLLM
+ * Contribution": a KDA-aware prefix cache keeps the recurrent state at
+ * prefix boundaries rather than keys and values).  Resuming is a call with
+ * the snapshot as initial_state on the remaining tokens.
+ *
+ *  snap_interval  tokens between snapshots, a positive multiple of 64 (other
+ *              values: KDA_ERR_SHAPE if <= 0, else KDA_ERR_UNSUPPORTED).
+ *  snapshots   [total, H, d_k, d_v] fp32, where sequence n of length L_n
+ *              contributes floor(L_n / snap_interval) snapshots, stored in
+ *              sequence order and, within a sequence, in position order:
+ *              snapshot j of sequence n is row sum_{m<n} floor(L_m /
+ *              snap_interval) + j and holds the state after tokens
+ *              0 .. (j + 1) snap_interval - 1 of that sequence.  May be NULL
+ *              when total is 0; must not overlap any other argument.
+ *  workspace   at least kda_chunk_fwd_snapshots_workspace_size() bytes.
+ * Every other argument, the outputs o and final_state, and all error
+ * behaviour are those of kda_chunk_fwd. */
+kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, float scale, const float* initial_state,
+                                   const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                   int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                   int32_t N, kda_dtype in_dtype, kda_dtype out_dtype, void* o,
+                                   float* final_state, int32_t snap_interval, float* snapshots,
+                                   void* workspace, size_t workspace_bytes, kda_variant variant,
+                                   void* stream);
+
 /* One token for each of N independent sequences, state updated in place
  * ("Understanding Kimi Delta Attention", section "Two execution modes":
  * the fused recurrent step with constant memory; the recurrence of section

@@ -98,3 +98,36 @@ def kda_fused_recurrent(q, k, v, g, beta, scale, state, dtype=np.float64):
     above with the rows as sequences (the fused recurrent mode of the first
     page run over several tokens)."""
     return kda_forward(q, k, v, g, beta, scale, state, None, dtype)
+
+
+def kda_forward_snapshots(q, k, v, g, beta, scale, interval, initial_state=None,
+                          cu_seqlens=None, dtype=np.float64):
+    """kda_forward that also keeps the state of every chain after each
+    `interval` tokens: states at prefix boundaries, as a KDA-aware prefix
+    cache stores them (concept page "Kimi Delta Attention (KDA)", section
+    "KV Caching Challenges & vLLM Contribution").
+
+    Returns (o, final, snaps): snaps [total, H, dk, dv] holds, chain by chain
+    in order and within a chain by position, the state after tokens
+    0 .. (j + 1) interval - 1 of the chain for j = 0 .. floor(len / interval) - 1.
+    """
+    q, k, v, g, beta = (_np(x, dtype) for x in (q, k, v, g, beta))
+    h0 = _np(initial_state, dtype)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    chains = chain_list(B, T, cu_seqlens)
+    o = np.zeros((B, T, H, dv), dtype=dtype)
+    final = np.zeros((len(chains), H, dk, dv), dtype=dtype)
+    snaps = []
+    for n, (b, t0, t1) in enumerate(chains):
+        S = np.zeros((H, dk, dv), dtype=dtype) if h0 is None else h0[n].copy()
+        for t in range(t0, t1):
+            S = np.exp(g[b, t])[:, :, None] * S
+            u = beta[b, t][:, None] * (v[b, t] - np.einsum("hkv,hk->hv", S, k[b, t]))
+            S = S + k[b, t][:, :, None] * u[:, None, :]
+            o[b, t] = scale * np.einsum("hkv,hk->hv", S, q[b, t])
+            if (t + 1 - t0) % interval == 0:   # a prefix boundary
+                snaps.append(S.copy())
+        final[n] = S
+    snaps = np.stack(snaps) if snaps else np.zeros((0, H, dk, dv), dtype=dtype)
+    return o, final, snaps

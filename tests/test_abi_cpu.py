@@ -169,3 +169,32 @@ def test_fused_recurrent_validation():
     assert steps(o=addr(0, 64)) == ALIAS
     assert steps(state=addr(6, 4 * 5 * 2 * 16 * 4 - 16)) == ALIAS   # state starts inside o
     assert steps(T=0) == OK and steps(N=0) == OK                      # no-ops
+
+
+def chunk_snap(interval=64, snaps=None, T=128, B=1, N=1, H=2, dk=16, dv=16, o=None, fin=None,
+               ws=None, ws_bytes=0, variant=1):
+    snaps = addr(9) if snaps is None else snaps
+    o = addr(5) if o is None else o
+    return kda.lib.kda_chunk_fwd_snapshots(addr(0), addr(1), addr(2), addr(3), addr(4), 0.25, None,
+                                           None, None, B, T, H, dk, dv, N, F32, F32, o, fin,
+                                           interval, snaps, ws, ws_bytes, variant, None)
+
+
+def test_snapshot_validation():
+    assert chunk_snap(interval=0) == SHAPE
+    assert chunk_snap(interval=-64) == SHAPE
+    assert chunk_snap(interval=96) == UNSUP            # not a multiple of 64
+    assert chunk_snap(snaps=P(0)) == NULL              # two snapshots requested, no buffer
+    assert chunk_snap(snaps=addr(9, 4)) == ALIGN
+    assert chunk_snap(snaps=addr(0, 256), ws=addr(10), ws_bytes=4096) == ALIAS    # over q
+    assert chunk_snap(snaps=addr(5, 1024), ws=addr(10), ws_bytes=4096) == ALIAS   # over o
+    assert chunk_snap(snaps=addr(10, 512), ws=addr(10), ws_bytes=4096) == ALIAS   # over the workspace
+    # the recurrent variant needs no workspace of its own; snapshots need the row table
+    assert chunk_snap() == WS
+    wsz = kda.lib.kda_chunk_fwd_snapshots_workspace_size
+    assert wsz(1, 128, 2, 16, 16, 1, None, F32, 1, 64) == 256
+    assert wsz(1, 63, 2, 16, 16, 1, None, F32, 1, 64) == 0      # shorter than the interval
+    assert wsz(1, 128, 2, 16, 16, 1, None, F32, 1, 100) == 0    # rejected interval
+    keep, cu = host_cu([0, 100000, 100100])
+    plain = kda.lib.kda_chunk_fwd_workspace_size(1, 100100, 4, 128, 128, 2, cu, BF16, 3)
+    assert wsz(1, 100100, 4, 128, 128, 2, cu, BF16, 3, 4096) == ((plain + 255) // 256) * 256 + 256

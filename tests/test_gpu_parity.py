@@ -208,6 +208,78 @@ def test_fused_recurrent_empty_and_rejects_long_runs():
         kda.fused_recurrent_fwd(x, x, x, x, torch.zeros(2, 65, 1, device=dev), 1.0, st)
 
 
+@pytest.mark.parametrize("variant,interval", [("chunk", 64), ("chunk", 192), ("chunk64", 128),
+                                              ("recurrent", 64), ("chunk_scan", 256)])
+def test_snapshots_varlen(variant, interval):
+    say(f"snapshots variant={variant} interval={interval} (ragged varlen, H=2)")
+    lens = [1, 63, 64, 65, 200, 384, 700, 1030] if variant != "chunk_scan" else [64, 2500, 4096, 130]
+    x = synth.make_inputs("varlen", lens=lens, H=2)
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    kda = _kda()
+    o, f, sn = kda.chunk_fwd_snapshots(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, interval,
+                                       initial_state=xd.h0, cu_seqlens=x.cu_seqlens, variant=variant)
+    o2, f2 = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, xd.h0, x.cu_seqlens,
+                           variant=variant)
+    torch.cuda.synchronize()
+    # the snapshot instantiation does the same arithmetic as the plain one
+    assert torch.equal(o, o2) and torch.equal(f, f2)
+    o_ref, f_ref, s_ref = ref.kda_forward_snapshots(x.q, x.k, x.v, x.g, x.beta, x.scale, interval,
+                                                    x.h0, x.cu_seqlens)
+    assert tuple(sn.shape) == s_ref.shape and s_ref.shape[0] == sum(L // interval for L in lens)
+    rows = kda.snapshot_rows(lens, interval)
+    for n, L in enumerate(lens):  # per sequence, so an error names its rows
+        a, b = rows[n], rows[n + 1]
+        if b > a:
+            assert_parity(sn[a:b], s_ref[a:b], x.q.dtype, f"snapshots of sequence {n}")
+    assert_parity(f, f_ref, x.q.dtype, "final")
+
+
+def test_snapshot_resume_equals_full_run():
+    say("resume from a snapshot == the uninterrupted run (prefix caching), T=1500 H=4")
+    x = synth.make_inputs("prefill", T=1500, H=4)
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    kda = _kda()
+    o, f, sn = kda.chunk_fwd_snapshots(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, 512,
+                                       initial_state=xd.h0)
+    assert sn.shape[0] == 2
+    p = 1024  # resume after the second snapshot
+    sl = lambda t: t[:, p:].contiguous()
+    o_r, f_r = kda.chunk_fwd(sl(xd.q), sl(xd.k), sl(xd.v), sl(xd.g), sl(xd.beta), x.scale,
+                             sn[1:2].contiguous())
+    torch.cuda.synchronize()
+    assert rel_rms(o_r, o[:, p:]) <= 2e-2 and rel_rms(f_r, f) <= 2e-2
+
+
+def test_snapshots_varlen_workload_full_size_sampled():
+    say("snapshots on the varlen workload (262144 tokens, H=32), interval 4096, sampled chains")
+    x = synth.make_inputs("varlen")
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    kda = _kda()
+    lens = np.diff(x.cu_seqlens)
+    o, f, sn = kda.chunk_fwd_snapshots(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, 4096,
+                                       initial_state=xd.h0, cu_seqlens=x.cu_seqlens)
+    o2, f2 = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, xd.h0, x.cu_seqlens)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(f, f2)
+    rows = kda.snapshot_rows(lens, 4096)
+    assert sn.shape[0] == rows[-1]
+    longest = int(np.argmax(lens))
+    # the snapshot after p tokens is the final state of the oracle run on the first p tokens
+    for n, j in ((longest, 0), (longest, int(lens[longest] // 4096) - 1), (int(np.argmax(lens >= 8192)), 1)):
+        p = (j + 1) * 4096
+        a = int(x.cu_seqlens[n])
+        sl = slice(a, a + p)
+        heads = [0, 17, 31]
+        _, fr = cref.kda_forward(x.q[:, sl, heads], x.k[:, sl, heads], x.v[:, sl, heads],
+                                 x.g[:, sl, heads], x.beta[:, sl, heads], x.scale,
+                                 x.h0[n:n + 1, heads], None, n_threads=THREADS)
+        say(f"  sequence {n} snapshot {j} (after {p} tokens), heads {heads}")
+        assert_parity(sn[rows[n] + j][heads], fr[0], x.q.dtype, f"snapshot {j} of sequence {n}")
+
+
 def test_prefill_then_decode_equals_prefill():
     say("prefill T-1 then decode == prefill T (H=4, T=300)")
     x = synth.make_inputs("prefill", T=300, H=4)

@@ -215,3 +215,33 @@ def test_fused_recurrent_is_successive_decode_steps():
     # each row from its own state: row 1 alone gives the same result
     o1, f1 = ref.kda_fused_recurrent(q[1:2], k[1:2], v[1:2], g[1:2], beta[1:2], 0.5, s0[1:2])
     assert np.max(np.abs(o1[0] - o[1])) < 1e-13 and np.max(np.abs(f1[0] - f[1])) < 1e-13
+
+
+def test_snapshots_are_prefix_final_states():
+    """Snapshot j of a chain is the final state of the recurrence run on the
+    chain's first (j + 1) * interval tokens; rows run chain by chain; o and the
+    final states are those of kda_forward."""
+    rng = np.random.default_rng(10)
+    lens = [13, 8, 0, 20, 4]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, H, dk, dv, iv = int(cu[-1]), 2, 5, 3, 4
+    q, k, v = (rng.standard_normal((1, T, H, d)) for d in (dk, dk, dv))
+    g = -rng.random((1, T, H, dk))
+    beta = rng.random((1, T, H))
+    h0 = rng.standard_normal((len(lens), H, dk, dv))
+    o, f, sn = ref.kda_forward_snapshots(q, k, v, g, beta, 0.5, iv, h0, cu)
+    o2, f2 = ref.kda_forward(q, k, v, g, beta, 0.5, h0, cu)
+    assert np.array_equal(o, o2) and np.array_equal(f, f2)
+    assert sn.shape[0] == sum(L // iv for L in lens)
+    row = 0
+    for n, L in enumerate(lens):
+        a = cu[n]
+        for j in range(L // iv):
+            p = (j + 1) * iv
+            sl = slice(a, a + p)
+            _, fp = ref.kda_forward(q[:, sl], k[:, sl], v[:, sl], g[:, sl], beta[:, sl], 0.5,
+                                    h0[n:n + 1])
+            assert np.max(np.abs(sn[row] - fp[0])) < 1e-13, (n, j)
+            row += 1
+    # a chain whose length is a multiple of the interval ends on a snapshot
+    assert np.max(np.abs(sn[sum(L // iv for L in lens[:2]) - 1] - f[1])) < 1e-13
