@@ -313,6 +313,20 @@ def main():
                 variant=args.variant),
                 stream, 5)
             sb = alg_b + nsn * H * dk * dv * 4
+            # The same prefill with the output gate and RMSNorm applied in the o store
+            # (kda_chunk_fwd_gated): reads a bf16 gate per token and head besides.
+            gen = torch.Generator(device=dev).manual_seed(12)
+            ogt = torch.sigmoid(torch.randn(x.v.shape, generator=gen, device=dev)).to(x.q.dtype)
+            nw = 1.0 + 0.1 * torch.randn(dv, generator=gen, device=dev)
+            gm = time_launches(lambda: kda.chunk_fwd(
+                x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0, cu_dev, o=o, final_state=fin,
+                workspace=ws, variant=args.variant, cu_seqlens_host=cu_host, out_gate=ogt,
+                norm_weight=nw, norm_eps=1e-6), stream, 5)
+            gb = alg_b + tokens * H * dv * x.q.element_size()
+            line["extras"]["gated_rmsnorm"] = {
+                "ms_per_launch": gm, "plain_ms": pre_avg, "overhead": gm / pre_avg - 1.0,
+                "gbs": gb / (gm * 1e-3) / 1e9, "frac": gb / (gm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "alg_bytes": gb, "config": f"{args.workload} prefill, o = gate * RMSNorm(o) in the store"}
             line["extras"]["snapshots"] = {
                 "ms_per_launch": sm, "plain_ms": pre_avg, "overhead": sm / pre_avg - 1.0,
                 "snapshots": nsn, "gbs": sb / (sm * 1e-3) / 1e9,

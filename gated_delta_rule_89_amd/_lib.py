@@ -24,7 +24,8 @@ F32, BF16 = 0, 1
 VARIANTS = {"auto": 0, "recurrent": 1, "chunk": 2, "chunk_scan": 3, "chunk64": 4}
 EXPORTS = ("kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd", "kda_decode_step", "kda_fused_recurrent_fwd",
-           "kda_chunk_fwd_snapshots_workspace_size", "kda_chunk_fwd_snapshots")
+           "kda_chunk_fwd_snapshots_workspace_size", "kda_chunk_fwd_snapshots",
+           "kda_chunk_fwd_gated")
 FUSED_RECURRENT_MAX_T = 64
 
 
@@ -60,6 +61,10 @@ def _load() -> ctypes.CDLL:
                                             I32, I32, I32, I32, I32, I32, ctypes.c_int, ctypes.c_int,
                                             P, P, I32, P, P, SZ, ctypes.c_int, P]
     lib.kda_chunk_fwd_snapshots.restype = ctypes.c_int
+    lib.kda_chunk_fwd_gated.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P,
+                                        I32, I32, I32, I32, I32, I32, ctypes.c_int, ctypes.c_int,
+                                        P, P, ctypes.c_float, P, P, P, SZ, ctypes.c_int, P]
+    lib.kda_chunk_fwd_gated.restype = ctypes.c_int
     return lib
 
 
@@ -142,14 +147,18 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               workspace: Optional[torch.Tensor] = None,
               cu_seqlens_host: Optional[torch.Tensor] = None,
               snapshot_interval: Optional[int] = None,
-              snapshots: Optional[torch.Tensor] = None):
+              snapshots: Optional[torch.Tensor] = None,
+              out_gate: Optional[torch.Tensor] = None,
+              norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6):
     """kda_chunk_fwd on torch tensors.  q, k, g: [B, T, H, dk]; v: [B, T, H, dv];
     beta: [B, T, H]; initial_state [N, H, dk, dv] fp32 or None; cu_seqlens int32
     [N+1] (device tensor, CPU tensor, numpy array or list) or None.  A caller
     holding both copies passes the device tensor as cu_seqlens and an int32 CPU
     tensor as cu_seqlens_host, and no copy is made.
     Returns (o [B, T, H, dv], final_state [N, H, dk, dv] or None), and with
-    snapshot_interval also the snapshots (kda_chunk_fwd_snapshots)."""
+    snapshot_interval also the snapshots (kda_chunk_fwd_snapshots).  With
+    out_gate [B, T, H, dv] (q's dtype) and norm_weight [dv] fp32, o is the gated
+    RMSNorm of the read-out (kda_chunk_fwd_gated)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
         _dev(t, name)
     B, T, H, dk = q.shape
@@ -202,6 +211,18 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     ws_bytes = workspace_size(B, T, H, dk, dv, N, q.dtype, variant, cu_host)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if out_gate is not None:
+        _dev(out_gate, "out_gate")
+        _dev(norm_weight, "norm_weight")
+        code = lib.kda_chunk_fwd_gated(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
+            _ptr(cu_dev), None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr()),
+            B, T, H, dk, dv, N, _dt(q.dtype), _dt(o.dtype), _ptr(out_gate), _ptr(norm_weight),
+            float(norm_eps), _ptr(o), _ptr(final_state), _ptr(workspace),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            VARIANTS[variant], _stream(dev))
+        _check(code)
+        return o, final_state
     code = lib.kda_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
         _ptr(cu_dev), None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr()),

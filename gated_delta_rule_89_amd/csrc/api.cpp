@@ -135,8 +135,11 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
                           int32_t T, int32_t H, int32_t d_k, int32_t d_v, int32_t N,
                           kda_dtype in_dtype, kda_dtype out_dtype, void* o, float* final_state,
                           void* workspace, size_t workspace_bytes, kda_variant variant,
-                          void* stream, bool snap_mode, int32_t snap_interval, float* snapshots) {
+                          void* stream, bool snap_mode, int32_t snap_interval, float* snapshots,
+                          bool gated = false, const void* out_gate = nullptr,
+                          const float* norm_weight = nullptr, float norm_eps = 0.f) {
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_DTYPE;
+    if (gated && !(norm_eps >= 0.f && norm_eps < 3.0e38f)) return KDA_ERR_SHAPE;  // also NaN
     if (snap_mode && snap_interval <= 0) return KDA_ERR_SHAPE;
     if (snap_mode && snap_interval % 64 != 0) return KDA_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || H < 0 || N < 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_SHAPE;
@@ -165,6 +168,8 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         return KDA_OK;
     }
     if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_NULL;
+    if (gated && (!out_gate || !norm_weight)) return KDA_ERR_NULL;
+    if (gated && (!aligned(out_gate, 16) || !aligned(norm_weight, 16))) return KDA_ERR_ALIGN;
     if (static_cast<int64_t>(N) * H * 8 > INT32_MAX || H > 65535) return KDA_ERR_SHAPE;
 
     const kda_variant var = resolve_variant(variant, B, T, H, d_k, d_v, N, in_dtype, cu_seqlens_host);
@@ -203,6 +208,12 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         if (!same_state && overlap(f_r, r)) return KDA_ERR_ALIAS;
     }
     if (overlap(o_r, f_r) || overlap(o_r, w_r) || overlap(f_r, w_r)) return KDA_ERR_ALIAS;
+    if (gated) {
+        const Range g_r = range(out_gate, th * d_v * esize(in_dtype));
+        const Range nw_r = range(norm_weight, static_cast<size_t>(d_v) * 4);
+        for (const Range& r : {g_r, nw_r})
+            if (overlap(o_r, r) || overlap(f_r, r) || overlap(w_r, r)) return KDA_ERR_ALIAS;
+    }
     if (nsnap > 0) {
         const Range s_r = range(snapshots, static_cast<size_t>(nsnap) * H * d_k * d_v * 4);
         for (const Range& r : in_r)
@@ -242,6 +253,12 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
             return KDA_ERR_HIP;
     }
 
+    if (gated) {
+        a.ogate = out_gate;
+        a.nweight = norm_weight;
+        a.neps = norm_eps;
+    }
+
     hipError_t e = hipErrorInvalidValue;
     switch (var) {
         case KDA_VARIANT_RECURRENT: e = kda::launch_recurrent(a); break;
@@ -250,6 +267,10 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         case KDA_VARIANT_CHUNK64: e = kda::launch_chunk(a, false, true); break;
         default: return KDA_ERR_UNSUPPORTED;
     }
+    // The 12-wave kernel (CHUNK, CHUNK_SCAN) fuses the gated RMSNorm into its o
+    // store; the other variants write o and the epilogue rewrites it in place.
+    if (e == hipSuccess && gated && (var == KDA_VARIANT_RECURRENT || var == KDA_VARIANT_CHUNK64))
+        e = kda::launch_gate_norm(a);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -283,6 +304,20 @@ size_t kda_chunk_fwd_snapshots_workspace_size(int32_t B, int32_t T, int32_t H, i
     if (static_cast<int64_t>(B) * T == 0 || snapshot_count(cu_seqlens_host, N, T, snap_interval) == 0)
         return plain;
     return align256_(plain) + align256_(static_cast<size_t>(N) * 4);
+}
+
+kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, float scale, const float* initial_state,
+                               const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                               int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                               int32_t N, kda_dtype in_dtype, kda_dtype out_dtype,
+                               const void* out_gate, const float* norm_weight, float norm_eps,
+                               void* o, float* final_state, void* workspace,
+                               size_t workspace_bytes, kda_variant variant, void* stream) {
+    return chunk_fwd_impl(q, k, v, g, beta, scale, initial_state, cu_seqlens, cu_seqlens_host, B, T,
+                          H, d_k, d_v, N, in_dtype, out_dtype, o, final_state, workspace,
+                          workspace_bytes, variant, stream, false, 0, nullptr, true, out_gate,
+                          norm_weight, norm_eps);
 }
 
 kda_status kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const float* g,

@@ -198,6 +198,21 @@ __device__ __forceinline__ float bload4(__amdgpu_buffer_rsrc_t r, int voff) {
 __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x, float*) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
 }
+// 8 consecutive outputs of one lane as 16-byte buffer stores (two for fp32).
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, int voff, const float* y, float*) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u4{__float_as_uint(y[4 * j]), __float_as_uint(y[4 * j + 1]), __float_as_uint(y[4 * j + 2]),
+               __float_as_uint(y[4 * j + 3])}, r, voff + 16 * j, 0, 0);
+}
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, int voff, const float* y, bf16_t*) {
+    u4 p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        p[e] = static_cast<uint32_t>(f32_to_bf16(y[2 * e])) | (static_cast<uint32_t>(f32_to_bf16(y[2 * e + 1])) << 16);
+    __builtin_amdgcn_raw_buffer_store_b128(p, r, voff, 0, 0);
+}
 __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x, bf16_t*) {
     __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, voff, soff, 0);
 }
@@ -810,6 +825,8 @@ struct alignas(16) Tiles {               // operands of one chunk's state pass
 };
 struct alignas(16) Smem {
     Tiles tl[2];
+    float otile[C][D + 4];               // o of the chunk, for the gated RMSNorm epilogue
+    float nw[D];                         // RMSNorm weight
     _Float16 rbs[SB][QP];                // k exp(tot_0 - G), sub-block 0 [token][channel]
     float gp[NP][2 * NSB + 2 * NX][SB][GP];
     float a[NSB][SB][20];                // A_JJ = Diag(beta) G_JJ, strictly lower, by row
@@ -818,14 +835,15 @@ struct alignas(16) Smem {
 };
 }  // namespace ws
 
-template <typename Tout, bool SNAP>
+template <typename Tout, bool SNAP, bool GATED>
 __global__ __launch_bounds__(ws::NW * 64) __attribute__((amdgpu_waves_per_eu(ws::NW / 4)))
 void chunk_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, const ChunkItem* __restrict__ items, int H,
     const float* __restrict__ h0, const float* __restrict__ staged, Tout* __restrict__ o,
-    float* __restrict__ out_state, float* __restrict__ snaps, int interval) {
+    float* __restrict__ out_state, float* __restrict__ snaps, int interval,
+    const uint16_t* __restrict__ ogate, const float* __restrict__ nweight, float neps) {
     using namespace ws;
     __shared__ ws::Smem sm;
 
@@ -1145,6 +1163,15 @@ void chunk_ws_kernel(
         const bool snapping = SNAP && snaps != nullptr && it.snap >= 0;
         SnapCursor sc{};
         if (snapping) sc.init(it, interval);
+        if (GATED && tid < D) sm.nw[tid] = nweight[tid];  // read after several barriers
+        // Gated epilogue: this wave normalises tokens 8 w .. 8 w + 7 of the chunk;
+        // lane l takes token 8 w + l / 8, channels 16 (l % 8) .. 16 (l % 8) + 15.
+        // The indices are rebuilt where used instead of held across the loop.
+        auto epi_lane = [&]() {
+            int x = l;
+            asm volatile("" : "+v"(x));
+            return x;
+        };
         for (int c = -1; c < nch; ++c) {
             const bool swork = c >= 0;        // run chunk c
             const int64_t c0 = t0 + static_cast<int64_t>(c) * C;
@@ -1209,7 +1236,10 @@ void chunk_ws_kernel(
     #pragma unroll
                         for (int ks = 0; ks < 4; ++ks) a = mfma16(qf8[ks], s16[ks][ct], a);
                         const int voc = vo + static_cast<int>(16 * ct * sizeof(Tout));
-                        if (valid == C) {
+                        if (GATED) {
+    #pragma unroll
+                            for (int i = 0; i < 4; ++i) sm.otile[16 * rt + 4 * g4 + i][col + 16 * ct + r] = a[i] * os;
+                        } else if (valid == C) {
     #pragma unroll
                             for (int i = 0; i < 4; ++i)
                                 bstore(ro, voc, static_cast<int>((16 * rt + i) * rowe * sizeof(Tout)), a[i] * os, o);
@@ -1224,12 +1254,50 @@ void chunk_ws_kernel(
             }
             __syncthreads();
             if (swork) {
+                u4 gv[2];  // output gate of this lane's epilogue row (its latency overlaps the S update)
+                if (GATED) {
+                    const int el = epi_lane(), erow = 8 * (w & 3) + (el >> 3), ecol = 16 * (el & 7);
+                    const auto rg = rsrc(ogate + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * 2);
+                    gv[0] = bload16(rg, (erow * rowe + ecol) * 2);
+                    gv[1] = bload16(rg, (erow * rowe + ecol) * 2 + 16);
+                }
     #pragma unroll
                 for (int rt = 0; rt < 8; ++rt) {
                     const f4 lam = *reinterpret_cast<const f4*>(&cur.lam[16 * rt + 4 * g4]);
                     const h8 kb8 = *reinterpret_cast<const h8*>(&cur.kbt[16 * rt + r][8 * g4]);
     #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb8, d16[ct], S[rt][ct] * lam);
+                }
+                if (GATED) {
+                    // y = gate * w * o / sqrt(mean(o^2) + eps) over the token's d_v channels;
+                    // two passes over the LDS row keep few values live.
+                    const int el = epi_lane(), erow = 8 * (w & 3) + (el >> 3), ecol = 16 * (el & 7);
+                    float ss = 0.f;
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const f4 x = *reinterpret_cast<const f4*>(&sm.otile[erow][ecol + 4 * j]);
+                        ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+                    }
+                    ss += __shfl_xor(ss, 1);
+                    ss += __shfl_xor(ss, 2);
+                    ss += __shfl_xor(ss, 4);
+                    const float rinv = __builtin_amdgcn_rsqf(ss * (1.f / D) + neps);
+                    const auto ro = rsrc(o + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * sizeof(Tout));
+                    const int vo = (erow * rowe + ecol) * static_cast<int>(sizeof(Tout));
+    #pragma unroll
+                    for (int j2 = 0; j2 < 2; ++j2) {  // 8 channels per step
+                        float gf[8], yv[8];
+                        unpack_bf16x8(gv[j2], gf);
+    #pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            const int c4 = ecol + 8 * j2 + 4 * jj;
+                            const f4 x = *reinterpret_cast<const f4*>(&sm.otile[erow][c4]);
+                            const f4 wv = *reinterpret_cast<const f4*>(&sm.nw[c4]);
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) yv[4 * jj + e] = x[e] * rinv * wv[e] * gf[4 * jj + e];
+                        }
+                        store8(ro, vo + 8 * j2 * static_cast<int>(sizeof(Tout)), yv, o);
+                    }
                 }
                 if (snapping && it.p0 + (c0 + valid - t0) == sc.next) {
                     store_state<NCT>(snaps + (sc.row * H + h) * D * D, S, ldexpf(1.f, -ex), g4, r, col);
@@ -1524,26 +1592,37 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
         const auto q = static_cast<const uint16_t*>(a.q);
         const auto k = static_cast<const uint16_t*>(a.k);
         const auto v = static_cast<const uint16_t*>(a.v);
-        auto go = [&](auto kernel, int threads, auto* o) {
-            hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, a.stream, q, k, v, a.g, a.beta, a.scale,
-                               items, a.H, a.h0, staged, o, a.hT, a.snaps, a.snap_interval);
-        };
         bf16_t* ob = static_cast<bf16_t*>(a.o);
         float* of = static_cast<float*>(a.o);
         const bool sn = a.snaps != nullptr;
-        if (c64) {  // single-role kernel, 64-token chunks
+        if (c64) {  // single-role kernel, 64-token chunks (a gated output is applied afterwards)
+            auto go = [&](auto kernel, auto* o) {
+                hipLaunchKernelGGL(kernel, grid, dim3(8 * 64), 0, a.stream, q, k, v, a.g, a.beta, a.scale,
+                                   items, a.H, a.h0, staged, o, a.hT, a.snaps, a.snap_interval);
+            };
             if (a.out_bf16)
-                sn ? go(chunk_kernel<8, 4, 1, false, 1, bf16_t, true>, 8 * 64, ob)
-                   : go(chunk_kernel<8, 4, 1, false, 1, bf16_t, false>, 8 * 64, ob);
+                sn ? go(chunk_kernel<8, 4, 1, false, 1, bf16_t, true>, ob)
+                   : go(chunk_kernel<8, 4, 1, false, 1, bf16_t, false>, ob);
             else
-                sn ? go(chunk_kernel<8, 4, 1, false, 1, float, true>, 8 * 64, of)
-                   : go(chunk_kernel<8, 4, 1, false, 1, float, false>, 8 * 64, of);
+                sn ? go(chunk_kernel<8, 4, 1, false, 1, float, true>, of)
+                   : go(chunk_kernel<8, 4, 1, false, 1, float, false>, of);
             return;
         }
-        if (a.out_bf16)
-            sn ? go(chunk_ws_kernel<bf16_t, true>, ws::NW * 64, ob) : go(chunk_ws_kernel<bf16_t, false>, ws::NW * 64, ob);
-        else
-            sn ? go(chunk_ws_kernel<float, true>, ws::NW * 64, of) : go(chunk_ws_kernel<float, false>, ws::NW * 64, of);
+        auto go = [&](auto kernel, auto* o) {
+            hipLaunchKernelGGL(kernel, grid, dim3(ws::NW * 64), 0, a.stream, q, k, v, a.g, a.beta, a.scale,
+                               items, a.H, a.h0, staged, o, a.hT, a.snaps, a.snap_interval,
+                               static_cast<const uint16_t*>(a.ogate), a.nweight, a.neps);
+        };
+        const bool gt = a.ogate != nullptr;
+        if (a.out_bf16) {
+            if (gt) go(chunk_ws_kernel<bf16_t, false, true>, ob);
+            else if (sn) go(chunk_ws_kernel<bf16_t, true, false>, ob);
+            else go(chunk_ws_kernel<bf16_t, false, false>, ob);
+        } else {
+            if (gt) go(chunk_ws_kernel<float, false, true>, of);
+            else if (sn) go(chunk_ws_kernel<float, true, false>, of);
+            else go(chunk_ws_kernel<float, false, false>, of);
+        }
     };
     if (!scan) {
         ChunkItem* items = reinterpret_cast<ChunkItem*>(ws);

@@ -26,6 +26,9 @@ struct PrefillArgs {
     float* snaps;        // [total snapshots, H, dk, dv] or nullptr
     int snap_interval;   // tokens between snapshots (multiple of 64) when snaps
     const int32_t* snap_base;  // device [N]: row of each sequence's first snapshot
+    const void* ogate;   // [B, T, H, dv] in_dtype output gate, or nullptr (plain o)
+    const float* nweight;  // [dv] RMSNorm weight (with ogate)
+    float neps;          // RMSNorm eps (with ogate)
     void* ws;
     size_t ws_bytes;
     hipStream_t stream;
@@ -72,6 +75,8 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStrea
 hipError_t launch_recurrent(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_steps(const DecodeArgs& a);
+// o <- gate * w * o / sqrt(mean(o^2) + eps) over d_v, in place, for every (token, head).
+hipError_t launch_gate_norm(const PrefillArgs& a);
 
 // Chunked MFMA prefill (bf16 inputs, d_k = d_v = 128).  With scan = true long
 // sequences are cut into segments whose (B, M) maps are composed by a scan.

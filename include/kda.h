@@ -139,6 +139,31 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          void* workspace, size_t workspace_bytes, kda_variant variant,
                          void* stream);
 
+/* kda_chunk_fwd whose output is the layer's gated, normalised read-out
+ * ("kimi delta attn from first principles", section "three gates": RMSNorm
+ * is applied to o_t = S_t^T q_t, then multiplied elementwise by the output
+ * gate): for every token and head, with o the read-out of kda_chunk_fwd,
+ *
+ *     o <- out_gate * norm_weight * o / sqrt(mean_j(o_j^2) + norm_eps)
+ *
+ * the mean over the d_v channels of that token and head.
+ *  out_gate    [B, T, H, d_v] in_dtype, the gate values as they multiply (the
+ *              caller applies the gate's activation); an input.
+ *  norm_weight [d_v] fp32, shared by all heads; an input.
+ *  norm_eps    >= 0 and finite (else KDA_ERR_SHAPE).
+ * The 12-wave chunk kernel (CHUNK, CHUNK_SCAN) applies this in its o store;
+ * RECURRENT and CHUNK64 write o and then rewrite it in place.  The
+ * workspace is that of kda_chunk_fwd_workspace_size(); every other argument
+ * and error behaviour is that of kda_chunk_fwd. */
+kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, float scale, const float* initial_state,
+                               const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                               int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                               int32_t N, kda_dtype in_dtype, kda_dtype out_dtype,
+                               const void* out_gate, const float* norm_weight, float norm_eps,
+                               void* o, float* final_state, void* workspace,
+                               size_t workspace_bytes, kda_variant variant, void* stream);
+
 /* Bytes of device workspace kda_chunk_fwd_snapshots needs (the same
  * arguments as kda_chunk_fwd_workspace_size plus the snapshot interval);
  * 0 for arguments it would reject. */

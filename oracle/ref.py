@@ -131,3 +131,21 @@ def kda_forward_snapshots(q, k, v, g, beta, scale, interval, initial_state=None,
         final[n] = S
     snaps = np.stack(snaps) if snaps else np.zeros((0, H, dk, dv), dtype=dtype)
     return o, final, snaps
+
+
+def rms_norm_gate(o, gate, weight, eps, dtype=np.float64):
+    """The output path after the read-out ("kimi delta attn from first
+    principles", section "three gates": RMSNorm is applied to o_t = S_t^T q_t,
+    then the result is multiplied elementwise by the output gate).
+
+    o, gate: [..., dv] (one vector per token and head); weight: [dv]; returns
+    gate * weight * o / sqrt(mean(o^2) + eps), the mean over the dv channels of
+    one (token, head).  Readings: the RMSNorm has a per-channel weight shared
+    by all heads and an eps inside the root (the pages name RMSNorm without
+    its parameters); the gate arrives already activated (the pages give the
+    gate a low-rank projection but not its activation).
+    """
+    o, gate = _np(o, dtype), _np(gate, dtype)
+    w = _np(weight, dtype)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    return gate * w * o / np.sqrt(ms + eps)

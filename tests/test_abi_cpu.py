@@ -198,3 +198,26 @@ def test_snapshot_validation():
     keep, cu = host_cu([0, 100000, 100100])
     plain = kda.lib.kda_chunk_fwd_workspace_size(1, 100100, 4, 128, 128, 2, cu, BF16, 3)
     assert wsz(1, 100100, 4, 128, 128, 2, cu, BF16, 3, 4096) == ((plain + 255) // 256) * 256 + 256
+
+
+def chunk_gated(gate=None, weight=None, eps=1e-6, o=None, ws=None, ws_bytes=0, variant=1,
+                T=64, H=2, dk=16, dv=16):
+    gate = addr(11) if gate is None else gate
+    weight = addr(12) if weight is None else weight
+    o = addr(5) if o is None else o
+    return kda.lib.kda_chunk_fwd_gated(addr(0), addr(1), addr(2), addr(3), addr(4), 0.25, None, None,
+                                       None, 1, T, H, dk, dv, 1, F32, F32, gate, weight, eps, o,
+                                       None, ws, ws_bytes, variant, None)
+
+
+def test_gated_validation():
+    assert chunk_gated(gate=P(0)) == NULL
+    assert chunk_gated(weight=P(0)) == NULL
+    assert chunk_gated(eps=-1e-6) == SHAPE
+    assert chunk_gated(eps=float("nan")) == SHAPE
+    assert chunk_gated(eps=float("inf")) == SHAPE
+    assert chunk_gated(gate=addr(11, 4)) == ALIGN
+    assert chunk_gated(weight=addr(12, 8)) == ALIGN
+    assert chunk_gated(gate=addr(5, 64)) == ALIAS      # the gate inside o
+    assert chunk_gated(weight=addr(5, 128)) == ALIAS   # the weight inside o
+    assert chunk_gated(T=0) == OK                      # no token: nothing to do

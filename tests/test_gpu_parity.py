@@ -280,6 +280,80 @@ def test_snapshots_varlen_workload_full_size_sampled():
         assert_parity(sn[rows[n] + j][heads], fr[0], x.q.dtype, f"snapshot {j} of sequence {n}")
 
 
+def _gate_inputs(x, seed=7):
+    gen = torch.Generator().manual_seed(seed)
+    B, T, H, _ = x.q.shape
+    dv = x.v.shape[-1]
+    gate = torch.sigmoid(torch.randn(B, T, H, dv, generator=gen)).to(x.q.dtype)
+    w = 1.0 + 0.5 * torch.randn(dv, generator=gen)
+    return gate, w
+
+
+@pytest.mark.parametrize("variant", ["chunk", "chunk_scan", "chunk64", "recurrent"])
+def test_gated_rmsnorm_output(variant):
+    say(f"gated RMSNorm output variant={variant} (ragged varlen, H=2)")
+    lens = [1, 31, 33, 64, 200, 700] if variant != "chunk_scan" else [64, 2500, 130]
+    x = synth.make_inputs("varlen", lens=lens, H=2)
+    gate, w = _gate_inputs(x)
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    y, f = _kda().chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, xd.h0, x.cu_seqlens,
+                            variant=variant, out_gate=gate.to(dev), norm_weight=w.to(dev),
+                            norm_eps=1e-5)
+    torch.cuda.synchronize()
+    o_ref, f_ref = ref.kda_forward(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0, x.cu_seqlens)
+    y_ref = ref.rms_norm_gate(o_ref, gate, w, 1e-5)
+    assert_parity(y, y_ref, x.q.dtype, "gated o")
+    assert_parity(f, f_ref, x.q.dtype, "final")
+
+
+def test_gated_rmsnorm_fp32_recurrent_and_bf16_out():
+    say("gated RMSNorm, fp32 inputs (recurrent, d=32/64), fp32 and bf16 outputs")
+    rng = np.random.default_rng(3)
+    B, T, H, dk, dv = 2, 40, 3, 32, 64
+    q = torch.tensor(rng.standard_normal((B, T, H, dk)), dtype=torch.float32)
+    k = torch.nn.functional.normalize(torch.tensor(rng.standard_normal((B, T, H, dk))), dim=-1).float()
+    v = torch.tensor(rng.standard_normal((B, T, H, dv)), dtype=torch.float32)
+    g = -torch.rand(B, T, H, dk, generator=torch.Generator().manual_seed(1))
+    beta = torch.rand(B, T, H, generator=torch.Generator().manual_seed(2))
+    gate = torch.rand(B, T, H, dv, generator=torch.Generator().manual_seed(4))
+    w = torch.randn(dv, generator=torch.Generator().manual_seed(5))
+    dev = torch.device("cuda")
+    args = [t.to(dev) for t in (q, k, v, g, beta)]
+    o_ref, _ = ref.kda_forward(q, k, v, g, beta, 0.3)
+    y_ref = ref.rms_norm_gate(o_ref, gate, w, 1e-6)
+    y, _ = _kda().chunk_fwd(*args, 0.3, out_gate=gate.to(dev), norm_weight=w.to(dev), norm_eps=1e-6)
+    yb, _ = _kda().chunk_fwd(*args, 0.3, out_gate=gate.to(dev), norm_weight=w.to(dev), norm_eps=1e-6,
+                             out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert max_abs(y, y_ref) <= 1e-4
+    # bf16 output: o is written in bf16 and rewritten in place, so each value
+    # carries at most two bf16 roundings plus the rms's: within 2^-7 of itself.
+    yr = np.asarray(y_ref)
+    err = np.abs(yb.float().cpu().numpy() - yr)
+    assert np.all(err <= 2.0 ** -7 * np.abs(yr) + 1e-6), float(np.max(err / (np.abs(yr) + 1e-6)))
+
+
+def test_gated_varlen_workload_full_size():
+    say("gated RMSNorm on the varlen workload (262144 tokens, H=32): fused == plain o then the formula")
+    x = synth.make_inputs("varlen")
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    gen = torch.Generator(device=dev).manual_seed(11)
+    gate = torch.sigmoid(torch.randn(xd.v.shape, generator=gen, device=dev)).to(torch.bfloat16)
+    w = 1.0 + 0.5 * torch.randn(128, generator=gen, device=dev)
+    kda = _kda()
+    y, f = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, xd.h0, x.cu_seqlens,
+                         out_gate=gate, norm_weight=w, norm_eps=1e-6)
+    o, f2 = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, xd.h0, x.cu_seqlens)
+    torch.cuda.synchronize()
+    assert torch.equal(f, f2)
+    y2 = gate.float() * w * o * torch.rsqrt(o.pow(2).mean(-1, keepdim=True) + 1e-6)
+    e = float(((y - y2).abs().max() / y2.pow(2).mean().sqrt()).item())
+    say(f"  fused vs formula on the plain output: max|d|/rms {e:.2e}")
+    assert e <= 1e-4
+
+
 def test_prefill_then_decode_equals_prefill():
     say("prefill T-1 then decode == prefill T (H=4, T=300)")
     x = synth.make_inputs("prefill", T=300, H=4)

@@ -245,3 +245,29 @@ def test_snapshots_are_prefix_final_states():
             row += 1
     # a chain whose length is a multiple of the interval ends on a snapshot
     assert np.max(np.abs(sn[sum(L // iv for L in lens[:2]) - 1] - f[1])) < 1e-13
+
+
+def test_rms_norm_gate_pins():
+    """RMSNorm then the output gate, against values fixed by the definition."""
+    # hand-computed: o = (3, 4): mean square 12.5, so y = o / sqrt(12.5)
+    y = ref.rms_norm_gate(np.array([3.0, 4.0]), np.ones(2), np.ones(2), 0.0)
+    assert np.max(np.abs(y - np.array([3.0, 4.0]) / np.sqrt(12.5))) < 1e-15
+    rng = np.random.default_rng(21)
+    o = rng.standard_normal((3, 5, 16))
+    one = np.ones(16)
+    # unit RMS with unit gate and weight, no eps
+    y = ref.rms_norm_gate(o, np.ones_like(o), one, 0.0)
+    assert np.max(np.abs(np.sqrt(np.mean(y * y, axis=-1)) - 1.0)) < 1e-13
+    # scale invariance per vector (positive factors), sign follows o
+    lam = rng.uniform(0.1, 10.0, size=(3, 5, 1))
+    assert np.max(np.abs(ref.rms_norm_gate(lam * o, np.ones_like(o), one, 0.0) - y)) < 1e-12
+    # a constant vector maps to ones
+    assert np.max(np.abs(ref.rms_norm_gate(np.full(16, 7.5), np.ones(16), one, 0.0) - 1.0)) < 1e-15
+    # gate and weight multiply elementwise; eps only shrinks; zero stays zero
+    gt, w = rng.uniform(0, 1, o.shape), rng.standard_normal(16)
+    assert np.max(np.abs(ref.rms_norm_gate(o, gt, w, 0.0) - gt * w * y)) < 1e-12
+    ye = ref.rms_norm_gate(o, np.ones_like(o), one, 0.5)
+    assert np.all(np.abs(ye) <= np.abs(y) + 1e-15)
+    # eps inside the root: a vector of ones with eps = 3 maps to 1 / sqrt(1 + 3) = 1/2
+    assert np.all(ref.rms_norm_gate(np.ones(16), np.ones(16), one, 3.0) == 0.5)
+    assert np.all(ref.rms_norm_gate(np.zeros(16), np.ones(16), one, 1e-6) == 0.0)
