@@ -296,6 +296,23 @@ def main():
             "us_per_launch": vm * 1e3, "gbs": vb / (vm * 1e-3) / 1e9,
             "frac": vb / (vm * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": vb,
             "config": f"{Nv} sequences x {Tv} tokens x {Hv} heads, d={dkv}, state in place"}}
+        # The gate inputs from their projections for every token of the workload
+        # (kda_fused_gate, bf16 MFMA up-projection of rank 128).
+        rk = 128
+        gen0 = torch.Generator(device=dev).manual_seed(13)
+        zq = (0.5 * torch.randn(tokens, rk, generator=gen0, device=dev)).to(torch.bfloat16)
+        wq = (torch.randn(H * dk, rk, generator=gen0, device=dev) / rk ** 0.5).to(torch.bfloat16)
+        bq = torch.randn(H * dk, generator=gen0, device=dev) - 2.0
+        uq = torch.randn(tokens, H, generator=gen0, device=dev)
+        fm = time_launches(lambda: kda.fused_gate(zq, wq, uq, bq), stream, 5)
+        fb = tokens * rk * 2 + rk * H * dk * 2 + H * dk * 4 + tokens * H * 4 * 2 + tokens * H * dk * 4
+        ff = 2.0 * tokens * rk * H * dk
+        line["extras"]["fused_gate"] = {
+            "ms_per_launch": fm, "gbs": fb / (fm * 1e-3) / 1e9,
+            "frac": fb / (fm * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": fb,
+            "tflops": ff / (fm * 1e-3) / 1e12,
+            "config": f"{tokens} tokens, rank {rk} up to {H} x {dk} log-gates (fp32) + beta"}
+        del zq, uq
         if args.workload == "varlen":
             # The same prefill with the state of every sequence kept each 4096 tokens
             # (kda_chunk_fwd_snapshots), against the plain prefill timed above.

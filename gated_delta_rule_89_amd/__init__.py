@@ -9,10 +9,12 @@ include/kda.h); this package is a thin binding over it:
                                      one token per sequence, state in place
     chunk_fwd_snapshots(q, k, v, g, beta, scale, interval, ...)
         -> (o, final_state, snapshots) states every `interval` tokens
+    fused_gate(z, w_up, u, b_up=None) -> (g, beta)
+                                     gate inputs from their projections
     fused_recurrent_fwd(q, k, v, g, beta, scale, state) -> o
                                      a short run of tokens per sequence
                                      (T <= 64), state in place
 """
 from ._lib import (KDAError, abi_version, chunk_fwd, chunk_fwd_snapshots, decode_step,  # noqa: F401
-                   fused_recurrent_fwd, lib, snapshot_rows, snapshots_workspace_size, status_str,
+                   fused_gate, fused_recurrent_fwd, lib, snapshot_rows, snapshots_workspace_size, status_str,
                    workspace_size)

@@ -25,7 +25,7 @@ VARIANTS = {"auto": 0, "recurrent": 1, "chunk": 2, "chunk_scan": 3, "chunk64": 4
 EXPORTS = ("kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd", "kda_decode_step", "kda_fused_recurrent_fwd",
            "kda_chunk_fwd_snapshots_workspace_size", "kda_chunk_fwd_snapshots",
-           "kda_chunk_fwd_gated")
+           "kda_chunk_fwd_gated", "kda_fused_gate")
 FUSED_RECURRENT_MAX_T = 64
 
 
@@ -65,6 +65,8 @@ def _load() -> ctypes.CDLL:
                                         I32, I32, I32, I32, I32, I32, ctypes.c_int, ctypes.c_int,
                                         P, P, ctypes.c_float, P, P, P, SZ, ctypes.c_int, P]
     lib.kda_chunk_fwd_gated.restype = ctypes.c_int
+    lib.kda_fused_gate.argtypes = [P, P, P, P, I32, I32, I32, I32, ctypes.c_int, P, P, P]
+    lib.kda_fused_gate.restype = ctypes.c_int
     return lib
 
 
@@ -268,3 +270,24 @@ def fused_recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
                                        _ptr(o), _stream(q.device))
     _check(code)
     return o
+
+
+def fused_gate(z: torch.Tensor, w_up: torch.Tensor, u: torch.Tensor,
+               b_up: Optional[torch.Tensor] = None, H: Optional[int] = None):
+    """kda_fused_gate: z [M, r] bf16, w_up [H*dk, r] bf16 (a linear layer's
+    weight), u [M, H] fp32, b_up [H*dk] fp32 or None.  Returns
+    (g [M, H, dk] fp32, beta [M, H] fp32) with g = -softplus(z w_up^T + b_up)
+    and beta = sigmoid(u)."""
+    for name, t in (("z", z), ("w_up", w_up), ("u", u)):
+        _dev(t, name)
+    if b_up is not None:
+        _dev(b_up, "b_up")
+    M, r = z.shape
+    H = u.shape[1] if H is None else H
+    dk = w_up.shape[0] // H
+    g = torch.empty(M, H, dk, dtype=torch.float32, device=z.device)
+    beta = torch.empty(M, H, dtype=torch.float32, device=z.device)
+    code = lib.kda_fused_gate(_ptr(z), _ptr(w_up), _ptr(b_up), _ptr(u), M, r, H, dk, _dt(z.dtype),
+                              _ptr(g), _ptr(beta), _stream(z.device))
+    _check(code)
+    return g, beta

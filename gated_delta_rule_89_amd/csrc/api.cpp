@@ -306,6 +306,30 @@ size_t kda_chunk_fwd_snapshots_workspace_size(int32_t B, int32_t T, int32_t H, i
     return align256_(plain) + align256_(static_cast<size_t>(N) * 4);
 }
 
+kda_status kda_fused_gate(const void* z, const void* w_up, const float* b_up, const float* u,
+                          int32_t M, int32_t r, int32_t H, int32_t d_k, kda_dtype in_dtype,
+                          float* g, float* beta, void* stream) {
+    if (!dtype_ok(in_dtype)) return KDA_ERR_DTYPE;
+    if (M < 0 || r <= 0 || H < 0 || d_k <= 0) return KDA_ERR_SHAPE;
+    if (in_dtype != KDA_BF16 || d_k != 128 || (r != 32 && r != 64 && r != 128 && r != 256))
+        return KDA_ERR_UNSUPPORTED;
+    if (M == 0 || H == 0) return KDA_OK;
+    if (!z || !w_up || !u || !g || !beta) return KDA_ERR_NULL;
+    if (static_cast<int64_t>(H) * d_k > INT32_MAX / 2) return KDA_ERR_SHAPE;
+    for (const void* p : {z, w_up, static_cast<const void*>(g)})
+        if (!aligned(p, 16)) return KDA_ERR_ALIGN;
+    if (!aligned(b_up, 16) || !aligned(u, 4) || !aligned(beta, 4)) return KDA_ERR_ALIGN;
+    const size_t n = static_cast<size_t>(H) * d_k, m = static_cast<size_t>(M);
+    const Range in_r[] = {range(z, m * r * 2), range(w_up, static_cast<size_t>(r) * n * 2),
+                          range(b_up, b_up ? n * 4 : 0), range(u, m * H * 4)};
+    const Range g_r = range(g, m * n * 4), b_r = range(beta, m * H * 4);
+    for (const Range& x : in_r)
+        if (overlap(g_r, x) || overlap(b_r, x)) return KDA_ERR_ALIAS;
+    if (overlap(g_r, b_r)) return KDA_ERR_ALIAS;
+    return kda::launch_fused_gate(z, w_up, b_up, u, M, r, H, g, beta,
+                                  static_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* g,
                                const float* beta, float scale, const float* initial_state,
                                const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,

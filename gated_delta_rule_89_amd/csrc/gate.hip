@@ -1,0 +1,118 @@
+// Fused gate computation: the forget gate's low-rank up-projection with its
+// activation, and the update gate's sigmoid ("kimi delta attn from first
+// principles", section "three gates": alpha comes from a low-rank projection,
+// a down projection to rank r followed by an up projection to the key
+// channels; beta is a sigmoid of its projection).
+//
+//   g[m, h, c]  = -softplus(sum_j z[m, j] W[h d_k + c, j] + b[h d_k + c])   (log alpha <= 0)
+//   beta[m, h]  = 1 / (1 + exp(-u[m, h]))
+//
+// W is [H d_k, r] (a linear layer's weight, output rows): every MFMA operand
+// fragment, 8 consecutive j of one row of z or of W, is one 16-byte read.
+// The up-projection is a dense contraction (M x r by r x H d_k), so it runs
+// on bf16 MFMA (16x16x32, fp32 accumulation).  The write of g (4 bytes per
+// element) dominates the traffic: the kernel is bound by HBM writes.
+#include "dev_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace gatek {
+
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr int ROWS = 64;   // rows of z per wave
+constexpr int DK = 128;    // key channels per head
+
+__device__ __forceinline__ float neg_softplus(float x) {
+    // -(max(x, 0) + log(1 + exp(-|x|))), in base 2 with the hardware exp2/log2
+    constexpr float LOG2E = 1.4426950408889634f, LN2 = 0.6931471805599453f;
+    const float t = __builtin_amdgcn_exp2f(-fabsf(x) * LOG2E);
+    return -(fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + t) * LN2);
+}
+
+// One wave per (64 rows of z, head): its MFMA fragments come straight from
+// global memory (z rows and W rows are both contiguous along j; W is small
+// and stays in L2), so there is no LDS staging and no barrier.  A workgroup
+// holds the 4 waves of 4 consecutive heads over the same rows, which share
+// those rows of z in the caches.
+template <int R>
+__global__ __launch_bounds__(256) void fused_gate_kernel(const uint16_t* __restrict__ z,
+                                                         const uint16_t* __restrict__ w,
+                                                         const float* __restrict__ bias,
+                                                         const float* __restrict__ u, int64_t M, int H,
+                                                         float* __restrict__ g, float* __restrict__ beta) {
+    constexpr int RT = ROWS / 16;  // 16-row tiles per wave
+    const int tid = threadIdx.x, l = tid & 63, r16 = l & 15, g4 = l >> 4;
+    const int h = blockIdx.y * 4 + (tid >> 6);
+    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * ROWS;
+    const int64_t N = static_cast<int64_t>(H) * DK;  // row length of g
+    if (h >= H) return;  // whole wave
+    if (h == 0) {  // beta of these rows, once per row block
+        for (int e = l; e < ROWS * H; e += 64) {
+            const int64_t idx = m0 * H + e;
+            if (idx < M * H) beta[idx] = 1.f / (1.f + __builtin_amdgcn_exp2f(-u[idx] * 1.4426950408889634f));
+        }
+    }
+    f4 acc[RT][DK / 16];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < DK / 16; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* wh = w + static_cast<int64_t>(h) * DK * R;
+#pragma unroll
+    for (int ks = 0; ks < R / 32; ++ks) {
+        b8 a[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int64_t m = m0 + 16 * rt + r16;
+            u4 val = {0, 0, 0, 0};
+            if (m < M) val = *reinterpret_cast<const u4*>(z + m * R + 32 * ks + 8 * g4);
+            a[rt] = __builtin_bit_cast(b8, val);
+        }
+#pragma unroll
+        for (int ct = 0; ct < DK / 16; ++ct) {
+            const b8 bf = __builtin_bit_cast(
+                b8, *reinterpret_cast<const u4*>(wh + (16 * ct + r16) * R + 32 * ks + 8 * g4));
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt], bf, acc[rt][ct], 0, 0, 0);
+        }
+    }
+    // D layout: lane holds rows 4 g4 + i of each 16 x 16 tile, column r16
+#pragma unroll
+    for (int ct = 0; ct < DK / 16; ++ct) {
+        const int c = 16 * ct + r16;
+        const float bc = bias ? bias[h * DK + c] : 0.f;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t m = m0 + 16 * rt + 4 * g4 + i;
+                if (m < M) __builtin_nontemporal_store(neg_softplus(acc[rt][ct][i] + bc), &g[m * N + h * DK + c]);
+            }
+    }
+}
+
+}  // namespace gatek
+
+hipError_t launch_fused_gate(const void* z, const void* w, const float* bias, const float* u,
+                             int64_t M, int r, int H, float* g, float* beta, hipStream_t stream) {
+    using namespace gatek;
+    const dim3 grid(static_cast<uint32_t>((M + ROWS - 1) / ROWS), static_cast<uint32_t>((H + 3) / 4));
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(z),
+                           static_cast<const uint16_t*>(w), bias, u, M, H, g, beta);
+    };
+    switch (r) {
+        case 32: go(fused_gate_kernel<32>); break;
+        case 64: go(fused_gate_kernel<64>); break;
+        case 128: go(fused_gate_kernel<128>); break;
+        case 256: go(fused_gate_kernel<256>); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -164,6 +164,32 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, cons
                                void* o, float* final_state, void* workspace,
                                size_t workspace_bytes, kda_variant variant, void* stream);
 
+/* The gate inputs of kda_chunk_fwd from their projections ("kimi delta attn
+ * from first principles", section "three gates": the forget gate alpha comes
+ * from a low-rank projection -- down to rank r, then up to the key channels
+ * -- and the update gate beta is the sigmoid of its projection):
+ *
+ *     g[m, h, c] = -softplus(sum_j z[m, j] w_up[h d_k + c, j] + b_up[h d_k + c])
+ *     beta[m, h] = 1 / (1 + exp(-u[m, h]))
+ *
+ * so that alpha = exp(g) lies in (0, 1).  The pages give the projection's
+ * structure but not the activation that makes it a log-decay; -softplus is
+ * this library's choice (documented as such).  m runs over the M tokens of
+ * the batch (B T, or the packed tokens).
+ *  z       [M, r] bf16, the down-projected activations (r in {32, 64, 128, 256})
+ *  w_up    [H d_k, r] bf16 (a linear layer's weight: one row per output
+ *          channel, d_k = 128)
+ *  b_up    [H d_k] fp32 or NULL (no bias); 16-byte aligned
+ *  u       [M, H] fp32, the beta projection
+ *  g       [M, H, d_k] fp32, written (the layout kda_chunk_fwd reads)
+ *  beta    [M, H] fp32, written
+ * Only in_dtype = KDA_BF16 with d_k = 128 is supported (else
+ * KDA_ERR_UNSUPPORTED).  g and beta must not overlap the inputs or each
+ * other.  M = 0 or H = 0 is a successful no-op. */
+kda_status kda_fused_gate(const void* z, const void* w_up, const float* b_up, const float* u,
+                          int32_t M, int32_t r, int32_t H, int32_t d_k, kda_dtype in_dtype,
+                          float* g, float* beta, void* stream);
+
 /* Bytes of device workspace kda_chunk_fwd_snapshots needs (the same
  * arguments as kda_chunk_fwd_workspace_size plus the snapshot interval);
  * 0 for arguments it would reject. */

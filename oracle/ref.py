@@ -149,3 +149,27 @@ def rms_norm_gate(o, gate, weight, eps, dtype=np.float64):
     w = _np(weight, dtype)
     ms = np.mean(o * o, axis=-1, keepdims=True)
     return gate * w * o / np.sqrt(ms + eps)
+
+
+def fused_gate(z, w_up, u, b_up=None, H=None, dtype=np.float64):
+    """The gate inputs from their projections ("kimi delta attn from first
+    principles", section "three gates": a low-rank projection -- down, then
+    up to the key channels -- gives the forget gate; a sigmoid of its
+    projection gives the update gate beta).
+
+    z [M, r], w_up [H dk, r] (one row per output channel), u [M, H],
+    b_up [H dk] or None.  Returns g [M, H, dk] = -softplus(z w_up^T + b_up)
+    (the log-decay, <= 0) and
+    beta [M, H] = sigmoid(u).  Reading: the pages do not give the activation
+    that turns the up-projection into a log-decay; -softplus is the one
+    adopted here (alpha = exp(g) = sigmoid(-(z w_up^T + b)) lies in (0, 1)).
+    """
+    z, w, u = _np(z, dtype), _np(w_up, dtype), _np(u, dtype)
+    M = z.shape[0]
+    H = u.shape[1] if H is None else H
+    a = z @ w.T
+    if b_up is not None:
+        a = a + _np(b_up, dtype)
+    g = -np.logaddexp(0.0, a)
+    beta = 1.0 / (1.0 + np.exp(-u))
+    return g.reshape(M, H, -1), beta

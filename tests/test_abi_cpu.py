@@ -221,3 +221,23 @@ def test_gated_validation():
     assert chunk_gated(gate=addr(5, 64)) == ALIAS      # the gate inside o
     assert chunk_gated(weight=addr(5, 128)) == ALIAS   # the weight inside o
     assert chunk_gated(T=0) == OK                      # no token: nothing to do
+
+
+def fgate(z=None, w=None, b=None, u=None, M=100, r=128, H=2, dk=128, ind=BF16, g=None, beta=None):
+    z = addr(0) if z is None else z
+    w = addr(1) if w is None else w
+    u = addr(2) if u is None else u
+    g = addr(3) if g is None else g
+    beta = addr(4) if beta is None else beta
+    return kda.lib.kda_fused_gate(z, w, b, u, M, r, H, dk, ind, g, beta, None)
+
+
+def test_fused_gate_validation():
+    assert fgate(ind=5) == DTYPE
+    assert fgate(M=-1) == SHAPE
+    assert fgate(ind=F32) == UNSUP and fgate(dk=64) == UNSUP and fgate(r=100) == UNSUP
+    assert fgate(u=P(0)) == NULL and fgate(g=P(0)) == NULL
+    assert fgate(b=P(BASE + 2)) == ALIGN and fgate(w=addr(1, 8)) == ALIGN
+    assert fgate(g=addr(0, 512)) == ALIAS                 # g over z
+    assert fgate(beta=addr(3, 1024)) == ALIAS             # beta inside g
+    assert fgate(M=0) == OK

@@ -354,6 +354,44 @@ def test_gated_varlen_workload_full_size():
     assert e <= 1e-4
 
 
+def _gate_proj(M, r, H, seed, dev=None):
+    gen = torch.Generator().manual_seed(seed)
+    z = (torch.randn(M, r, generator=gen) * 0.5).to(torch.bfloat16)
+    w = (torch.randn(H * 128, r, generator=gen) / np.sqrt(r)).to(torch.bfloat16)
+    b = torch.randn(H * 128, generator=gen) - 2.0
+    u = torch.randn(M, H, generator=gen) * 2.0
+    return z, w, b, u
+
+
+@pytest.mark.parametrize("M,r,H,bias", [(1, 32, 1, True), (127, 64, 3, False), (300, 128, 2, True),
+                                        (129, 256, 1, True)])
+def test_fused_gate(M, r, H, bias):
+    say(f"fused gate M={M} r={r} H={H} bias={bias}")
+    z, w, b, u = _gate_proj(M, r, H, M + r)
+    dev = torch.device("cuda")
+    g, beta = _kda().fused_gate(z.to(dev), w.to(dev), u.to(dev), b.to(dev) if bias else None)
+    torch.cuda.synchronize()
+    g_ref, b_ref = ref.fused_gate(z, w, u, b if bias else None)
+    gd = g.cpu().double().numpy()
+    assert np.all(np.abs(gd - g_ref) <= 1e-5 * (1.0 + np.abs(g_ref)))
+    assert max_abs(beta, b_ref) <= 1e-6
+
+
+def test_fused_gate_full_size_sampled_rows():
+    say("fused gate M=262144 r=128 H=32 (the varlen workload's tokens), sampled rows")
+    M, r, H = 262144, 128, 32
+    z, w, b, u = _gate_proj(M, r, H, 99)
+    dev = torch.device("cuda")
+    g, beta = _kda().fused_gate(z.to(dev), w.to(dev), u.to(dev), b.to(dev))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 4095, 131071, 200003, M - 1])
+    g_ref, b_ref = ref.fused_gate(z[rows], w, u[rows], b)
+    gd = g[torch.as_tensor(rows, device=dev)].cpu().double().numpy()
+    assert np.all(np.abs(gd - g_ref) <= 1e-5 * (1.0 + np.abs(g_ref)))
+    assert max_abs(beta[torch.as_tensor(rows, device=dev)], b_ref) <= 1e-6
+    assert bool(torch.isfinite(g).all()) and bool((g < 0).all())
+
+
 def test_prefill_then_decode_equals_prefill():
     say("prefill T-1 then decode == prefill T (H=4, T=300)")
     x = synth.make_inputs("prefill", T=300, H=4)

@@ -271,3 +271,40 @@ def test_rms_norm_gate_pins():
     # eps inside the root: a vector of ones with eps = 3 maps to 1 / sqrt(1 + 3) = 1/2
     assert np.all(ref.rms_norm_gate(np.ones(16), np.ones(16), one, 3.0) == 0.5)
     assert np.all(ref.rms_norm_gate(np.zeros(16), np.ones(16), one, 1e-6) == 0.0)
+
+
+def test_fused_gate_pins():
+    """g = -softplus(z w + b) and beta = sigmoid(u), against closed forms, an
+    explicit triple loop for the contraction, and a one-hot layout check."""
+    # closed forms: softplus(0) = ln 2; softplus(a) -> a for large a, -> e^a for very negative a
+    z0 = np.zeros((1, 4))
+    w0 = np.zeros((2 * 3, 4))
+    g, b = ref.fused_gate(z0, w0, np.zeros((1, 2)))
+    assert g.shape == (1, 2, 3) and np.all(np.abs(g + np.log(2.0)) < 1e-15) and np.all(b == 0.5)
+    g, _ = ref.fused_gate(z0, w0, np.zeros((1, 2)), b_up=np.full(6, 40.0))
+    assert np.all(np.abs(g + 40.0) < 1e-15)
+    g, _ = ref.fused_gate(z0, w0, np.zeros((1, 2)), b_up=np.full(6, -40.0))
+    assert np.all(np.abs(g + np.exp(-40.0)) < 1e-30) and np.all(g < 0)
+    _, b = ref.fused_gate(z0, w0, np.array([[40.0, -40.0]]))
+    assert abs(b[0, 0] - 1.0) < 1e-15 and abs(b[0, 1] - np.exp(-40.0)) < 1e-30
+    # the contraction against explicit loops, with the head/channel layout
+    rng = np.random.default_rng(22)
+    M, r, H, dk = 3, 5, 2, 4
+    z, w = rng.standard_normal((M, r)), rng.standard_normal((H * dk, r))
+    bias, u = rng.standard_normal(H * dk), rng.standard_normal((M, H))
+    g, b = ref.fused_gate(z, w, u, b_up=bias)
+    for m in range(M):
+        for h in range(H):
+            for c in range(dk):
+                a = bias[h * dk + c] + sum(z[m, j] * w[h * dk + c, j] for j in range(r))
+                sp = a + np.log1p(np.exp(-a)) if a > 0 else np.log1p(np.exp(a))
+                assert abs(g[m, h, c] + sp) < 1e-12
+            assert abs(b[m, h] - 1.0 / (1.0 + np.exp(-u[m, h]))) < 1e-15
+    # one hot: a single nonzero weight moves only its (head, channel)
+    w1 = np.zeros((H * dk, r))
+    w1[1 * dk + 3, 2] = 5.0
+    z1 = np.zeros((M, r))
+    z1[1, 2] = 1.0
+    g, _ = ref.fused_gate(z1, w1, u)
+    moved = np.argwhere(np.abs(g + np.log(2.0)) > 1e-12)
+    assert moved.tolist() == [[1, 1, 3]] and abs(g[1, 1, 3] + np.logaddexp(0.0, 5.0)) < 1e-15
