@@ -229,12 +229,16 @@ __device__ __forceinline__ void unpack_bf16x8(u4 w, float* out) {
     }
 }
 
-// Exponent e with max(|S|, |v|) * 2^e in [2^9, 2^10): the fp16 copies of the
-// value-side operands then stay far from both ends of the fp16 range.
+// Exponent e for max(|S|, |v|) = mx: the current one while mx * 2^ex stays
+// in [2^8, 2^11), else the one that puts it in [2^9, 2^10).  The fp16 copies
+// of the value-side operands then stay far from both ends of the fp16 range
+// (K~ S with unit keys is at most sqrt(128) 2^11 < 2^15), and the state is
+// rescaled only when its magnitude has drifted by a factor of two or more.
 __device__ __forceinline__ int value_exponent(float mx, int ex) {
     if (!(mx > 0.f) || !(mx < 3.0e38f)) return ex;
     int e2;
-    (void)frexpf(mx, &e2);
+    (void)frexpf(mx, &e2);  // mx in [2^(e2-1), 2^e2)
+    if (e2 - 1 + ex >= 8 && e2 + ex <= 11) return ex;
     const int e = 10 - e2;
     return e < -120 ? -120 : (e > 120 ? 120 : e);
 }
