@@ -24,20 +24,25 @@ namespace kda {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int DK, int DV>
+// NT threads per (sequence, head): TPR threads cover a row in 16-byte pieces,
+// RGS row groups of R rows each.  A single step streams the state once and
+// wants many requests in flight (512 threads measured faster); a run of
+// tokens crosses a barrier per token and wants fewer, fuller threads (256).
+template <int DK, int DV, int NT = 256>
 struct DecodeShape {
     static constexpr int TPR = DV / 4;                                    // threads per row
-    static constexpr int RGS = (256 / TPR) < DK ? (256 / TPR) : DK;      // row groups
+    static constexpr int RGS = (NT / TPR) < DK ? (NT / TPR) : DK;        // row groups
     static constexpr int THREADS = TPR * RGS;
     static constexpr int R = DK / RGS;                                    // rows per thread
 };
+constexpr int kDecodeThreads = 512;
 
 template <int DK, int DV, typename Tin, typename Tout>
-__global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void decode_kernel(
+__global__ __launch_bounds__((DecodeShape<DK, DV, kDecodeThreads>::THREADS)) void decode_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float scale,
     float* __restrict__ state, Tout* __restrict__ o) {
-    using Sh = DecodeShape<DK, DV>;
+    using Sh = DecodeShape<DK, DV, kDecodeThreads>;
     constexpr int TPR = Sh::TPR, RGS = Sh::RGS, R = Sh::R;
     __shared__ float red_k[RGS][DV];
     __shared__ float red_q[RGS][DV];
@@ -109,7 +114,7 @@ template <int DK, int DV, typename Tin, typename Tout>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
     const int64_t blocks = static_cast<int64_t>(a.N) * a.H;
     hipLaunchKernelGGL((decode_kernel<DK, DV, Tin, Tout>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(DecodeShape<DK, DV>::THREADS), 0, a.stream,
+                       dim3(DecodeShape<DK, DV, kDecodeThreads>::THREADS), 0, a.stream,
                        static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                        static_cast<const Tin*>(a.v), a.g, a.beta, a.scale, a.state,
                        static_cast<Tout*>(a.o));
