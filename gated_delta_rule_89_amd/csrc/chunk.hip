@@ -825,6 +825,7 @@ struct alignas(16) Tiles {               // operands of one chunk's state pass
     _Float16 tb[NSB + NX][SB][BP];       // T00, T11, -G10
     _Float16 p[C][TP];                   // P    [token][token, operand order]
     uint16_t v[C][QP];                   // v tile (bf16 bits) [token][column]
+    uint16_t og[C][QP];                  // output gate tile (bf16 bits), gated output only
     float lam[D];                        // Lambda_last
 };
 struct alignas(16) Smem {
@@ -875,7 +876,7 @@ void chunk_ws_kernel(
     const int I = gw / NP, part = gw % NP;
     const int gtid = tid - NSW * 64;
     const int tok = SB * I + r;
-    u4 kw[KS], qw[KS], vp[VU];
+    u4 kw[KS], qw[KS], vp[VU], gp_[VU];
     f4 ga[KS], gb[KS];
     float bt = 0.f;
     // Tokens at or past the end of the sequence lie outside the buffer range
@@ -902,12 +903,14 @@ void chunk_ws_kernel(
         }
         bt = bload4(rb, 4 * tok * H);
     };
-    auto fetch_v = [&](int64_t cs) {
+    auto fetch_v = [&](int64_t cs) {  // v (and the output gate) in the staging layout
         const auto rv = rsrc(v + (cs * H + h) * D, valid_at(cs) * rowe * 2);
+        const auto rog = rsrc(ogate + (cs * H + h) * D, GATED ? valid_at(cs) * rowe * 2 : 0u);
 #pragma unroll
         for (int j = 0; j < VU; ++j) {
             const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
             vp[j] = bload16(rv, 2 * (vt * rowe + vc));
+            if (GATED) gp_[j] = bload16(rog, 2 * (vt * rowe + vc));
         }
     };
     fetch_gate(t0);
@@ -1041,6 +1044,7 @@ void chunk_ws_kernel(
                 for (int j = 0; j < VU; ++j) {
                     const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
                     *reinterpret_cast<u4*>(&nxt.v[vt][vc]) = vp[j];
+                    if (GATED) *reinterpret_cast<u4*>(&nxt.og[vt][vc]) = gp_[j];
                 }
             }
             fetch_v(t0 + static_cast<int64_t>(c + 2) * C);
@@ -1258,13 +1262,6 @@ void chunk_ws_kernel(
             }
             __syncthreads();
             if (swork) {
-                u4 gv[2];  // output gate of this lane's epilogue row (its latency overlaps the S update)
-                if (GATED) {
-                    const int el = epi_lane(), erow = 8 * (w & 3) + (el >> 3), ecol = 16 * (el & 7);
-                    const auto rg = rsrc(ogate + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * 2);
-                    gv[0] = bload16(rg, (erow * rowe + ecol) * 2);
-                    gv[1] = bload16(rg, (erow * rowe + ecol) * 2 + 16);
-                }
     #pragma unroll
                 for (int rt = 0; rt < 8; ++rt) {
                     const f4 lam = *reinterpret_cast<const f4*>(&cur.lam[16 * rt + 4 * g4]);
@@ -1291,7 +1288,7 @@ void chunk_ws_kernel(
     #pragma unroll
                     for (int j2 = 0; j2 < 2; ++j2) {  // 8 channels per step
                         float gf[8], yv[8];
-                        unpack_bf16x8(gv[j2], gf);
+                        unpack_bf16x8(*reinterpret_cast<const u4*>(&cur.og[erow][ecol + 8 * j2]), gf);
     #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
                             const int c4 = ecol + 8 * j2 + 4 * jj;
