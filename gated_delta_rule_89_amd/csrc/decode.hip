@@ -26,9 +26,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // NT threads per (sequence, head): TPR threads cover a row in 16-byte pieces,
 // RGS row groups of R rows each.  A single step streams the state once and
-// wants many requests in flight (512 threads measured faster); a run of
-// tokens crosses a barrier per token and wants fewer, fuller threads (256).
-template <int DK, int DV, int NT = 256>
+// wants many requests in flight (512 threads measured faster than 256).
+template <int DK, int DV, int NT>
 struct DecodeShape {
     static constexpr int TPR = DV / 4;                                    // threads per row
     static constexpr int RGS = (NT / TPR) < DK ? (NT / TPR) : DK;        // row groups
@@ -137,110 +136,123 @@ hipError_t launch_decode(const DecodeArgs& a) {
     });
 }
 
-// T consecutive tokens per (sequence, head) with the state in place: the
-// same step as decode_kernel, repeated while the state stays in registers,
-// so the state still makes one trip in and one trip out for the whole run
-// (the fused recurrent mode over a short run of tokens).  Token t's inputs
-// sit at ((n T + t) H + h) of the [N, T, H, .] tensors.  The two reductions
-// over the rows go through double-buffered LDS partials, one barrier per
-// token; the next token's row inputs are read before that barrier.
+// T consecutive tokens per (sequence, head) with the state in place (the
+// fused recurrent mode over a short run of tokens): the state is read once,
+// kept in registers for the whole run and written once.  Token t's inputs
+// sit at ((n T + t) H + h) of the [N, T, H, .] tensors.
+//
+// One wave owns CW (<= 32) columns of one state: lane l holds rows
+// R rg .. R rg + R - 1 (rg = l / TPR) of 4 columns (16-byte pieces, so a row
+// segment of the wave is CW * 4 contiguous bytes).  The two reductions over
+// the rows (S^T k and S^T q of the decayed state) stay inside the wave: DPP
+// row rotations inside each 16-lane row, then the row-pair swaps
+// v_permlane16_swap / v_permlane32_swap across rows.  No LDS, no barrier;
+// the next token's inputs are loaded before the current token's reductions.
+template <int TPR>
+__device__ __forceinline__ float sum_row_groups(float x) {
+    // lanes that share l % TPR; TPR in {4, 8}
+    if (TPR == 4) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
+template <int R, typename T>
+__device__ __forceinline__ void load_rows(const T* __restrict__ p, int64_t b, float (&x)[R]) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) x[i] = ld(p, b + i);
+}
+
 template <int DK, int DV, typename Tin, typename Tout>
-__global__ __launch_bounds__((DecodeShape<DK, DV>::THREADS)) void steps_kernel(
+__global__ __launch_bounds__(256) void steps_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float scale,
-    float* __restrict__ state, Tout* __restrict__ o, int T, int H) {
-    using Sh = DecodeShape<DK, DV>;
-    constexpr int TPR = Sh::TPR, RGS = Sh::RGS, R = Sh::R;
-    __shared__ float red_k[2][RGS][DV];
-    __shared__ float red_q[2][RGS][DV];
-    __shared__ float red_qk[2][RGS];
-
-    const int c4 = threadIdx.x % TPR;
-    const int rg = threadIdx.x / TPR;
-    const int64_t nh = blockIdx.x;  // n * H + h
+    float* __restrict__ state, Tout* __restrict__ o, int T, int H, int64_t items) {
+    constexpr int CW = DV < 32 ? DV : 32;   // columns per wave
+    constexpr int TPR = CW / 4;              // lanes per row
+    constexpr int RG = 64 / TPR;             // row groups per wave
+    constexpr int R = DK / RG;               // rows per lane
+    constexpr int NCB = DV / CW;             // waves per state
+    static_assert(TPR == 4 || TPR == 8, "4 or 8 lanes per row");
+    static_assert(R >= 1 && DK % RG == 0, "rows split evenly over the row groups");
+    const int l = threadIdx.x & 63;
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (item >= items) return;  // whole wave
+    const int64_t nh = item / NCB;
+    const int col = static_cast<int>(item % NCB) * CW + 4 * (l % TPR);
+    const int r0 = (l / TPR) * R;
     const int64_t n = nh / H, h = nh % H;
-    float* S = state + nh * DK * DV;
+    float* S = state + nh * DK * DV + col;
 
     f32x4 s[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) s[i] = *(reinterpret_cast<const f32x4*>(S + (rg + RGS * i) * DV) + c4);
+    for (int i = 0; i < R; ++i) s[i] = *reinterpret_cast<const f32x4*>(S + (r0 + i) * DV);
 
-    // row inputs of the token being processed (kr, qr, a) and of the next one
-    float kr[R], qr[R], a[R], nk[R], nq[R], na[R];
-    auto fetch = [&](int t, float* fk, float* fq, float* fa) {
-        const int64_t b = ((n * T + t) * H + h) * DK;
+    // k is double-buffered (the update needs it after the reductions); q and
+    // g of the next token are loaded as soon as the dot products are done.
+    float kr[R], qr[R], ga[R], nk[R];
+    f32x4 vt, nv;
+    float bt, nb;
+    auto fetch_k = [&](int t) {
+        const int64_t tv = (n * T + t) * H + h;
+        load_rows<R>(k, tv * DK + r0, nk);
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const int r = rg + RGS * i;
-            fk[i] = ld(k, b + r);
-            fq[i] = ld(q, b + r);
-            fa[i] = gate_exp(g[b + r]);
-        }
+        for (int c = 0; c < 4; ++c) nv[c] = ld(v, tv * DV + col + c);
+        nb = beta[tv];
     };
-    fetch(0, kr, qr, a);
+    auto fetch_qg = [&](int t) {
+        const int64_t tv = (n * T + t) * H + h;
+        load_rows<R>(q, tv * DK + r0, qr);
+        load_rows<R>(g, tv * DK + r0, ga);
+    };
+    fetch_k(0);
+    fetch_qg(0);
     for (int t = 0; t < T; ++t) {
-        const int buf = t & 1;
-        const int64_t tv = (n * T + t) * H + h;  // token row of v, beta, o
+        const int64_t tv = (n * T + t) * H + h;
+        const int tn = t + 1 < T ? t + 1 : t;  // every iteration loads: exact load counting
+#pragma unroll
+        for (int i = 0; i < R; ++i) kr[i] = nk[i];
+        vt = nv;
+        bt = nb;
+        fetch_k(tn);
         f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
         float qk = 0.f;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            s[i] *= a[i];  // decay row
+            s[i] *= gate_exp(ga[i]);  // decay row
             pk += s[i] * kr[i];
             pq += s[i] * qr[i];
             qk += qr[i] * kr[i];
         }
+        fetch_qg(tn);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            red_k[buf][rg][4 * c4 + c] = pk[c];
-            red_q[buf][rg][4 * c4 + c] = pq[c];
+            pk[c] = sum_row_groups<TPR>(pk[c]);
+            pq[c] = sum_row_groups<TPR>(pq[c]);
         }
-        if (c4 == 0) red_qk[buf][rg] = qk;
-        f32x4 vt;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) vt[c] = ld(v, tv * DV + 4 * c4 + c);
-        const float bt = beta[tv];
-        if (t + 1 < T) fetch(t + 1, nk, nq, na);
-        __syncthreads();
-
-        f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
-        float qk_all = 0.f;
-#pragma unroll
-        for (int x = 0; x < RGS; ++x) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                sk[c] += red_k[buf][x][4 * c4 + c];
-                sq[c] += red_q[buf][x][4 * c4 + c];
-            }
-            qk_all += red_qk[buf][x];
-        }
-        const f32x4 u = bt * (vt - sk);
+        qk = sum_row_groups<TPR>(qk);
+        const f32x4 u = bt * (vt - pk);
 #pragma unroll
         for (int i = 0; i < R; ++i) s[i] += kr[i] * u;  // rank-1 write
-        if (rg == 0) {
+        if (l < TPR) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) st(o, tv * DV + 4 * c4 + c, scale * (sq[c] + qk_all * u[c]));
-        }
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            kr[i] = nk[i];
-            qr[i] = nq[i];
-            a[i] = na[i];
+            for (int c = 0; c < 4; ++c) st(o, tv * DV + col + c, scale * (pq[c] + qk * u[c]));
         }
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-        __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (rg + RGS * i) * DV) + c4);
+    for (int i = 0; i < R; ++i) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (r0 + i) * DV));
 }
 
 template <int DK, int DV, typename Tin, typename Tout>
 static hipError_t launch_steps_t(const DecodeArgs& a) {
-    const int64_t blocks = static_cast<int64_t>(a.N) * a.H;
-    hipLaunchKernelGGL((steps_kernel<DK, DV, Tin, Tout>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(DecodeShape<DK, DV>::THREADS), 0, a.stream,
-                       static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
+    constexpr int NCB = DV / (DV < 32 ? DV : 32);
+    const int64_t items = static_cast<int64_t>(a.N) * a.H * NCB;
+    hipLaunchKernelGGL((steps_kernel<DK, DV, Tin, Tout>), dim3(static_cast<uint32_t>((items + 3) / 4)),
+                       dim3(256), 0, a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
                        static_cast<const Tin*>(a.v), a.g, a.beta, a.scale, a.state,
-                       static_cast<Tout*>(a.o), a.T, a.H);
+                       static_cast<Tout*>(a.o), a.T, a.H, items);
     return hipGetLastError();
 }
 
