@@ -392,6 +392,73 @@ def test_fused_gate_full_size_sampled_rows():
     assert bool(torch.isfinite(g).all()) and bool((g < 0).all())
 
 
+def test_many_sequences_beyond_ordering_limit():
+    say("20000 short sequences (lengths 0..64), H=2: past the longest-first ordering limit")
+    rng = np.random.default_rng(31)
+    lens = rng.integers(0, 65, size=20000)
+    x = synth.make_inputs("varlen", lens=lens, H=2)
+    o, f = run_prefill(x)
+    o_ref, f_ref = oracle_prefill(x)
+    assert_parity(o, o_ref, x.q.dtype, "o")
+    assert_parity(f, f_ref, x.q.dtype, "final")
+    empty = np.flatnonzero(lens == 0)
+    assert torch.equal(f[torch.as_tensor(empty)].cpu(), x.h0[torch.as_tensor(empty)])
+
+
+def test_scan_and_snapshots_over_many_sequence_blocks():
+    say("segment scan + snapshots with 300 sequences (several 256-sequence plan blocks), H=2")
+    rng = np.random.default_rng(32)
+    lens = rng.integers(1, 90, size=300)
+    lens[[3, 150, 257, 299]] = [3000, 2100, 1500, 2600]
+    x = synth.make_inputs("varlen", lens=lens, H=2)
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    kda = _kda()
+    o, f, sn = kda.chunk_fwd_snapshots(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, 512,
+                                       initial_state=xd.h0, cu_seqlens=x.cu_seqlens,
+                                       variant="chunk_scan")
+    torch.cuda.synchronize()
+    o_ref, f_ref = oracle_prefill(x)
+    assert_parity(o, o_ref, x.q.dtype, "o")
+    assert_parity(f, f_ref, x.q.dtype, "final")
+    rows = kda.snapshot_rows(lens, 512)
+    for n in (3, 150, 257, 299):
+        a = int(x.cu_seqlens[n])
+        for j in range(int(rows[n + 1] - rows[n])):
+            sl = slice(a, a + 512 * (j + 1))
+            _, fr = cref.kda_forward(x.q[:, sl], x.k[:, sl], x.v[:, sl], x.g[:, sl], x.beta[:, sl],
+                                     x.scale, x.h0[n:n + 1], None, n_threads=THREADS)
+            assert_parity(sn[rows[n] + j], fr[0], x.q.dtype, f"snapshot {j} of sequence {n}")
+
+
+def test_many_heads():
+    say("H=96 (the largest head count the pages mention), T=300")
+    x = synth.make_inputs("prefill", T=300, H=96)
+    o, f = run_prefill(x)
+    o_ref, f_ref = oracle_prefill(x)
+    assert_parity(o, o_ref, x.q.dtype, "o")
+    assert_parity(f, f_ref, x.q.dtype, "final")
+
+
+@pytest.mark.parametrize("variant", ["chunk", "chunk_scan", "recurrent"])
+def test_no_decay_no_write_keeps_state(variant):
+    say(f"g = 0 and beta = 0: the state is untouched and o = scale S0^T q ({variant})")
+    x = synth.make_inputs("prefill", T=1100, H=2)
+    dev = torch.device("cuda")
+    g0 = torch.zeros_like(x.g)
+    b0 = torch.zeros_like(x.beta)
+    o, f = _kda().chunk_fwd(x.q.to(dev), x.k.to(dev), x.v.to(dev), g0.to(dev), b0.to(dev), x.scale,
+                            x.h0.to(dev), variant=variant)
+    torch.cuda.synchronize()
+    if variant == "chunk_scan":
+        # the scan composes segment maps (identities here) in split bf16, ~16 significant bits
+        assert max_abs(f, x.h0) <= 1e-5 * float(x.h0.abs().max())
+    else:
+        assert torch.equal(f.cpu(), x.h0)  # alpha = 1 and no write leave every value exact
+    o_ref = x.scale * np.einsum("hkv,bthk->bthv", x.h0[0].double().numpy(), x.q.double().numpy())
+    assert_parity(o, o_ref, x.q.dtype, "o")
+
+
 def test_prefill_then_decode_equals_prefill():
     say("prefill T-1 then decode == prefill T (H=4, T=300)")
     x = synth.make_inputs("prefill", T=300, H=4)
