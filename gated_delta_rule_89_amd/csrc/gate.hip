@@ -22,7 +22,7 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-constexpr int ROWS = 64;   // rows of z per wave
+constexpr int ROWS = 32;   // rows of z per wave
 constexpr int DK = 128;    // key channels per head
 
 __device__ __forceinline__ float neg_softplus(float x) {
@@ -32,7 +32,7 @@ __device__ __forceinline__ float neg_softplus(float x) {
     return -(fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + t) * LN2);
 }
 
-// One wave per (64 rows of z, head): its MFMA fragments come straight from
+// One wave per (32 rows of z, head): its MFMA fragments come straight from
 // global memory (z rows and W rows are both contiguous along j; W is small
 // and stays in L2), so there is no LDS staging and no barrier.  A workgroup
 // holds the 4 waves of 4 consecutive heads over the same rows, which share
