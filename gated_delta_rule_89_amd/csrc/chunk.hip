@@ -871,78 +871,76 @@ void chunk_ws_kernel(
     // outstanding loads exactly and never waits for the prefetch of chunk
     // c + 2 before it is consumed.
     if (gate) {
-    // ---- gate waves: sub-block I, channel part `part`; raw inputs fetched ahead
-    const int gw = w - NSW;
-    const int I = gw / NP, part = gw % NP;
-    const int gtid = tid - NSW * 64;
-    const int tok = SB * I + r;
-    u4 kw[KS], qw[KS], vp[VU], gp_[VU];
-    f4 ga[KS], gb[KS];
-    float bt = 0.f;
-    // Tokens at or past the end of the sequence lie outside the buffer range
-    // of the chunk (valid tokens x row bytes), so their loads return zeros.
-    auto valid_at = [&](int64_t cs) {
-        const int64_t n = t1 - cs;
-        return static_cast<uint32_t>(n < 0 ? 0 : n < C ? n : C);
-    };
-    auto fetch_gate = [&](int64_t cs) {  // k, q, g, beta of this lane's token
-        const uint32_t vld = valid_at(cs);
-        const int64_t cb = (cs * H + h) * D;
-        const auto rk = rsrc(k + cb, vld * rowe * 2);
-        const auto rq = rsrc(q + cb, vld * rowe * 2);
-        const auto rg = rsrc(g + cb, vld * rowe * 4);
-        const auto rb = rsrc(beta + cs * H + h, vld * H * 4);
+        // ---- gate waves: sub-block I, channel part `part`; raw inputs fetched ahead
+        const int gw = w - NSW;
+        const int I = gw / NP, part = gw % NP;
+        const int gtid = tid - NSW * 64;
+        const int tok = SB * I + r;
+        u4 kw[KS], qw[KS], vp[VU], gp_[VU];
+        f4 ga[KS], gb[KS];
+        float bt = 0.f;
+        // Tokens at or past the end of the sequence lie outside the buffer range
+        // of the chunk (valid tokens x row bytes), so their loads return zeros.
+        auto valid_at = [&](int64_t cs) {
+            const int64_t n = t1 - cs;
+            return static_cast<uint32_t>(n < 0 ? 0 : n < C ? n : C);
+        };
+        auto fetch_gate = [&](int64_t cs) {  // k, q, g, beta of this lane's token
+            const uint32_t vld = valid_at(cs);
+            const int64_t cb = (cs * H + h) * D;
+            const auto rk = rsrc(k + cb, vld * rowe * 2);
+            const auto rq = rsrc(q + cb, vld * rowe * 2);
+            const auto rg = rsrc(g + cb, vld * rowe * 4);
+            const auto rb = rsrc(beta + cs * H + h, vld * H * 4);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
-            kw[ks] = bload16(rk, 2 * off);
-            qw[ks] = bload16(rq, 2 * off);
-            const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
-            ga[ks] = f4{__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]), __uint_as_float(a0[3])};
-            gb[ks] = f4{__uint_as_float(a1[0]), __uint_as_float(a1[1]), __uint_as_float(a1[2]), __uint_as_float(a1[3])};
-        }
-        bt = bload4(rb, 4 * tok * H);
-    };
-    auto fetch_v = [&](int64_t cs) {  // v (and the output gate) in the staging layout
-        const auto rv = rsrc(v + (cs * H + h) * D, valid_at(cs) * rowe * 2);
-        const auto rog = rsrc(ogate + (cs * H + h) * D, GATED ? valid_at(cs) * rowe * 2 : 0u);
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
+                kw[ks] = bload16(rk, 2 * off);
+                qw[ks] = bload16(rq, 2 * off);
+                const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
+                ga[ks] = f4{__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]), __uint_as_float(a0[3])};
+                gb[ks] = f4{__uint_as_float(a1[0]), __uint_as_float(a1[1]), __uint_as_float(a1[2]), __uint_as_float(a1[3])};
+            }
+            bt = bload4(rb, 4 * tok * H);
+        };
+        auto fetch_v = [&](int64_t cs) {  // v (and the output gate) in the staging layout
+            const auto rv = rsrc(v + (cs * H + h) * D, valid_at(cs) * rowe * 2);
+            const auto rog = rsrc(ogate + (cs * H + h) * D, GATED ? valid_at(cs) * rowe * 2 : 0u);
 #pragma unroll
-        for (int j = 0; j < VU; ++j) {
-            const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
-            vp[j] = bload16(rv, 2 * (vt * rowe + vc));
-            if (GATED) gp_[j] = bload16(rog, 2 * (vt * rowe + vc));
-        }
-    };
-    fetch_gate(t0);
-    fetch_v(t0);
-    h8 l16[KS], q16[KS], rb16[KS];  // gate registers carried from phase 1 to phase 2
+            for (int j = 0; j < VU; ++j) {
+                const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
+                vp[j] = bload16(rv, 2 * (vt * rowe + vc));
+                if (GATED) gp_[j] = bload16(rog, 2 * (vt * rowe + vc));
+            }
+        };
+        fetch_gate(t0);
+        fetch_v(t0);
+        h8 l16[KS], q16[KS], rb16[KS];  // gate registers carried from phase 1 to phase 2
 
         for (int c = -1; c < nch; ++c) {
             const bool gwork = c + 1 < nch;   // prepare chunk c + 1
-            const int64_t c0 = t0 + static_cast<int64_t>(c) * C;
-            const Tiles& cur = sm.tl[c & 1];
             Tiles& nxt = sm.tl[(c + 1) & 1];
 
             if (gwork) {
                 constexpr float LOG2E = 1.4426950408889634f;
                 constexpr float FAST_SPAN = 8.f * LOG2E;
                 f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int ch = CPG * part + 32 * ks + 8 * g4;
                     float kf[8], qf[8], G[8], Gt[8];
                     unpack_bf16x8(kw[ks], kf);
                     unpack_bf16x8(qw[ks], qf);
-    #pragma unroll
+#pragma unroll
                     for (int m = 0; m < 8; ++m) G[m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
-    #pragma unroll
+#pragma unroll
                     for (int m = 0; m < 8; ++m) Gt[m] = row_bcast16<15>(G[m]);
                     // Factors referenced to half the sub-block total: a = exp(G - tot/2),
                     // 1/a, and the channel's exp(tot/2), which is a at the last token.
                     // exp(G) = a exp(tot/2) and exp(tot - G) = exp(tot/2) / a.
                     float xa[8], La[8], Ra[8], Qa[8], hh[8];
                     float span = 0.f;
-    #pragma unroll
+#pragma unroll
                     for (int m = 0; m < 8; ++m) {
                         xa[m] = fmaf(-0.5f, Gt[m], G[m]);
                         span = fmaxf(span, fabsf(xa[m]));
@@ -953,7 +951,7 @@ void chunk_ws_kernel(
                         Qa[m] = qf[m] * a;
                         hh[m] = row_bcast16<15>(a);
                     }
-    #pragma unroll
+#pragma unroll
                     for (int m = 0; m < 8; ++m) {
                         l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G)
                         rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
@@ -961,7 +959,7 @@ void chunk_ws_kernel(
                     }
                     if (!__any(span > FAST_SPAN)) {
                         h8 la, ra, qa;
-    #pragma unroll
+#pragma unroll
                         for (int m = 0; m < 8; ++m) {
                             la[m] = static_cast<_Float16>(La[m]);
                             ra[m] = static_cast<_Float16>(Ra[m]);
@@ -970,7 +968,7 @@ void chunk_ws_kernel(
                         accA = mfma16(la, ra, accA);
                         accP = mfma16(qa, ra, accP);
                     } else {
-    #pragma unroll
+#pragma unroll
                         for (int m = 0; m < 8; ++m) {
                             accA = mfma4(La[m], Ra[m], accA);
                             accP = mfma4(Qa[m], Ra[m], accP);
@@ -984,7 +982,7 @@ void chunk_ws_kernel(
                     }
                     if (I == 0) *reinterpret_cast<h8*>(&sm.rbs[r][ch]) = rb16[ks];
                 }
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
                     sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
@@ -995,7 +993,7 @@ void chunk_ws_kernel(
             __syncthreads();
             if (gwork) {
                 f4 a10 = {0.f, 0.f, 0.f, 0.f}, p10 = {0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int ch = CPG * part + 32 * ks + 8 * g4;
                     const f4 oa = *reinterpret_cast<const f4*>(&sm.etot[1 - I][ch]);
@@ -1017,7 +1015,7 @@ void chunk_ws_kernel(
                     *reinterpret_cast<h4*>(&nxt.qt[tok][p0]) = __builtin_shufflevector(qv, qv, 0, 1, 2, 3);
                     *reinterpret_cast<h4*>(&nxt.qt[tok][p1]) = __builtin_shufflevector(qv, qv, 4, 5, 6, 7);
                     const int tp = kpos(tok);
-    #pragma unroll
+#pragma unroll
                     for (int m = 0; m < 8; ++m) nxt.kbt[ch + m][tp] = bv[m];
                     if (I == 1) {
                         const h8 rv = *reinterpret_cast<const h8*>(&sm.rbs[r][ch]);
@@ -1026,7 +1024,7 @@ void chunk_ws_kernel(
                     }
                 }
                 if (I == 1) {
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         sm.gp[part][2 * NSB][4 * g4 + i][r] = a10[i];
                         sm.gp[part][2 * NSB + 1][4 * g4 + i][r] = p10[i];
@@ -1036,11 +1034,11 @@ void chunk_ws_kernel(
                 for (int e = gtid; e < NSB * SB * SB; e += GT) {
                     const int J = e >> 8, i = (e >> 4) & 15, m = e & 15;
                     float s = 0.f;
-    #pragma unroll
+#pragma unroll
                     for (int pp = 0; pp < NP; ++pp) s += sm.gp[pp][2 * J][i][m];
                     sm.a[J][i][m] = m < i ? s * sm.beta[SB * J + i] : 0.f;  // A_JJ, strictly lower
                 }
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < VU; ++j) {
                     const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
                     *reinterpret_cast<u4*>(&nxt.v[vt][vc]) = vp[j];
@@ -1095,32 +1093,32 @@ void chunk_ws_kernel(
                         }
                     }
                 }
-        }
+            }
             __syncthreads();
         }
     } else {
-    // ---- state waves: S[16 rt + 4 g4 + i][col + 16 ct + r] * 2^ex in S[rt][ct][i]
-    const int col = 32 * (w & 3);
-    f4 S[8][NCT];
-    int ex = 0;
-    h8 d16[NCT];      // fp16 Delta (B operand of P Delta, K-bar^T Delta), chunk-local
-    {
-        const float* src = nullptr;
-        if (it.sin >= 0 && h0) src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
-        else if (it.sin <= -2) src = staged + (static_cast<int64_t>(-it.sin - 2) * H + h) * D * D;
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
-        if (src) {
+        // ---- state waves: S[16 rt + 4 g4 + i][col + 16 ct + r] * 2^ex in S[rt][ct][i]
+        const int col = 32 * (w & 3);
+        f4 S[8][NCT];
+        int ex = 0;
+        h8 d16[NCT];      // fp16 Delta (B operand of P Delta, K-bar^T Delta), chunk-local
+        {
+            const float* src = nullptr;
+            if (it.sin >= 0 && h0) src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
+            else if (it.sin <= -2) src = staged + (static_cast<int64_t>(-it.sin - 2) * H + h) * D * D;
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
+                for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+            if (src) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
+                for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
+            }
         }
-    }
         // Operands of the next chunk's state pass, prepared right after the
         // previous S update (its v tile is in LDS by then): v, the scale
         // exponent, and fp16 S (B operand of both K~ S and Q~ S).
@@ -1128,41 +1126,41 @@ void chunk_ws_kernel(
         h8 s16[4][NCT];
         float sig = 1.f;
         auto prepare = [&](const Tiles& t) {
-    #pragma unroll
+#pragma unroll
             for (int rt = 0; rt < NSB; ++rt)
-    #pragma unroll
+#pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i)
                         vv[rt][ct][i] = bf16_to_f32(t.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
             float mv = 0.f, ms = 0.f;
-    #pragma unroll
+#pragma unroll
             for (int rt = 0; rt < NSB; ++rt)
-    #pragma unroll
+#pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(vv[rt][ct][i]));
-    #pragma unroll
+#pragma unroll
             for (int rt = 0; rt < 8; ++rt)
-    #pragma unroll
+#pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[rt][ct][i]));
             const int nex = value_exponent(wave_max_nonneg(fmaxf(ms * ldexpf(1.f, -ex), mv)), ex);
             if (nex != ex) {
                 const float f = ldexpf(1.f, nex - ex);
-    #pragma unroll
+#pragma unroll
                 for (int rt = 0; rt < 8; ++rt)
-    #pragma unroll
+#pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= f;
                 ex = nex;
             }
             sig = ldexpf(1.f, ex);
-    #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-    #pragma unroll
+#pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
-    #pragma unroll
+#pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         s16[ks][ct][m] = static_cast<_Float16>(S[2 * ks][ct][m]);
                         s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
@@ -1188,39 +1186,39 @@ void chunk_ws_kernel(
             const int valid = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
             if (swork) {
                 f4 y[NSB][NCT];
-    #pragma unroll
+#pragma unroll
                 for (int rt = 0; rt < NSB; ++rt) {
-    #pragma unroll
+#pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) y[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
-    #pragma unroll
+#pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
                         const h8 kf8 = *reinterpret_cast<const h8*>(&cur.kt[16 * rt + r][32 * ks + 8 * g4]);
-    #pragma unroll
+#pragma unroll
                         for (int ct = 0; ct < NCT; ++ct) y[rt][ct] = mfma16(kf8, s16[ks][ct], y[rt][ct]);
                     }
                 }
                 const h4 t00 = *reinterpret_cast<const h4*>(&cur.tb[0][r][4 * g4]);
                 const h4 t11 = *reinterpret_cast<const h4*>(&cur.tb[1][r][4 * g4]);
                 const h4 g10 = *reinterpret_cast<const h4*>(&cur.tb[2][r][4 * g4]);
-    #pragma unroll
+#pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
                     h4 x0;
                     f4 x1;
-    #pragma unroll
+#pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         x0[m] = static_cast<_Float16>(fmaf(vv[0][ct][m], sig, -y[0][ct][m]));
                         x1[m] = fmaf(vv[1][ct][m], sig, -y[1][ct][m]);
                     }
                     const f4 d0 = mfma16k16(t00, x0, f4{0.f, 0.f, 0.f, 0.f});
                     h4 d0h;
-    #pragma unroll
+#pragma unroll
                     for (int m = 0; m < 4; ++m) d0h[m] = static_cast<_Float16>(d0[m]);
                     const f4 z = mfma16k16(g10, d0h, x1);
                     h4 zh;
-    #pragma unroll
+#pragma unroll
                     for (int m = 0; m < 4; ++m) zh[m] = static_cast<_Float16>(z[m]);
                     const f4 d1 = mfma16k16(t11, zh, f4{0.f, 0.f, 0.f, 0.f});
-    #pragma unroll
+#pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         d16[ct][m] = d0h[m];
                         d16[ct][4 + m] = static_cast<_Float16>(d1[m]);
@@ -1231,28 +1229,28 @@ void chunk_ws_kernel(
                 const int vlim = valid - 4 * g4;  // rows of this lane group still inside the chunk
                 const auto ro = rsrc(o + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * sizeof(Tout));
                 const int vo = static_cast<int>(((4 * g4) * rowe + col + r) * sizeof(Tout));
-    #pragma unroll
+#pragma unroll
                 for (int rt = 0; rt < NSB; ++rt) {
                     h8 qf8[4];
-    #pragma unroll
+#pragma unroll
                     for (int ks = 0; ks < 4; ++ks)
                         qf8[ks] = *reinterpret_cast<const h8*>(&cur.qt[16 * rt + r][32 * ks + 8 * g4]);
                     const h8 pf = *reinterpret_cast<const h8*>(&cur.p[16 * rt + r][8 * g4]);
-    #pragma unroll
+#pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) {
                         f4 a = mfma16(pf, d16[ct], f4{0.f, 0.f, 0.f, 0.f});
-    #pragma unroll
+#pragma unroll
                         for (int ks = 0; ks < 4; ++ks) a = mfma16(qf8[ks], s16[ks][ct], a);
                         const int voc = vo + static_cast<int>(16 * ct * sizeof(Tout));
                         if (GATED) {
-    #pragma unroll
+#pragma unroll
                             for (int i = 0; i < 4; ++i) sm.otile[16 * rt + 4 * g4 + i][col + 16 * ct + r] = a[i] * os;
                         } else if (valid == C) {
-    #pragma unroll
+#pragma unroll
                             for (int i = 0; i < 4; ++i)
                                 bstore(ro, voc, static_cast<int>((16 * rt + i) * rowe * sizeof(Tout)), a[i] * os, o);
                         } else {
-    #pragma unroll
+#pragma unroll
                             for (int i = 0; i < 4; ++i)
                                 if (16 * rt + i < vlim)
                                     bstore(ro, voc, static_cast<int>((16 * rt + i) * rowe * sizeof(Tout)), a[i] * os, o);
@@ -1262,11 +1260,11 @@ void chunk_ws_kernel(
             }
             __syncthreads();
             if (swork) {
-    #pragma unroll
+#pragma unroll
                 for (int rt = 0; rt < 8; ++rt) {
                     const f4 lam = *reinterpret_cast<const f4*>(&cur.lam[16 * rt + 4 * g4]);
                     const h8 kb8 = *reinterpret_cast<const h8*>(&cur.kbt[16 * rt + r][8 * g4]);
-    #pragma unroll
+#pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb8, d16[ct], S[rt][ct] * lam);
                 }
                 if (GATED) {
@@ -1274,7 +1272,7 @@ void chunk_ws_kernel(
                     // two passes over the LDS row keep few values live.
                     const int el = epi_lane(), erow = 8 * (w & 3) + (el >> 3), ecol = 16 * (el & 7);
                     float ss = 0.f;
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const f4 x = *reinterpret_cast<const f4*>(&sm.otile[erow][ecol + 4 * j]);
                         ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
@@ -1285,16 +1283,16 @@ void chunk_ws_kernel(
                     const float rinv = __builtin_amdgcn_rsqf(ss * (1.f / D) + neps);
                     const auto ro = rsrc(o + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * sizeof(Tout));
                     const int vo = (erow * rowe + ecol) * static_cast<int>(sizeof(Tout));
-    #pragma unroll
+#pragma unroll
                     for (int j2 = 0; j2 < 2; ++j2) {  // 8 channels per step
                         float gf[8], yv[8];
                         unpack_bf16x8(*reinterpret_cast<const u4*>(&cur.og[erow][ecol + 8 * j2]), gf);
-    #pragma unroll
+#pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
                             const int c4 = ecol + 8 * j2 + 4 * jj;
                             const f4 x = *reinterpret_cast<const f4*>(&sm.otile[erow][c4]);
                             const f4 wv = *reinterpret_cast<const f4*>(&sm.nw[c4]);
-    #pragma unroll
+#pragma unroll
                             for (int e = 0; e < 4; ++e) yv[4 * jj + e] = x[e] * rinv * wv[e] * gf[4 * jj + e];
                         }
                         store8(ro, vo + 8 * j2 * static_cast<int>(sizeof(Tout)), yv, o);
@@ -1313,11 +1311,11 @@ void chunk_ws_kernel(
         if (it.sout >= 0 && out_state) {
             const float un = ldexpf(1.f, -ex);
             float* dst = out_state + (static_cast<int64_t>(it.sout) * H + h) * D * D;
-    #pragma unroll
+#pragma unroll
             for (int rt = 0; rt < 8; ++rt)
-    #pragma unroll
+#pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i)
                         dst[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] = S[rt][ct][i] * un;
         }
