@@ -10,8 +10,11 @@
 // W is [H d_k, r] (a linear layer's weight, output rows): every MFMA operand
 // fragment, 8 consecutive j of one row of z or of W, is one 16-byte read.
 // The up-projection is a dense contraction (M x r by r x H d_k), so it runs
-// on bf16 MFMA (16x16x32, fp32 accumulation).  The write of g (4 bytes per
-// element) dominates the traffic: the kernel is bound by HBM writes.
+// on bf16 MFMA (16x16x32, fp32 accumulation), computed transposed (W as the
+// A operand, z as B) so that each lane ends with 4 consecutive channels of
+// one token: the g tile is written with 16-byte stores.  The write of g
+// (4 bytes per element) dominates the traffic: the kernel is bound by HBM
+// writes.
 #include "dev_common.h"
 #include "kda_internal.h"
 
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(256) void fused_gate_kernel(const uint16_t* __restr
             if (idx < M * H) beta[idx] = 1.f / (1.f + __builtin_amdgcn_exp2f(-u[idx] * 1.4426950408889634f));
         }
     }
-    f4 acc[RT][DK / 16];
+    f4 acc[RT][DK / 16];  // acc[rt][ct]: channels 16 ct + 4 g4 + i of token 16 rt + r16
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -63,35 +66,37 @@ __global__ __launch_bounds__(256) void fused_gate_kernel(const uint16_t* __restr
     const uint16_t* wh = w + static_cast<int64_t>(h) * DK * R;
 #pragma unroll
     for (int ks = 0; ks < R / 32; ++ks) {
-        b8 a[RT];
+        b8 zf[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int64_t m = m0 + 16 * rt + r16;
             u4 val = {0, 0, 0, 0};
             if (m < M) val = *reinterpret_cast<const u4*>(z + m * R + 32 * ks + 8 * g4);
-            a[rt] = __builtin_bit_cast(b8, val);
+            zf[rt] = __builtin_bit_cast(b8, val);
         }
 #pragma unroll
         for (int ct = 0; ct < DK / 16; ++ct) {
-            const b8 bf = __builtin_bit_cast(
+            const b8 wf = __builtin_bit_cast(
                 b8, *reinterpret_cast<const u4*>(wh + (16 * ct + r16) * R + 32 * ks + 8 * g4));
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rt], bf, acc[rt][ct], 0, 0, 0);
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, zf[rt], acc[rt][ct], 0, 0, 0);
         }
     }
-    // D layout: lane holds rows 4 g4 + i of each 16 x 16 tile, column r16
+    // D layout of the transposed product: lane holds rows 4 g4 + i (channels)
+    // of column r16 (token) of each 16 x 16 tile
 #pragma unroll
     for (int ct = 0; ct < DK / 16; ++ct) {
-        const int c = 16 * ct + r16;
-        const float bc = bias ? bias[h * DK + c] : 0.f;
+        const int c = 16 * ct + 4 * g4;
+        const f4 bc = bias ? *reinterpret_cast<const f4*>(bias + h * DK + c) : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt) {
+            const int64_t m = m0 + 16 * rt + r16;
+            f4 out;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t m = m0 + 16 * rt + 4 * g4 + i;
-                if (m < M) __builtin_nontemporal_store(neg_softplus(acc[rt][ct][i] + bc), &g[m * N + h * DK + c]);
-            }
+            for (int i = 0; i < 4; ++i) out[i] = neg_softplus(acc[rt][ct][i] + bc[i]);
+            if (m < M) __builtin_nontemporal_store(out, reinterpret_cast<f4*>(g + m * N + h * DK + c));
+        }
     }
 }
 
