@@ -161,6 +161,20 @@ __device__ __forceinline__ void subst_all(float (&x)[4], const f4 (&arow)[4], st
     (subst_step<M>(x, arow), ...);
 }
 
+// The same step for two columns, and steps M0 .. M0 + n - 1.
+template <int M>
+__device__ __forceinline__ void subst_step2(float (&x)[2], const f4 (&arow)[4]) {
+    float xb[2];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) xb[qq] = row_bcast16<M>(x[qq]);
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) x[qq] = fmaf(-arow[M >> 2][M & 3], xb[qq], x[qq]);
+}
+template <int M0, int... M>
+__device__ __forceinline__ void subst_range2(float (&x)[2], const f4 (&arow)[4], std::integer_sequence<int, M...>) {
+    (subst_step2<M0 + M>(x, arow), ...);
+}
+
 // Inclusive prefix sum over the 16 lanes of a DPP row.
 __device__ __forceinline__ float row_scan16(float x) {
     x += row_shr<1>(x);
@@ -215,6 +229,18 @@ __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, int voff, const
 }
 __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, int voff, int soff, float x, bf16_t*) {
     __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), r, voff, soff, 0);
+}
+
+// 4 consecutive outputs of one lane as one buffer store (16 bytes fp32, 8 bytes bf16).
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, int voff, f4 y, float*) {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u4{__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])}, r, voff, 0, 0);
+}
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, int voff, f4 y, bf16_t*) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 p = {static_cast<uint32_t>(f32_to_bf16(y[0])) | (static_cast<uint32_t>(f32_to_bf16(y[1])) << 16),
+                  static_cast<uint32_t>(f32_to_bf16(y[2])) | (static_cast<uint32_t>(f32_to_bf16(y[3])) << 16)};
+    __builtin_amdgcn_raw_buffer_store_b64(p, r, voff, 0, 0);
 }
 
 __device__ __forceinline__ h8 cat(h4 a, h4 b) {
@@ -817,6 +843,7 @@ constexpr int NP = NGW / NSB;  // channel parts per sub-block (gate waves per su
 constexpr int CPG = D / NP, KS = CPG / 32;
 constexpr int GT = NGW * 64;            // gate threads
 constexpr int VU = (C * D / 8) / GT;    // 16-byte pieces of the v tile per gate thread
+constexpr bool STAGE_O = true;          // o goes through an LDS tile and leaves as whole rows
 
 struct alignas(16) Tiles {               // operands of one chunk's state pass
     _Float16 qt[C][QP];                  // Q~   [token][channel, operand order]
@@ -915,26 +942,42 @@ void chunk_ws_kernel(
         };
         fetch_gate(t0);
         fetch_v(t0);
+        // P01 (tokens of sub-block 0 against sub-block 1) is zero in every chunk:
+        // written once into both operand sets, never touched again.
+        for (int e = gtid; e < 2 * SB * SB; e += GT)
+            sm.tl[e >> 8].p[(e >> 4) & 15][kpos(SB + (e & 15))] = static_cast<_Float16>(0.f);
         h8 l16[KS], q16[KS], rb16[KS];  // gate registers carried from phase 1 to phase 2
 
         for (int c = -1; c < nch; ++c) {
             const bool gwork = c + 1 < nch;   // prepare chunk c + 1
             Tiles& nxt = sm.tl[(c + 1) & 1];
 
+            constexpr float LOG2E = 1.4426950408889634f;
+            // The raw inputs of chunk c + 1 are unpacked first (cumulative
+            // gates included), so the fetch of chunk c + 2 into the same
+            // registers is issued early in the phase, not behind its work.
+            float kf[KS][8], qf[KS][8], G[KS][8];
             if (gwork) {
-                constexpr float LOG2E = 1.4426950408889634f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    unpack_bf16x8(kw[ks], kf[ks]);
+                    unpack_bf16x8(qw[ks], qf[ks]);
+#pragma unroll
+                    for (int m = 0; m < 8; ++m)
+                        G[ks][m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
+                }
+                if (part == 0 && g4 == 0) sm.beta[tok] = bt;
+            }
+            fetch_gate(t0 + static_cast<int64_t>(c + 2) * C);
+            if (gwork) {
                 constexpr float FAST_SPAN = 8.f * LOG2E;
                 f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int ch = CPG * part + 32 * ks + 8 * g4;
-                    float kf[8], qf[8], G[8], Gt[8];
-                    unpack_bf16x8(kw[ks], kf);
-                    unpack_bf16x8(qw[ks], qf);
+                    float Gt[8];
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) G[m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) Gt[m] = row_bcast16<15>(G[m]);
+                    for (int m = 0; m < 8; ++m) Gt[m] = row_bcast16<15>(G[ks][m]);
                     // Factors referenced to half the sub-block total: a = exp(G - tot/2),
                     // 1/a, and the channel's exp(tot/2), which is a at the last token.
                     // exp(G) = a exp(tot/2) and exp(tot - G) = exp(tot/2) / a.
@@ -942,13 +985,13 @@ void chunk_ws_kernel(
                     float span = 0.f;
 #pragma unroll
                     for (int m = 0; m < 8; ++m) {
-                        xa[m] = fmaf(-0.5f, Gt[m], G[m]);
+                        xa[m] = fmaf(-0.5f, Gt[m], G[ks][m]);
                         span = fmaxf(span, fabsf(xa[m]));
                         const float a = __builtin_amdgcn_exp2f(xa[m]);
                         const float ia = __builtin_amdgcn_exp2f(-xa[m]);
-                        La[m] = kf[m] * a;
-                        Ra[m] = kf[m] * ia;
-                        Qa[m] = qf[m] * a;
+                        La[m] = kf[ks][m] * a;
+                        Ra[m] = kf[ks][m] * ia;
+                        Qa[m] = qf[ks][m] * a;
                         hh[m] = row_bcast16<15>(a);
                     }
 #pragma unroll
@@ -987,10 +1030,17 @@ void chunk_ws_kernel(
                     sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
                     sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
                 }
-                if (part == 0 && g4 == 0) sm.beta[tok] = bt;
             }
-            fetch_gate(t0 + static_cast<int64_t>(c + 2) * C);
             __syncthreads();
+            if (gwork) {  // v (and the output gate) of chunk c + 1 first, then the fetch of c + 2
+#pragma unroll
+                for (int j = 0; j < VU; ++j) {
+                    const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
+                    *reinterpret_cast<u4*>(&nxt.v[vt][vc]) = vp[j];
+                    if (GATED) *reinterpret_cast<u4*>(&nxt.og[vt][vc]) = gp_[j];
+                }
+            }
+            fetch_v(t0 + static_cast<int64_t>(c + 2) * C);
             if (gwork) {
                 f4 a10 = {0.f, 0.f, 0.f, 0.f}, p10 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1038,59 +1088,49 @@ void chunk_ws_kernel(
                     for (int pp = 0; pp < NP; ++pp) s += sm.gp[pp][2 * J][i][m];
                     sm.a[J][i][m] = m < i ? s * sm.beta[SB * J + i] : 0.f;  // A_JJ, strictly lower
                 }
-#pragma unroll
-                for (int j = 0; j < VU; ++j) {
-                    const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
-                    *reinterpret_cast<u4*>(&nxt.v[vt][vc]) = vp[j];
-                    if (GATED) *reinterpret_cast<u4*>(&nxt.og[vt][vc]) = gp_[j];
-                }
             }
-            fetch_v(t0 + static_cast<int64_t>(c + 2) * C);
             __syncthreads();
             if (gwork) {
-                if (gw < NSB) {
-                    // Column-oriented substitution for T = (I + A_JJ)^-1: lane
-                    // (i, g4) holds row i of columns 4 g4 .. 4 g4 + 3 and row i of
-                    // A (zero on and above the diagonal).  Step m broadcasts x_m of
-                    // each column across its 16-lane row (DPP) and updates every
-                    // row at once: x_i -= A[i][m] x_m.
-                    const int J = gw;
+                if (gw < 2 * NSB) {
+                    // Column-oriented substitution for T = (I + A_JJ)^-1, two waves
+                    // per block: columns 8 hh .. 8 hh + 7.  Lane (i, g4) holds row i
+                    // of columns 8 hh + 2 g4 + {0, 1} and row i of A (zero on and
+                    // above the diagonal).  Step m broadcasts x_m of each column
+                    // across its 16-lane row (DPP) and updates every row at once:
+                    // x_i -= A[i][m] x_m.  Column j has x_m = 0 for m < j, so the
+                    // right half starts at step 8; step 15 changes nothing.
+                    const int J = gw >> 1, hh = gw & 1;
                     f4 arow[4];
 #pragma unroll
                     for (int cc = 0; cc < 4; ++cc) arow[cc] = *reinterpret_cast<const f4*>(&sm.a[J][r][4 * cc]);
-                    const f4 bcol = *reinterpret_cast<const f4*>(&sm.beta[SB * J + 4 * g4]);
-                    float x[4];
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) x[qq] = (r == 4 * g4 + qq) ? 1.f : 0.f;
-                    subst_all(x, arow, std::make_integer_sequence<int, SB>{});
-                    h4 tv;
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) tv[qq] = static_cast<_Float16>(x[qq] * bcol[qq]);
-                    *reinterpret_cast<h4*>(&nxt.tb[J][r][4 * g4]) = tv;
+                    const int c0 = 8 * hh + 2 * g4;
+                    const float b0 = sm.beta[SB * J + c0], b1 = sm.beta[SB * J + c0 + 1];
+                    float x[2] = {r == c0 ? 1.f : 0.f, r == c0 + 1 ? 1.f : 0.f};
+                    if (hh == 0) subst_range2<0>(x, arow, std::make_integer_sequence<int, SB - 1>{});
+                    else subst_range2<8>(x, arow, std::make_integer_sequence<int, SB - 9>{});
+                    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                    *reinterpret_cast<h2*>(&nxt.tb[J][r][c0]) =
+                        h2{static_cast<_Float16>(x[0] * b0), static_cast<_Float16>(x[1] * b1)};
                 } else {
-                    // One 16 x 16 block per wave (gate waves 2-6): P00, P11, P10, P01 (zero)
-                    // and -G10, 4 consecutive entries per lane.
-                    const int blk = gw - NSB;  // wave-uniform
-                    if (blk < 5) {
-                        const int i = (l >> 2) & 15, m4 = (l & 3) * 4;
-                        const int tile = blk == 0 ? 1 : blk == 1 ? 3 : blk == 2 ? 5 : blk == 4 ? 4 : -1;
-                        f4 val = {0.f, 0.f, 0.f, 0.f};
-                        if (tile >= 0) {
+                    // One 16 x 16 block per wave (gate waves 4-7): P00, P11, P10 and
+                    // -G10, 4 consecutive entries per lane (P01 is zero, written once).
+                    const int blk = gw - 2 * NSB;  // wave-uniform
+                    const int i = (l >> 2) & 15, m4 = (l & 3) * 4;
+                    const int tile = blk == 0 ? 1 : blk == 1 ? 3 : blk == 2 ? 5 : 4;
+                    f4 val = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                            for (int pp = 0; pp < NP; ++pp) val += *reinterpret_cast<const f4*>(&sm.gp[pp][tile][i][m4]);
-                        }
-                        h4 hv;
-                        if (blk == 4) {
+                    for (int pp = 0; pp < NP; ++pp) val += *reinterpret_cast<const f4*>(&sm.gp[pp][tile][i][m4]);
+                    h4 hv;
+                    if (blk == 3) {
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(-val[e]);
-                            *reinterpret_cast<h4*>(&nxt.tb[2][i][m4]) = hv;
-                        } else {
-                            const int bi = (blk == 1 || blk == 2) ? 1 : 0, bj = (blk == 1 || blk == 3) ? 1 : 0;
+                        for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(-val[e]);
+                        *reinterpret_cast<h4*>(&nxt.tb[2][i][m4]) = hv;
+                    } else {
+                        const int bi = blk >= 1 ? 1 : 0, bj = blk == 1 ? 1 : 0;
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                hv[e] = static_cast<_Float16>((bi > bj || m4 + e <= i) ? val[e] : 0.f);
-                            *reinterpret_cast<h4*>(&nxt.p[16 * bi + i][kpos(16 * bj + m4)]) = hv;
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            hv[e] = static_cast<_Float16>((bi > bj || m4 + e <= i) ? val[e] : 0.f);
+                        *reinterpret_cast<h4*>(&nxt.p[16 * bi + i][kpos(16 * bj + m4)]) = hv;
                     }
                 }
             }
@@ -1119,43 +1159,15 @@ void chunk_ws_kernel(
                         for (int i = 0; i < 4; ++i) S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
             }
         }
-        // Operands of the next chunk's state pass, prepared right after the
-        // previous S update (its v tile is in LDS by then): v, the scale
-        // exponent, and fp16 S (B operand of both K~ S and Q~ S).
+        // Operands of the next chunk's state pass.  Right after the S update
+        // (interval 2): max|S| over the wave and fp16 S at the current
+        // exponent.  Once chunk c + 1's v tile is staged (interval 3): v, the
+        // scale exponent from max(|S|, |v|), and -- only when the exponent
+        // moves -- the rescaled S and its fp16 copy again.
         float vv[NSB][NCT][4];
         h8 s16[4][NCT];
         float sig = 1.f;
-        auto prepare = [&](const Tiles& t) {
-#pragma unroll
-            for (int rt = 0; rt < NSB; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        vv[rt][ct][i] = bf16_to_f32(t.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
-            float mv = 0.f, ms = 0.f;
-#pragma unroll
-            for (int rt = 0; rt < NSB; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(vv[rt][ct][i]));
-#pragma unroll
-            for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[rt][ct][i]));
-            const int nex = value_exponent(wave_max_nonneg(fmaxf(ms * ldexpf(1.f, -ex), mv)), ex);
-            if (nex != ex) {
-                const float f = ldexpf(1.f, nex - ex);
-#pragma unroll
-                for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= f;
-                ex = nex;
-            }
-            sig = ldexpf(1.f, ex);
+        auto to_fp16 = [&]() {  // B operand of both K~ S and Q~ S
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -1165,6 +1177,44 @@ void chunk_ws_kernel(
                         s16[ks][ct][m] = static_cast<_Float16>(S[2 * ks][ct][m]);
                         s16[ks][ct][4 + m] = static_cast<_Float16>(S[2 * ks + 1][ct][m]);
                     }
+        };
+        auto state_max = [&]() {  // max|S| * 2^ex over the wave, with fp16 S at exponent ex
+            float ms = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(S[rt][ct][i]));
+            to_fp16();
+            return wave_max_nonneg(ms);
+        };
+        auto prepare = [&](const Tiles& t, float msw) {
+#pragma unroll
+            for (int rt = 0; rt < NSB; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        vv[rt][ct][i] = bf16_to_f32(t.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
+            float mv = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < NSB; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(vv[rt][ct][i]));
+            const int nex = value_exponent(fmaxf(msw * ldexpf(1.f, -ex), wave_max_nonneg(mv)), ex);
+            if (nex != ex) {
+                const float f = ldexpf(1.f, nex - ex);
+#pragma unroll
+                for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) S[rt][ct] *= f;
+                ex = nex;
+                to_fp16();
+            }
+            sig = ldexpf(1.f, ex);
         };
         const bool snapping = SNAP && snaps != nullptr && it.snap >= 0;
         SnapCursor sc{};
@@ -1242,7 +1292,7 @@ void chunk_ws_kernel(
 #pragma unroll
                         for (int ks = 0; ks < 4; ++ks) a = mfma16(qf8[ks], s16[ks][ct], a);
                         const int voc = vo + static_cast<int>(16 * ct * sizeof(Tout));
-                        if (GATED) {
+                        if (GATED || STAGE_O) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i) sm.otile[16 * rt + 4 * g4 + i][col + 16 * ct + r] = a[i] * os;
                         } else if (valid == C) {
@@ -1266,6 +1316,19 @@ void chunk_ws_kernel(
                     const h8 kb8 = *reinterpret_cast<const h8*>(&cur.kbt[16 * rt + r][8 * g4]);
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb8, d16[ct], S[rt][ct] * lam);
+                }
+                if (!GATED && STAGE_O) {
+                    // o rows of chunk c from the LDS tile: this wave stores tokens
+                    // 8 w .. 8 w + 7, two whole rows per 16-byte-per-lane store.
+                    // Rows past the end of the sequence fall outside the buffer range.
+                    const auto ro = rsrc(o + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * sizeof(Tout));
+                    const int el = epi_lane(), c4 = 4 * (el & 31);
+#pragma unroll
+                    for (int k2 = 0; k2 < 4; ++k2) {
+                        const int row = 8 * (w & 3) + 2 * k2 + (el >> 5);
+                        store4(ro, (row * rowe + c4) * static_cast<int>(sizeof(Tout)),
+                               *reinterpret_cast<const f4*>(&sm.otile[row][c4]), o);
+                    }
                 }
                 if (GATED) {
                     // y = gate * w * o / sqrt(mean(o^2) + eps) over the token's d_v channels;
@@ -1304,8 +1367,10 @@ void chunk_ws_kernel(
                     ++sc.row;
                 }
             }
+            float msw = 0.f;
+            if (c + 1 < nch) msw = state_max();
             __syncthreads();
-            if (c + 1 < nch) prepare(nxt);  // v of chunk c + 1 was staged in interval 2
+            if (c + 1 < nch) prepare(nxt, msw);  // v of chunk c + 1 was staged in interval 2
             __syncthreads();
         }
         if (it.sout >= 0 && out_state) {
