@@ -918,7 +918,8 @@ void chunk_ws_kernel(
             const auto rk = rsrc(k + cb, vld * rowe * 2);
             const auto rq = rsrc(q + cb, vld * rowe * 2);
             const auto rg = rsrc(g + cb, vld * rowe * 4);
-            const auto rb = rsrc(beta + cs * H + h, vld * H * 4);
+            // beta is read by the channel-part-0 waves only (an empty range for the others)
+            const auto rb = rsrc(beta + cs * H + h, part == 0 ? vld * H * 4 : 0u);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
@@ -954,8 +955,10 @@ void chunk_ws_kernel(
 
             constexpr float LOG2E = 1.4426950408889634f;
             // The raw inputs of chunk c + 1 are unpacked first (cumulative
-            // gates included), so the fetch of chunk c + 2 into the same
-            // registers is issued early in the phase, not behind its work.
+            // gates included).  Sub-block 0 waves then issue the fetch of chunk
+            // c + 2 into the same registers at once, sub-block 1 waves only after
+            // their phase-1 work, so the two groups' loads do not queue together
+            // (one fetch site, so the compiler still counts the loads exactly).
             float kf[KS][8], qf[KS][8], G[KS][8];
             if (gwork) {
 #pragma unroll
@@ -968,8 +971,7 @@ void chunk_ws_kernel(
                 }
                 if (part == 0 && g4 == 0) sm.beta[tok] = bt;
             }
-            fetch_gate(t0 + static_cast<int64_t>(c + 2) * C);
-            if (gwork) {
+            auto phase1 = [&]() {
                 constexpr float FAST_SPAN = 8.f * LOG2E;
                 f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1030,9 +1032,12 @@ void chunk_ws_kernel(
                     sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
                     sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
                 }
-            }
+            };
+            if (gwork && I == 1) phase1();
+            fetch_gate(t0 + static_cast<int64_t>(c + 2) * C);
+            if (gwork && I == 0) phase1();
             __syncthreads();
-            if (gwork) {  // v (and the output gate) of chunk c + 1 first, then the fetch of c + 2
+            if (gwork) {  // v (and the output gate) of chunk c + 1
 #pragma unroll
                 for (int j = 0; j < VU; ++j) {
                     const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
@@ -1040,7 +1045,6 @@ void chunk_ws_kernel(
                     if (GATED) *reinterpret_cast<u4*>(&nxt.og[vt][vc]) = gp_[j];
                 }
             }
-            fetch_v(t0 + static_cast<int64_t>(c + 2) * C);
             if (gwork) {
                 f4 a10 = {0.f, 0.f, 0.f, 0.f}, p10 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1090,6 +1094,7 @@ void chunk_ws_kernel(
                 }
             }
             __syncthreads();
+            fetch_v(t0 + static_cast<int64_t>(c + 2) * C);  // no other vector memory traffic in this interval
             if (gwork) {
                 if (gw < 2 * NSB) {
                     // Column-oriented substitution for T = (I + A_JJ)^-1, two waves
