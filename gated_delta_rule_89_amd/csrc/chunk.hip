@@ -46,7 +46,8 @@
 //  * Value-side fp16 operands (S, v, Delta) carry a per-wave power-of-two scale
 //    chosen every chunk from max(|S|, |v|), which keeps them inside fp16 range
 //    and away from subnormals; the scale is exact and is removed in fp32.
-//  * The next chunk's inputs are fetched into registers during the state pass.
+//  * The next chunk's inputs are fetched into registers a chunk ahead, right
+//    after the current chunk's have been unpacked (v after it is staged).
 #include <utility>
 
 #include "dev_common.h"
@@ -379,15 +380,17 @@ void chunk_kernel(
     u4 kw[KS], qw[KS], vp[VU];
     f4 ga[KS], gb[KS];
     float bt;
-    auto fetch = [&](int64_t cs) {
+    auto valid_at = [&](int64_t cs) {
         const int64_t nv = t1 - cs;
-        const uint32_t vld = static_cast<uint32_t>(nv < 0 ? 0 : nv < C ? nv : C);
+        return static_cast<uint32_t>(nv < 0 ? 0 : nv < C ? nv : C);
+    };
+    auto fetch_gate = [&](int64_t cs) {
+        const uint32_t vld = valid_at(cs);
         const int64_t cb = (cs * H + h) * D;
         const auto rk = rsrc(k + cb, vld * rowe * 2);
         const auto rq = rsrc(q + cb, vld * rowe * 2);
         const auto rg = rsrc(g + cb, vld * rowe * 4);
         const auto rb = rsrc(beta + cs * H + h, vld * H * 4);
-        const auto rv = rsrc(v + cb, vld * rowe * 2);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
@@ -398,13 +401,17 @@ void chunk_kernel(
             gb[ks] = f4{__uint_as_float(a1[0]), __uint_as_float(a1[1]), __uint_as_float(a1[2]), __uint_as_float(a1[3])};
         }
         bt = bload4(rb, 4 * tok * H);
+    };
+    auto fetch_v = [&](int64_t cs) {
+        const auto rv = rsrc(v + (cs * H + h) * D, valid_at(cs) * rowe * 2);
 #pragma unroll
         for (int j = 0; j < VU; ++j) {
             const int e = tid + NT * j, vt = e >> 4, vc = (e & 15) * 8;
             vp[j] = bload16(rv, 2 * (vt * rowe + vc));
         }
     };
-    fetch(t0);
+    fetch_gate(t0);
+    fetch_v(t0);
     const bool snapping = SNAP && !MAP && snaps != nullptr && it.snap >= 0;
     SnapCursor sc{};
     if (snapping) sc.init(it, interval);
@@ -421,31 +428,40 @@ void chunk_kernel(
             // A k-step whose exponents all stay within +-8 (natural units) over
             // the wave feeds them to fp16 MFMA; otherwise fp32 MFMA keeps fp32 range.
             constexpr float FAST_SPAN = 8.f * LOG2E;
+            // This chunk's raw inputs are unpacked first (Gamma from the
+            // sub-block start, in log2 units), so the next chunk's fetch into
+            // the same registers goes out a whole chunk ahead of its use.
+            float kf[KS][8], qf[KS][8], G[KS][8];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                unpack_bf16x8(kw[ks], kf[ks]);
+                if (!MAP) unpack_bf16x8(qw[ks], qf[ks]);
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    G[ks][m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
+            }
+            if (part == 0 && g4 == 0) sm.beta[tok] = bt;
+            fetch_gate(c0 + C);
             f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = CPG * part + 32 * ks + 8 * g4;
-                float kf[8], qf[8], G[8], Gt[8];
-                unpack_bf16x8(kw[ks], kf);
-                unpack_bf16x8(qw[ks], qf);
-                // Gamma from the sub-block start, in log2 units; Gt = sub-block total (lane 15)
+                float Gt[8];  // sub-block total (lane 15)
 #pragma unroll
-                for (int m = 0; m < 8; ++m) G[m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) Gt[m] = row_bcast16<15>(G[m]);
+                for (int m = 0; m < 8; ++m) Gt[m] = row_bcast16<15>(G[ks][m]);
                 // a = exp(G - tot/2), 1/a, and the channel's exp(tot/2) (a at the
                 // last token): exp(G) = a exp(tot/2), exp(tot - G) = exp(tot/2) / a.
                 float La[8], Ra[8], Qa[8], hh[8];
                 float span = 0.f;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
-                    const float xa = fmaf(-0.5f, Gt[m], G[m]);
+                    const float xa = fmaf(-0.5f, Gt[m], G[ks][m]);
                     span = fmaxf(span, fabsf(xa));
                     const float a = __builtin_amdgcn_exp2f(xa);
                     const float ia = __builtin_amdgcn_exp2f(-xa);
-                    La[m] = kf[m] * a;
-                    Ra[m] = kf[m] * ia;
-                    if (!MAP) Qa[m] = qf[m] * a;
+                    La[m] = kf[ks][m] * a;
+                    Ra[m] = kf[ks][m] * ia;
+                    if (!MAP) Qa[m] = qf[ks][m] * a;
                     hh[m] = row_bcast16<15>(a);
                 }
 #pragma unroll
@@ -485,7 +501,6 @@ void chunk_kernel(
                 sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
                 if (!MAP) sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
             }
-            if (part == 0 && g4 == 0) sm.beta[tok] = bt;
         }
         __syncthreads();  // B1
 
@@ -593,6 +608,7 @@ void chunk_kernel(
                 const int e = tid + NT * j, vt = e >> 4, vc = (e & 15) * 8;
                 *reinterpret_cast<u4*>(&sm.v[vt][vc]) = vp[j];
             }
+            fetch_v(c0 + C);
         }
         __syncthreads();  // B2
 
@@ -664,7 +680,6 @@ void chunk_kernel(
         __syncthreads();  // B3
 
         // ---------------- state pass on this wave's columns
-        fetch(c0 + C);
         {
             // v at token 16 rt + 4 g4 + i, column col + 16 ct + r (accumulator layout).
             float vv[NSB][NCT][4];
