@@ -844,8 +844,8 @@ void chunk_kernel(
 // ---------------------------------------------------------------------------
 // Full-mode kernel with wave roles: 32-token chunks (two sub-blocks); waves
 // 0-3 run the state pass of chunk c on 32 state columns each while waves
-// 4-11 prepare chunk c+1 (cumulative gates, Grams, the diagonal solves, P and
-// the cross Grams) into the other half of double-buffered operand tiles.
+// 4-11 prepare the next chunks (cumulative gates, Grams, the diagonal solves,
+// P and the cross Grams) into the other half of double-buffered operand tiles.
 // Each SIMD then holds one MFMA/LDS-heavy state wave and two VALU-heavy gate
 // waves of the same chain, and every A operand is read from LDS by 4 waves.
 namespace ws {
@@ -878,7 +878,7 @@ struct alignas(16) Smem {
     float gp[NP][2 * NSB + 2 * NX][SB][GP];
     float a[NSB][SB][20];                // A_JJ = Diag(beta) G_JJ, strictly lower, by row
     float etot[NSB][D];
-    float beta[C];
+    float beta[2][C];                    // beta of the chunks in phases 1-2 and 3 (by chunk parity)
 };
 }  // namespace ws
 
@@ -906,7 +906,13 @@ void chunk_ws_kernel(
     const int rowe = H * D;  // elements per token row
 
     // The two roles run separate loops with the same trip count and exactly
-    // three barriers per iteration (the barriers pair up across the roles).
+    // two barriers per iteration (the barriers pair up across the roles).
+    // Iteration c: the state waves run chunk c (Y, Delta, o into the LDS o
+    // tile, the S update) in interval 1, then store o and prepare chunk c + 1's
+    // operands in interval 2; the gate waves solve chunk c + 1's diagonal
+    // blocks and run phase 1 of chunk c + 2 in interval 1, and phase 2 of chunk
+    // c + 2 in interval 2.  The state waves also sum chunk c + 1's cross-block
+    // partials into P10 and -G10 at the start of interval 1.
     // Each role's memory traffic stays inside its own branch, and every
     // iteration issues the same loads (past the end of the sequence they fall
     // outside the buffer range and read zeros): the compiler can then count
@@ -964,9 +970,13 @@ void chunk_ws_kernel(
             sm.tl[e >> 8].p[(e >> 4) & 15][kpos(SB + (e & 15))] = static_cast<_Float16>(0.f);
         h8 l16[KS], q16[KS], rb16[KS];  // gate registers carried from phase 1 to phase 2
 
-        for (int c = -1; c < nch; ++c) {
-            const bool gwork = c + 1 < nch;   // prepare chunk c + 1
-            Tiles& nxt = sm.tl[(c + 1) & 1];
+        for (int c = -2; c < nch; ++c) {
+            const bool gwork = c + 2 < nch;              // phases 1 and 2 of chunk c + 2
+            const bool w3 = c + 1 >= 0 && c + 1 < nch;   // the solves of chunk c + 1
+            Tiles& nxt = sm.tl[c & 1];                   // chunk c + 2 (chunk c's buffer)
+            Tiles& t3 = sm.tl[(c + 1) & 1];
+            float* const bnx = sm.beta[c & 1];           // beta of chunk c + 2
+            const float* const b3 = sm.beta[(c + 1) & 1];
 
             constexpr float LOG2E = 1.4426950408889634f;
             // The raw inputs of chunk c + 1 are unpacked first (cumulative
@@ -984,7 +994,28 @@ void chunk_ws_kernel(
                     for (int m = 0; m < 8; ++m)
                         G[ks][m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
                 }
-                if (part == 0 && g4 == 0) sm.beta[tok] = bt;
+                if (part == 0 && g4 == 0) bnx[tok] = bt;
+            }
+            if (w3 && gw < 2 * NSB) {
+                // Column-oriented substitution for T = (I + A_JJ)^-1 of chunk c + 1,
+                // two waves per block: columns 8 hh .. 8 hh + 7.  Lane (i, g4) holds
+                // row i of columns 8 hh + 2 g4 + {0, 1} and row i of A (zero on and
+                // above the diagonal).  Step m broadcasts x_m of each column across
+                // its 16-lane row (DPP) and updates every row at once:
+                // x_i -= A[i][m] x_m.  Column j has x_m = 0 for m < j, so the right
+                // half starts at step 8; step 15 changes nothing.
+                const int J = gw & 1, hh = gw >> 1;  // the longer halves on SIMDs 0 and 1
+                f4 arow[4];
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) arow[cc] = *reinterpret_cast<const f4*>(&sm.a[J][r][4 * cc]);
+                const int cs0 = 8 * hh + 2 * g4;
+                const float b0 = b3[SB * J + cs0], b1 = b3[SB * J + cs0 + 1];
+                float x[2] = {r == cs0 ? 1.f : 0.f, r == cs0 + 1 ? 1.f : 0.f};
+                if (hh == 0) subst_range2<0>(x, arow, std::make_integer_sequence<int, SB - 1>{});
+                else subst_range2<8>(x, arow, std::make_integer_sequence<int, SB - 9>{});
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                *reinterpret_cast<h2*>(&t3.tb[J][r][cs0]) =
+                    h2{static_cast<_Float16>(x[0] * b0), static_cast<_Float16>(x[1] * b1)};
             }
             auto phase1 = [&]() {
                 constexpr float FAST_SPAN = 8.f * LOG2E;
@@ -1049,10 +1080,10 @@ void chunk_ws_kernel(
                 }
             };
             if (gwork && I == 1) phase1();
-            fetch_gate(t0 + static_cast<int64_t>(c + 2) * C);
+            fetch_gate(t0 + static_cast<int64_t>(c + 3) * C);
             if (gwork && I == 0) phase1();
             __syncthreads();
-            if (gwork) {  // v (and the output gate) of chunk c + 1
+            if (gwork) {  // v (and the output gate) of chunk c + 2
 #pragma unroll
                 for (int j = 0; j < VU; ++j) {
                     const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
@@ -1099,61 +1130,27 @@ void chunk_ws_kernel(
                         sm.gp[part][2 * NSB + 1][4 * g4 + i][r] = p10[i];
                     }
                 }
-                if (gtid < D) nxt.lam[gtid] = sm.etot[0][gtid] * sm.etot[1][gtid];
+                // lam, P00 and P11 on gate waves 2 and 3 (sub-block 0: lighter phase 2)
+                if (gtid >= 128 && gtid < 128 + D) nxt.lam[gtid - 128] = sm.etot[0][gtid - 128] * sm.etot[1][gtid - 128];
                 for (int e = gtid; e < NSB * SB * SB; e += GT) {
                     const int J = e >> 8, i = (e >> 4) & 15, m = e & 15;
                     float s = 0.f;
 #pragma unroll
                     for (int pp = 0; pp < NP; ++pp) s += sm.gp[pp][2 * J][i][m];
-                    sm.a[J][i][m] = m < i ? s * sm.beta[SB * J + i] : 0.f;  // A_JJ, strictly lower
+                    sm.a[J][i][m] = m < i ? s * bnx[SB * J + i] : 0.f;  // A_JJ, strictly lower
                 }
-            }
-            __syncthreads();
-            fetch_v(t0 + static_cast<int64_t>(c + 2) * C);  // no other vector memory traffic in this interval
-            if (gwork) {
-                if (gw < 2 * NSB) {
-                    // Column-oriented substitution for T = (I + A_JJ)^-1, two waves
-                    // per block: columns 8 hh .. 8 hh + 7.  Lane (i, g4) holds row i
-                    // of columns 8 hh + 2 g4 + {0, 1} and row i of A (zero on and
-                    // above the diagonal).  Step m broadcasts x_m of each column
-                    // across its 16-lane row (DPP) and updates every row at once:
-                    // x_i -= A[i][m] x_m.  Column j has x_m = 0 for m < j, so the
-                    // right half starts at step 8; step 15 changes nothing.
-                    const int J = gw >> 1, hh = gw & 1;
-                    f4 arow[4];
-#pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) arow[cc] = *reinterpret_cast<const f4*>(&sm.a[J][r][4 * cc]);
-                    const int c0 = 8 * hh + 2 * g4;
-                    const float b0 = sm.beta[SB * J + c0], b1 = sm.beta[SB * J + c0 + 1];
-                    float x[2] = {r == c0 ? 1.f : 0.f, r == c0 + 1 ? 1.f : 0.f};
-                    if (hh == 0) subst_range2<0>(x, arow, std::make_integer_sequence<int, SB - 1>{});
-                    else subst_range2<8>(x, arow, std::make_integer_sequence<int, SB - 9>{});
-                    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-                    *reinterpret_cast<h2*>(&nxt.tb[J][r][c0]) =
-                        h2{static_cast<_Float16>(x[0] * b0), static_cast<_Float16>(x[1] * b1)};
-                } else {
-                    // One 16 x 16 block per wave (gate waves 4-7): P00, P11, P10 and
-                    // -G10, 4 consecutive entries per lane (P01 is zero, written once).
-                    const int blk = gw - 2 * NSB;  // wave-uniform
-                    const int i = (l >> 2) & 15, m4 = (l & 3) * 4;
-                    const int tile = blk == 0 ? 1 : blk == 1 ? 3 : blk == 2 ? 5 : 4;
+                if (gtid >= 128 && gtid < 256) {  // P00 and P11, 4 consecutive entries per thread
+                    const int blk = (gtid >> 6) & 1, i = (gtid >> 2) & 15, m4 = (gtid & 3) * 4;
                     f4 val = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int pp = 0; pp < NP; ++pp) val += *reinterpret_cast<const f4*>(&sm.gp[pp][tile][i][m4]);
+                    for (int pp = 0; pp < NP; ++pp) val += *reinterpret_cast<const f4*>(&sm.gp[pp][2 * blk + 1][i][m4]);
                     h4 hv;
-                    if (blk == 3) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(-val[e]);
-                        *reinterpret_cast<h4*>(&nxt.tb[2][i][m4]) = hv;
-                    } else {
-                        const int bi = blk >= 1 ? 1 : 0, bj = blk == 1 ? 1 : 0;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            hv[e] = static_cast<_Float16>((bi > bj || m4 + e <= i) ? val[e] : 0.f);
-                        *reinterpret_cast<h4*>(&nxt.p[16 * bi + i][kpos(16 * bj + m4)]) = hv;
-                    }
+                    for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(m4 + e <= i ? val[e] : 0.f);
+                    *reinterpret_cast<h4*>(&nxt.p[16 * blk + i][kpos(16 * blk + m4)]) = hv;
                 }
             }
+            fetch_v(t0 + static_cast<int64_t>(c + 3) * C);
             __syncthreads();
         }
     } else {
@@ -1248,12 +1245,29 @@ void chunk_ws_kernel(
             asm volatile("" : "+v"(x));
             return x;
         };
-        for (int c = -1; c < nch; ++c) {
+        u4 ogr[2];  // gated output: this lane's output gate, read in interval 1
+        for (int c = -2; c < nch; ++c) {
             const bool swork = c >= 0;        // run chunk c
             const int64_t c0 = t0 + static_cast<int64_t>(c) * C;
             const Tiles& cur = sm.tl[c & 1];
-            const Tiles& nxt = sm.tl[(c + 1) & 1];
+            Tiles& nxt = sm.tl[(c + 1) & 1];
             const int valid = static_cast<int>(t1 - c0 < C ? t1 - c0 : C);
+            if (c + 1 >= 0 && c + 1 < nch && w >= 2) {
+                // P10 (wave 2) and -G10 (wave 3) of chunk c + 1 from the cross-Gram
+                // partials of its phase 2, 4 consecutive entries per lane (SIMDs 2
+                // and 3 carry the shorter halves of the diagonal solves).
+                const int i = (l >> 2) & 15, m4 = (l & 3) * 4;
+                const int tile = w == 2 ? 2 * NSB + 1 : 2 * NSB;
+                f4 val = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) val += *reinterpret_cast<const f4*>(&sm.gp[pp][tile][i][m4]);
+                h4 hv;
+                const float sgn = w == 2 ? 1.f : -1.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(sgn * val[e]);
+                if (w == 2) *reinterpret_cast<h4*>(&nxt.p[SB + i][kpos(m4)]) = hv;
+                else *reinterpret_cast<h4*>(&nxt.tb[2][i][m4]) = hv;
+            }
             if (swork) {
                 f4 y[NSB][NCT];
 #pragma unroll
@@ -1327,9 +1341,11 @@ void chunk_ws_kernel(
                         }
                     }
                 }
-            }
-            __syncthreads();
-            if (swork) {
+                            if (GATED) {  // the output gate of this wave's epilogue rows, before its tile is reused
+                    const int el = epi_lane(), erow = 8 * (w & 3) + (el >> 3), ecol = 16 * (el & 7);
+                    ogr[0] = *reinterpret_cast<const u4*>(&cur.og[erow][ecol]);
+                    ogr[1] = *reinterpret_cast<const u4*>(&cur.og[erow][ecol + 8]);
+                }
 #pragma unroll
                 for (int rt = 0; rt < 8; ++rt) {
                     const f4 lam = *reinterpret_cast<const f4*>(&cur.lam[16 * rt + 4 * g4]);
@@ -1337,6 +1353,14 @@ void chunk_ws_kernel(
 #pragma unroll
                     for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb8, d16[ct], S[rt][ct] * lam);
                 }
+                if (snapping && it.p0 + (c0 + valid - t0) == sc.next) {
+                    store_state<NCT>(snaps + (sc.row * H + h) * D * D, S, ldexpf(1.f, -ex), g4, r, col);
+                    sc.next += interval;
+                    ++sc.row;
+                }
+            }
+            __syncthreads();
+            if (swork) {
                 if (!GATED && STAGE_O) {
                     // o rows of chunk c from the LDS tile: this wave stores tokens
                     // 8 w .. 8 w + 7, two whole rows per 16-byte-per-lane store.
@@ -1369,7 +1393,7 @@ void chunk_ws_kernel(
 #pragma unroll
                     for (int j2 = 0; j2 < 2; ++j2) {  // 8 channels per step
                         float gf[8], yv[8];
-                        unpack_bf16x8(*reinterpret_cast<const u4*>(&cur.og[erow][ecol + 8 * j2]), gf);
+                        unpack_bf16x8(ogr[j2], gf);
 #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
                             const int c4 = ecol + 8 * j2 + 4 * jj;
@@ -1381,16 +1405,8 @@ void chunk_ws_kernel(
                         store8(ro, vo + 8 * j2 * static_cast<int>(sizeof(Tout)), yv, o);
                     }
                 }
-                if (snapping && it.p0 + (c0 + valid - t0) == sc.next) {
-                    store_state<NCT>(snaps + (sc.row * H + h) * D * D, S, ldexpf(1.f, -ex), g4, r, col);
-                    sc.next += interval;
-                    ++sc.row;
-                }
             }
-            float msw = 0.f;
-            if (c + 1 < nch) msw = state_max();
-            __syncthreads();
-            if (c + 1 < nch) prepare(nxt, msw);  // v of chunk c + 1 was staged in interval 2
+            if (c + 1 >= 0 && c + 1 < nch) prepare(nxt, state_max());  // v of chunk c + 1 was staged two intervals ago
             __syncthreads();
         }
         if (it.sout >= 0 && out_state) {
