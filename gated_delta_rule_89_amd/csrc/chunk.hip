@@ -1359,6 +1359,10 @@ void chunk_ws_kernel(
                     ++sc.row;
                 }
             }
+            // The gated epilogue makes interval 2 the longer one for these waves:
+            // take max|S| and fp16 S there only without it.
+            float msw = 0.f;
+            if (GATED && c + 1 >= 0 && c + 1 < nch) msw = state_max();
             __syncthreads();
             if (swork) {
                 if (!GATED && STAGE_O) {
@@ -1406,7 +1410,7 @@ void chunk_ws_kernel(
                     }
                 }
             }
-            if (c + 1 >= 0 && c + 1 < nch) prepare(nxt, state_max());  // v of chunk c + 1 was staged two intervals ago
+            if (c + 1 >= 0 && c + 1 < nch) prepare(nxt, GATED ? msw : state_max());  // v of chunk c + 1 staged two intervals ago
             __syncthreads();
         }
         if (it.sout >= 0 && out_state) {
