@@ -283,17 +283,18 @@ def main():
                           "frac": tb / (dm * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "config": f"{N3} sequences x {H3} heads, d=128"}
     if not args.no_extras:
-        # A measured streaming peak beside the spec one: a 1 GiB device-to-device
-        # copy (read + write) on the same stream, timed after the steps.
+        # A measured streaming rate beside the spec peak: an elementwise kernel
+        # reading 1 GiB and writing 1 GiB (torch.neg; the runtime's own
+        # device-to-device copy is slower), timed after the steps.
         csrc = torch.ones(1 << 28, device=dev)
         cdst = torch.empty_like(csrc)
-        cm = time_launches(lambda: cdst.copy_(csrc), stream, 5)
-        copy_gbs = 2 * csrc.numel() * 4 / (cm * 1e-3) / 1e9
+        cm = time_launches(lambda: torch.neg(csrc, out=cdst), stream, 5)
+        stream_gbs = 2 * csrc.numel() * 4 / (cm * 1e-3) / 1e9
         del csrc, cdst
-        line["measured_copy_gbs"] = copy_gbs
-        line["roofline"]["frac_of_measured_copy"] = achieved / copy_gbs
+        line["measured_stream_gbs"] = stream_gbs
+        line["roofline"]["frac_of_measured_stream"] = achieved / stream_gbs
         if dec:
-            line["decode"]["frac_of_measured_copy"] = line["decode"]["total_gbs"] / copy_gbs
+            line["decode"]["frac_of_measured_stream"] = line["decode"]["total_gbs"] / stream_gbs
         # Outside the timed step: a short run of 8 tokens per sequence with the
         # state in place (speculative verification), through kda_fused_recurrent_fwd.
         vx = synth.make_inputs("verify", device=dev)
