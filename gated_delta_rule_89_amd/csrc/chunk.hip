@@ -1176,11 +1176,11 @@ void chunk_ws_kernel(
                         for (int i = 0; i < 4; ++i) S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
             }
         }
-        // Operands of the next chunk's state pass.  Right after the S update
-        // (interval 2): max|S| over the wave and fp16 S at the current
-        // exponent.  Once chunk c + 1's v tile is staged (interval 3): v, the
-        // scale exponent from max(|S|, |v|), and -- only when the exponent
-        // moves -- the rescaled S and its fp16 copy again.
+        // Operands of the next chunk's state pass (interval 2; interval 1 for
+        // max|S| with the gated epilogue): max|S| over the wave and fp16 S at
+        // the current exponent, then chunk c + 1's v (staged two intervals
+        // earlier), the scale exponent from max(|S|, |v|), and -- only when
+        // the exponent moves -- the rescaled S and its fp16 copy again.
         float vv[NSB][NCT][4];
         h8 s16[4][NCT];
         float sig = 1.f;
