@@ -1130,14 +1130,19 @@ void chunk_ws_kernel(
                         sm.gp[part][2 * NSB + 1][4 * g4 + i][r] = p10[i];
                     }
                 }
-                // lam, P00 and P11 on gate waves 2 and 3 (sub-block 0: lighter phase 2)
+                // A_JJ on gate waves 0 and 1, lam, P00 and P11 on gate waves 2 and 3
+                // (sub-block 0: the lighter phase 2)
                 if (gtid >= 128 && gtid < 128 + D) nxt.lam[gtid - 128] = sm.etot[0][gtid - 128] * sm.etot[1][gtid - 128];
-                for (int e = gtid; e < NSB * SB * SB; e += GT) {
-                    const int J = e >> 8, i = (e >> 4) & 15, m = e & 15;
-                    float s = 0.f;
+                if (gtid < 128) {  // A_JJ = Diag(beta) G_JJ, strictly lower, 4 entries per thread
+                    const int J = gtid >> 6, i = (gtid >> 2) & 15, m4 = (gtid & 3) * 4;
+                    f4 val = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int pp = 0; pp < NP; ++pp) s += sm.gp[pp][2 * J][i][m];
-                    sm.a[J][i][m] = m < i ? s * bnx[SB * J + i] : 0.f;  // A_JJ, strictly lower
+                    for (int pp = 0; pp < NP; ++pp) val += *reinterpret_cast<const f4*>(&sm.gp[pp][2 * J][i][m4]);
+                    const float bi = bnx[SB * J + i];
+                    f4 av;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) av[e] = m4 + e < i ? val[e] * bi : 0.f;
+                    *reinterpret_cast<f4*>(&sm.a[J][i][m4]) = av;
                 }
                 if (gtid >= 128 && gtid < 256) {  // P00 and P11, 4 consecutive entries per thread
                     const int blk = (gtid >> 6) & 1, i = (gtid >> 2) & 15, m4 = (gtid & 3) * 4;
