@@ -293,6 +293,15 @@ def main():
         del csrc, cdst
         line["measured_stream_gbs"] = stream_gbs
         line["roofline"]["frac_of_measured_stream"] = achieved / stream_gbs
+        # A measured dense bf16 matrix rate beside the spec MFMA peak: one
+        # 8192^3 bf16 GEMM through torch (the vendor BLAS).
+        ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        gb_ = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        gm_ms = time_launches(lambda: torch.mm(ga, gb_), stream, 5)
+        gemm_tflops = 2.0 * 8192 ** 3 / (gm_ms * 1e-3) / 1e12
+        del ga, gb_
+        line["measured_bf16_gemm_tflops"] = gemm_tflops
+        line["mfma_frac_of_measured_gemm"] = alg_f / (pre_avg * 1e-3) / (gemm_tflops * 1e12)
         if dec:
             line["decode"]["frac_of_measured_stream"] = line["decode"]["total_gbs"] / stream_gbs
         # Outside the timed step: a short run of 8 tokens per sequence with the
