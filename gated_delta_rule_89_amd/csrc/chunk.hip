@@ -917,7 +917,7 @@ void chunk_ws_kernel(
     // iteration issues the same loads (past the end of the sequence they fall
     // outside the buffer range and read zeros): the compiler can then count
     // outstanding loads exactly and never waits for the prefetch of chunk
-    // c + 2 before it is consumed.
+    // c + 3 before it is consumed.
     if (gate) {
         // ---- gate waves: sub-block I, channel part `part`; raw inputs fetched ahead
         const int gw = w - NSW;
@@ -979,11 +979,12 @@ void chunk_ws_kernel(
             const float* const b3 = sm.beta[(c + 1) & 1];
 
             constexpr float LOG2E = 1.4426950408889634f;
-            // The raw inputs of chunk c + 1 are unpacked first (cumulative
+            // The raw inputs of chunk c + 2 are unpacked first (cumulative
             // gates included).  Sub-block 0 waves then issue the fetch of chunk
-            // c + 2 into the same registers at once, sub-block 1 waves only after
-            // their phase-1 work, so the two groups' loads do not queue together
-            // (one fetch site, so the compiler still counts the loads exactly).
+            // c + 3 into the same registers at once (after their solves),
+            // sub-block 1 waves only after their phase-1 work, so the two
+            // groups' loads do not queue together (one fetch site, so the
+            // compiler still counts the loads exactly).
             float kf[KS][8], qf[KS][8], G[KS][8];
             if (gwork) {
 #pragma unroll
