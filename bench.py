@@ -290,8 +290,13 @@ def main():
         cdst = torch.empty_like(csrc)
         cm = time_launches(lambda: torch.neg(csrc, out=cdst), stream, 5)
         stream_gbs = 2 * csrc.numel() * 4 / (cm * 1e-3) / 1e9
+        # and a write-only one (torch.fill_ over 1 GiB), the ceiling of a
+        # kernel whose traffic is almost all writes
+        wm = time_launches(lambda: cdst.fill_(0.5), stream, 5)
+        write_gbs = cdst.numel() * 4 / (wm * 1e-3) / 1e9
         del csrc, cdst
         line["measured_stream_gbs"] = stream_gbs
+        line["measured_write_gbs"] = write_gbs
         line["roofline"]["frac_of_measured_stream"] = achieved / stream_gbs
         # A measured dense bf16 matrix rate beside the spec MFMA peak: one
         # 8192^3 bf16 GEMM through torch (the vendor BLAS).
@@ -332,6 +337,7 @@ def main():
             "ms_per_launch": fm, "gbs": fb / (fm * 1e-3) / 1e9,
             "frac": fb / (fm * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": fb,
             "tflops": ff / (fm * 1e-3) / 1e12,
+            "frac_of_measured_write": fb / (fm * 1e-3) / 1e9 / write_gbs,
             "config": f"{tokens} tokens, rank {rk} up to {H} x {dk} log-gates (fp32) + beta"}
         del zq, uq
         if args.workload == "varlen":
