@@ -146,8 +146,9 @@ hipError_t launch_decode(const DecodeArgs& a) {
 // segment of the wave is CW * 4 contiguous bytes).  The two reductions over
 // the rows (S^T k and S^T q of the decayed state) stay inside the wave: DPP
 // row rotations inside each 16-lane row, then the row-pair swaps
-// v_permlane16_swap / v_permlane32_swap across rows.  No LDS, no barrier;
-// the next token's inputs are loaded before the current token's reductions.
+// v_permlane16_swap / v_permlane32_swap across rows.  Only the decay factors
+// pass through LDS (a slice per wave), so there is no barrier; the next
+// token's inputs are loaded before the current token's reductions.
 template <int TPR>
 __device__ __forceinline__ float sum_row_groups(float x) {
     // lanes that share l % TPR; TPR in {4, 8}
@@ -192,7 +193,15 @@ __global__ __launch_bounds__(256) void steps_kernel(
 
     // k is double-buffered (the update needs it after the reductions); q and
     // g of the next token are loaded as soon as the dot products are done.
-    float kr[R], qr[R], ga[R], nk[R];
+    // The decay factors exp(g) of a token are computed once per wave, NE rows
+    // per lane, and shared through the wave's slice of LDS: the lanes of a row
+    // group hold the same rows, so computing them per lane would repeat each
+    // exponential TPR times.  Only this wave touches its slice, and its LDS
+    // operations complete in order, so no barrier is needed.
+    constexpr int NE = (DK + 63) / 64;  // decay rows per lane
+    __shared__ __align__(16) float eg_lds[4][DK];
+    float* const egw = eg_lds[threadIdx.x >> 6];
+    float kr[R], qr[R], ga[R], nk[R], gn[NE];
     f32x4 vt, nv;
     float bt, nb;
     auto fetch_k = [&](int t) {
@@ -205,10 +214,18 @@ __global__ __launch_bounds__(256) void steps_kernel(
     auto fetch_qg = [&](int t) {
         const int64_t tv = (n * T + t) * H + h;
         load_rows<R>(q, tv * DK + r0, qr);
-        load_rows<R>(g, tv * DK + r0, ga);
+#pragma unroll
+        for (int j = 0; j < NE; ++j) gn[j] = (DK >= 64 || l < DK) ? g[tv * DK + l + 64 * j] : 0.f;
+    };
+    auto put_decay = [&]() {
+#pragma unroll
+        for (int j = 0; j < NE; ++j)
+            if (DK >= 64 || l < DK) egw[l + 64 * j] = gate_exp(gn[j]);
+        __builtin_amdgcn_wave_barrier();
     };
     fetch_k(0);
     fetch_qg(0);
+    put_decay();
     for (int t = 0; t < T; ++t) {
         const int64_t tv = (n * T + t) * H + h;
         const int tn = t + 1 < T ? t + 1 : t;  // every iteration loads: exact load counting
@@ -220,8 +237,11 @@ __global__ __launch_bounds__(256) void steps_kernel(
         f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
         float qk = 0.f;
 #pragma unroll
+        for (int i = 0; i < R; ++i) ga[i] = egw[r0 + i];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
         for (int i = 0; i < R; ++i) {
-            s[i] *= gate_exp(ga[i]);  // decay row
+            s[i] *= ga[i];  // decay row
             pk += s[i] * kr[i];
             pq += s[i] * qr[i];
             qk += qr[i] * kr[i];
@@ -240,6 +260,7 @@ __global__ __launch_bounds__(256) void steps_kernel(
 #pragma unroll
             for (int c = 0; c < 4; ++c) st(o, tv * DV + col + c, scale * (pq[c] + qk * u[c]));
         }
+        put_decay();  // the next token's (this token's factors are read above)
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (r0 + i) * DV));
