@@ -12,8 +12,11 @@ as state/total HBM GB/s.  Inputs are generated on the device before the
 timed region.  The roofline entry is for the prefill kernel: algorithmic
 bytes per launch / average launch time from HIP events on the launch stream.
 The CPU baseline is the C oracle on a bounded sample of the same workload.
-Entry points outside the hot path (a short run of tokens per sequence with
-the state in place) are timed after the steps and reported under "extras".
+After the steps, the long-context workload (one sequence of 1,048,576
+tokens, H=32) is timed through the same entry point and reported under
+"long"; entry points outside the hot path (short runs, gated output,
+snapshots, the fused gate) are timed after the steps and reported under
+"extras".
 
     python bench.py [--steps K] [--warmup W] [--workload varlen|long|prefill]
 """
@@ -175,6 +178,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the entry points outside the timed step (short runs)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context workload timed after the varlen steps")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device copy first (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -261,7 +266,8 @@ def main():
         "metric": "KDA prefill tokens/s (H=32,d=128) + decode state HBM GB/s; % of roofline",
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in; fp16 MFMA operands, fp32 accumulate, fp32 state and o",
         "data": "synthetic (seeded, generated on the device)",
         "config": {"workload": f"{args.workload}: {N} sequences, {tokens} tokens, H={H}, "
                                f"d_k=d_v={dk}, bf16 q/k/v, fp32 g/beta/state/o",
@@ -376,6 +382,33 @@ def main():
                 "snapshots": nsn, "gbs": sb / (sm * 1e-3) / 1e9,
                 "frac": sb / (sm * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": sb,
                 "config": f"{args.workload} prefill with the state every {iv} tokens"}
+    if args.workload == "varlen" and not args.no_long:
+        # The long-context workload (one sequence of 1,048,576 tokens, H=32)
+        # through the same entry point (AUTO: the segment scan), timed like the
+        # prefill above and reported beside it.
+        print("bench: generating long inputs on the device", file=sys.stderr, flush=True)
+        lx = synth.make_inputs("long", device=dev)
+        _, LT, LH, ldk = lx.q.shape
+        lo = torch.empty(1, LT, LH, lx.v.shape[-1], device=dev)
+        lf = torch.empty(1, LH, ldk, lx.v.shape[-1], device=dev)
+        lws = torch.empty(max(1, kda.workspace_size(1, LT, LH, ldk, ldk, 1, lx.q.dtype, "auto")),
+                          dtype=torch.uint8, device=dev)
+        lm = time_launches(lambda: kda.chunk_fwd(lx.q, lx.k, lx.v, lx.g, lx.beta, lx.scale, None,
+                                                 o=lo, final_state=lf, workspace=lws),
+                           stream, 5, warmup=1)
+        lb = prefill_alg_bytes(LT, LH, ldk, ldk, 1, h0=False)
+        lt = measured_traffic("long", "long prefill: 1 sequence, 1048576 tokens, H=32, d=128")
+        lach = lb / (lm * 1e-3) / 1e9
+        line["long"] = {
+            "ms_per_launch": lm, "tokens_per_s": LT / (lm * 1e-3), "alg_bytes": lb,
+            "mfma_peak_equiv_frac": prefill_alg_flops(LT, LH, ldk, ldk) / (lm * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+            "roofline": {"bound": "hbm", "achieved": lach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": lach / HBM_PEAK_GBS,
+                         "traffic": None if lt is None else lt / 1e9, "traffic_unit": "GB per launch",
+                         "kernel": "prefill (auto: segment maps, scan, segment pass)"},
+            "config": f"long: 1 sequence, {LT} tokens, H={LH}, d_k=d_v={ldk}, bf16 q/k/v, "
+                      f"fp32 g/beta/o, zero initial state"}
+        del lx, lo, lf, lws
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(x)

@@ -32,10 +32,13 @@
 //    relative to the sub-block start, across sub-blocks relative to sub-block
 //    ends, so every factor is <= 1 except in the diagonal Gram blocks.  Those
 //    take operands referenced to half the sub-block's gate total: fp16 MFMA
-//    when the wave's exponents stay within +-8, fp32 MFMA otherwise.  Every
-//    other product runs on fp16 MFMA with fp32 accumulation.  The kernel
-//    needs the sum of g over any 16 consecutive tokens of a channel to stay
-//    above about -85 (k exp(G) is formed in fp32 before the rescaling).
+//    when the wave's exponents stay within +-8, fp32 MFMA while they stay
+//    within +-120 (log2 units), and beyond that (a channel that forgets
+//    almost everything inside 16 tokens) every factor from its own exponent
+//    and the diagonal blocks entry by entry (phase1_direct), so any g <= 0
+//    is handled.  Every other product runs on fp16 MFMA with fp32
+//    accumulation; factors below the fp16 range underflow to zero, which
+//    only drops terms smaller than 2^-24 of the ones kept.
 //  * T is kept as its diagonal blocks T_JJ = (I + A_JJ)^-1 Diag(beta_J) and
 //    the raw cross Grams G_JK (A_JK = Diag(beta_J) G_JK); Delta = T X is then
 //    forward block substitution, Delta_J = T_JJ (X_J - sum_K<J G_JK Delta_K).
@@ -81,6 +84,10 @@ constexpr int D = 128;    // head size (d_k = d_v)
 constexpr int QP = 136;   // row stride (halves) of [token][channel] tiles
 constexpr int GP = 20;    // row stride (floats) of 16x16 Gram tiles (16-byte rows)
 constexpr int BP = 20;    // row stride (halves) of 16x16 fp16 blocks
+// Largest |G - tot/2| (log2 units) over a wave's k-step for which the
+// half-total reference keeps every factor and its inverse in fp32 range;
+// beyond it phase 1 takes the entry-by-entry form (phase1_direct).
+constexpr float SAFE_SPAN = 120.f;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -183,6 +190,72 @@ __device__ __forceinline__ float row_scan16(float x) {
     x += row_shr<4>(x);
     x += row_shr<8>(x);
     return x;
+}
+
+// Sum over the four 16-lane rows of the wave (every lane gets the total):
+// the gfx950 row-pair swaps exchange rows 0/1 and 2/3, then the two halves.
+__device__ __forceinline__ float sum_rows4(float x) {
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
+// Gate phase 1 for one 32-channel k-step whose exponents leave the fp32
+// range of the half-total reference (a channel's 16-token gate sum below
+// about -166): every factor from its own exponent, so nothing overflows.
+// Lane (r, g4) holds token r of the sub-block and channels 8 g4 .. 8 g4 + 7:
+// k (kf), q (qf) and the raw log-gates (gr, natural units).  Log-gates are
+// clamped at -100 first: alpha = e^-100 (about 4e-44) is zero next to any
+// fp32 state entry, and the clamp keeps the fp32 cumulative sums within
+// about 2^-12 of their exponents (no cancellation against a huge total).
+// Outputs: the fp16 operands k exp(G), q exp(G), k exp(tot - G), exp(tot)
+// per channel, and the diagonal Gram blocks entry by entry,
+//   A[r][j] = sum_c k_rc k_jc exp(G_rc - G_jc),  P[r][j] = sum_c q_rc k_jc exp(G_rc - G_jc),
+// over this lane group's channels, summed over the wave's four row groups;
+// lane (r, g4) adds columns j = 4 g4 .. 4 g4 + 3 of row r into oa and op.
+// Entries on or above the diagonal of A and above it for P are not used;
+// their exponent is capped at 0 so they stay finite.
+template <bool WITHQ>
+__device__ __forceinline__ void phase1_direct(const float (&kf)[8], const float (&qf)[8],
+                                              const float (&gr)[8], int g4, h8& l16, h8& q16,
+                                              h8& rb16, float (&et)[8], f4& oa, f4& op) {
+    constexpr float LOG2E = 1.4426950408889634f;
+    float Gc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        Gc[m] = row_scan16(fmaxf(gr[m], -100.f) * LOG2E);
+        const float tot = row_bcast16<15>(Gc[m]);
+        const float e = __builtin_amdgcn_exp2f(Gc[m]);
+        l16[m] = static_cast<_Float16>(kf[m] * e);
+        if (WITHQ) q16[m] = static_cast<_Float16>(qf[m] * e);
+        rb16[m] = static_cast<_Float16>(kf[m] * __builtin_amdgcn_exp2f(tot - Gc[m]));
+        et[m] = __builtin_amdgcn_exp2f(tot);
+    }
+    // Token j's values come from lane j of the same 16-lane row (a rolled
+    // loop with lane-indexed reads keeps this rarely taken path small).
+    const int rowbase = (__lane_id() & 48);
+#pragma unroll 1
+    for (int j = 0; j < SB; ++j) {
+        float a = 0.f, p = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float gj = __shfl(Gc[m], rowbase | j);
+            const float kj = __shfl(kf[m], rowbase | j);
+            const float t = kj * __builtin_amdgcn_exp2f(fminf(Gc[m] - gj, 0.f));
+            a = fmaf(kf[m], t, a);
+            if (WITHQ) p = fmaf(qf[m], t, p);
+        }
+        a = sum_rows4(a);
+        if (WITHQ) p = sum_rows4(p);
+        const bool mine = g4 == (j >> 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool sel = mine && (j & 3) == e;
+            oa[e] += sel ? a : 0.f;
+            if (WITHQ) op[e] += sel ? p : 0.f;
+        }
+    }
 }
 
 // Maximum of a non-negative value over the wave: prefix maxima inside each
@@ -443,6 +516,8 @@ void chunk_kernel(
             if (part == 0 && g4 == 0) sm.beta[tok] = bt;
             fetch_gate(c0 + C);
             f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+            f4 oa = {0.f, 0.f, 0.f, 0.f}, op = {0.f, 0.f, 0.f, 0.f};
+            bool direct = false;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = CPG * part + 32 * ks + 8 * g4;
@@ -451,48 +526,72 @@ void chunk_kernel(
                 for (int m = 0; m < 8; ++m) Gt[m] = row_bcast16<15>(G[ks][m]);
                 // a = exp(G - tot/2), 1/a, and the channel's exp(tot/2) (a at the
                 // last token): exp(G) = a exp(tot/2), exp(tot - G) = exp(tot/2) / a.
-                float La[8], Ra[8], Qa[8], hh[8];
+                float xa[8];
                 float span = 0.f;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
-                    const float xa = fmaf(-0.5f, Gt[m], G[ks][m]);
-                    span = fmaxf(span, fabsf(xa));
-                    const float a = __builtin_amdgcn_exp2f(xa);
-                    const float ia = __builtin_amdgcn_exp2f(-xa);
-                    La[m] = kf[ks][m] * a;
-                    Ra[m] = kf[ks][m] * ia;
-                    if (!MAP) Qa[m] = qf[ks][m] * a;
-                    hh[m] = row_bcast16<15>(a);
+                    xa[m] = fmaf(-0.5f, Gt[m], G[ks][m]);
+                    span = fmaxf(span, fabsf(xa[m]));
                 }
+                if (__any(span > SAFE_SPAN)) {
+                    // Out of the reference's fp32 range: factors and diagonal Grams
+                    // from the raw log-gates of this k-step (read again).
+                    const auto rg = rsrc(g + (c0 * H + h) * D, valid_at(c0) * rowe * 4);
+                    const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
+                    const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
+                    float gr[8], et[8];
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G) <= |k|
-                    rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
-                    if (!MAP) q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);
-                }
-                if (!__any(span > FAST_SPAN)) {  // wave-uniform
-                    h8 la, ra, qa;
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        la[m] = static_cast<_Float16>(La[m]);
-                        ra[m] = static_cast<_Float16>(Ra[m]);
-                        if (!MAP) qa[m] = static_cast<_Float16>(Qa[m]);
+                    for (int m = 0; m < 4; ++m) {
+                        gr[m] = __uint_as_float(a0[m]);
+                        gr[4 + m] = __uint_as_float(a1[m]);
                     }
-                    accA = mfma16(la, ra, accA);
-                    if (!MAP) accP = mfma16(qa, ra, accP);
+                    phase1_direct<!MAP>(kf[ks], qf[ks], gr, g4, l16[ks], q16[ks], rb16[ks], et, oa, op);
+                    direct = true;
+                    if (r == 15) {
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{et[0], et[1], et[2], et[3]};
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{et[4], et[5], et[6], et[7]};
+                    }
                 } else {
-                    // MFMA m contracts channel 8 g4 + m (k index g4).
+                    float La[8], Ra[8], Qa[8], hh[8];
 #pragma unroll
                     for (int m = 0; m < 8; ++m) {
-                        accA = mfma4(La[m], Ra[m], accA);
-                        if (!MAP) accP = mfma4(Qa[m], Ra[m], accP);
+                        const float a = __builtin_amdgcn_exp2f(xa[m]);
+                        const float ia = __builtin_amdgcn_exp2f(-xa[m]);
+                        La[m] = kf[ks][m] * a;
+                        Ra[m] = kf[ks][m] * ia;
+                        if (!MAP) Qa[m] = qf[ks][m] * a;
+                        hh[m] = row_bcast16<15>(a);
                     }
-                }
-                if (r == 15) {  // exp(sum of g over the sub-block) = exp(tot/2)^2
-                    *reinterpret_cast<f4*>(&sm.etot[I][ch]) =
-                        f4{hh[0] * hh[0], hh[1] * hh[1], hh[2] * hh[2], hh[3] * hh[3]};
-                    *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) =
-                        f4{hh[4] * hh[4], hh[5] * hh[5], hh[6] * hh[6], hh[7] * hh[7]};
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G) <= |k|
+                        rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
+                        if (!MAP) q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);
+                    }
+                    if (!__any(span > FAST_SPAN)) {  // wave-uniform
+                        h8 la, ra, qa;
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            la[m] = static_cast<_Float16>(La[m]);
+                            ra[m] = static_cast<_Float16>(Ra[m]);
+                            if (!MAP) qa[m] = static_cast<_Float16>(Qa[m]);
+                        }
+                        accA = mfma16(la, ra, accA);
+                        if (!MAP) accP = mfma16(qa, ra, accP);
+                    } else {
+                        // MFMA m contracts channel 8 g4 + m (k index g4).
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            accA = mfma4(La[m], Ra[m], accA);
+                            if (!MAP) accP = mfma4(Qa[m], Ra[m], accP);
+                        }
+                    }
+                    if (r == 15) {  // exp(sum of g over the sub-block) = exp(tot/2)^2
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch]) =
+                            f4{hh[0] * hh[0], hh[1] * hh[1], hh[2] * hh[2], hh[3] * hh[3]};
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) =
+                            f4{hh[4] * hh[4], hh[5] * hh[5], hh[6] * hh[6], hh[7] * hh[7]};
+                    }
                 }
                 if (I < NSB - 1) *reinterpret_cast<h8*>(&sm.rbs[I][r][ch]) = rb16[ks];
             }
@@ -500,6 +599,14 @@ void chunk_kernel(
             for (int i = 0; i < 4; ++i) {
                 sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
                 if (!MAP) sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
+            }
+            if (direct) {  // entry-by-entry k-steps, by row (same wave: LDS in order)
+                f4* pa = reinterpret_cast<f4*>(&sm.gp[part][2 * I][r][4 * g4]);
+                *pa = *pa + oa;
+                if (!MAP) {
+                    f4* pp = reinterpret_cast<f4*>(&sm.gp[part][2 * I + 1][r][4 * g4]);
+                    *pp = *pp + op;
+                }
             }
         }
         __syncthreads();  // B1
@@ -1021,6 +1128,8 @@ void chunk_ws_kernel(
             auto phase1 = [&]() {
                 constexpr float FAST_SPAN = 8.f * LOG2E;
                 f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+                f4 oa = {0.f, 0.f, 0.f, 0.f}, op = {0.f, 0.f, 0.f, 0.f};
+                bool direct = false;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int ch = CPG * part + 32 * ks + 8 * g4;
@@ -1030,47 +1139,72 @@ void chunk_ws_kernel(
                     // Factors referenced to half the sub-block total: a = exp(G - tot/2),
                     // 1/a, and the channel's exp(tot/2), which is a at the last token.
                     // exp(G) = a exp(tot/2) and exp(tot - G) = exp(tot/2) / a.
-                    float xa[8], La[8], Ra[8], Qa[8], hh[8];
+                    float xa[8];
                     float span = 0.f;
 #pragma unroll
                     for (int m = 0; m < 8; ++m) {
                         xa[m] = fmaf(-0.5f, Gt[m], G[ks][m]);
                         span = fmaxf(span, fabsf(xa[m]));
-                        const float a = __builtin_amdgcn_exp2f(xa[m]);
-                        const float ia = __builtin_amdgcn_exp2f(-xa[m]);
-                        La[m] = kf[ks][m] * a;
-                        Ra[m] = kf[ks][m] * ia;
-                        Qa[m] = qf[ks][m] * a;
-                        hh[m] = row_bcast16<15>(a);
                     }
+                    if (__any(span > SAFE_SPAN)) {
+                        // Out of the reference's fp32 range: factors and diagonal
+                        // Grams from the raw log-gates of this k-step (read again).
+                        const int64_t cs = t0 + static_cast<int64_t>(c + 2) * C;
+                        const auto rg = rsrc(g + (cs * H + h) * D, valid_at(cs) * rowe * 4);
+                        const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
+                        const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
+                        float gr[8], et[8];
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G)
-                        rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
-                        q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);   // q exp(G)
-                    }
-                    if (!__any(span > FAST_SPAN)) {
-                        h8 la, ra, qa;
-#pragma unroll
-                        for (int m = 0; m < 8; ++m) {
-                            la[m] = static_cast<_Float16>(La[m]);
-                            ra[m] = static_cast<_Float16>(Ra[m]);
-                            qa[m] = static_cast<_Float16>(Qa[m]);
+                        for (int m = 0; m < 4; ++m) {
+                            gr[m] = __uint_as_float(a0[m]);
+                            gr[4 + m] = __uint_as_float(a1[m]);
                         }
-                        accA = mfma16(la, ra, accA);
-                        accP = mfma16(qa, ra, accP);
+                        phase1_direct<true>(kf[ks], qf[ks], gr, g4, l16[ks], q16[ks], rb16[ks], et, oa, op);
+                        direct = true;
+                        if (r == 15) {
+                            *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{et[0], et[1], et[2], et[3]};
+                            *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{et[4], et[5], et[6], et[7]};
+                        }
                     } else {
+                        float La[8], Ra[8], Qa[8], hh[8];
 #pragma unroll
                         for (int m = 0; m < 8; ++m) {
-                            accA = mfma4(La[m], Ra[m], accA);
-                            accP = mfma4(Qa[m], Ra[m], accP);
+                            const float a = __builtin_amdgcn_exp2f(xa[m]);
+                            const float ia = __builtin_amdgcn_exp2f(-xa[m]);
+                            La[m] = kf[ks][m] * a;
+                            Ra[m] = kf[ks][m] * ia;
+                            Qa[m] = qf[ks][m] * a;
+                            hh[m] = row_bcast16<15>(a);
                         }
-                    }
-                    if (r == 15) {  // exp(tot) = exp(tot/2)^2
-                        *reinterpret_cast<f4*>(&sm.etot[I][ch]) =
-                            f4{hh[0] * hh[0], hh[1] * hh[1], hh[2] * hh[2], hh[3] * hh[3]};
-                        *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) =
-                            f4{hh[4] * hh[4], hh[5] * hh[5], hh[6] * hh[6], hh[7] * hh[7]};
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G)
+                            rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
+                            q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);   // q exp(G)
+                        }
+                        if (!__any(span > FAST_SPAN)) {
+                            h8 la, ra, qa;
+#pragma unroll
+                            for (int m = 0; m < 8; ++m) {
+                                la[m] = static_cast<_Float16>(La[m]);
+                                ra[m] = static_cast<_Float16>(Ra[m]);
+                                qa[m] = static_cast<_Float16>(Qa[m]);
+                            }
+                            accA = mfma16(la, ra, accA);
+                            accP = mfma16(qa, ra, accP);
+                        } else {
+#pragma unroll
+                            for (int m = 0; m < 8; ++m) {
+                                accA = mfma4(La[m], Ra[m], accA);
+                                accP = mfma4(Qa[m], Ra[m], accP);
+                            }
+                        }
+                        if (r == 15) {  // exp(tot) = exp(tot/2)^2
+                            *reinterpret_cast<f4*>(&sm.etot[I][ch]) =
+                                f4{hh[0] * hh[0], hh[1] * hh[1], hh[2] * hh[2], hh[3] * hh[3]};
+                            *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) =
+                                f4{hh[4] * hh[4], hh[5] * hh[5], hh[6] * hh[6], hh[7] * hh[7]};
+                        }
                     }
                     if (I == 0) *reinterpret_cast<h8*>(&sm.rbs[r][ch]) = rb16[ks];
                 }
@@ -1078,6 +1212,12 @@ void chunk_ws_kernel(
                 for (int i = 0; i < 4; ++i) {
                     sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
                     sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
+                }
+                if (direct) {  // entry-by-entry k-steps, by row (same wave: LDS in order)
+                    f4* pa = reinterpret_cast<f4*>(&sm.gp[part][2 * I][r][4 * g4]);
+                    f4* pp = reinterpret_cast<f4*>(&sm.gp[part][2 * I + 1][r][4 * g4]);
+                    *pa = *pa + oa;
+                    *pp = *pp + op;
                 }
             };
             if (gwork && I == 1) phase1();

@@ -127,9 +127,11 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
  *  workspace   device scratch of at least kda_chunk_fwd_workspace_size()
  *              bytes (may be NULL when that is 0), 256-byte aligned; its
  *              contents on entry do not matter and are overwritten.
- * The chunked variants need the sum of g over any 16 consecutive tokens of a
- * channel to stay above about -85; beyond that their results are undefined
- * (the recurrent variant has no such limit).
+ * Every variant accepts any g <= 0 with |g| < 1e38, down to full
+ * forgetting.  The chunked variants may treat a log-gate below -100 as -100
+ * (alpha = e^-100, about 4e-44, is zero next to any fp32 state value); for
+ * alpha = 0 pass a large negative value rather than -inf.  g > 0 (a gate
+ * above one) is accepted without a range guarantee.
  * T = 0 or N = 0 is a successful no-op. */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, float scale, const float* initial_state,
