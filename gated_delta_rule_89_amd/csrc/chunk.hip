@@ -516,8 +516,7 @@ void chunk_kernel(
             if (part == 0 && g4 == 0) sm.beta[tok] = bt;
             fetch_gate(c0 + C);
             f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-            f4 oa = {0.f, 0.f, 0.f, 0.f}, op = {0.f, 0.f, 0.f, 0.f};
-            bool direct = false;
+            bool redo = false;  // wave-uniform: a k-step beyond the reference's range
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ch = CPG * part + 32 * ks + 8 * g4;
@@ -526,72 +525,49 @@ void chunk_kernel(
                 for (int m = 0; m < 8; ++m) Gt[m] = row_bcast16<15>(G[ks][m]);
                 // a = exp(G - tot/2), 1/a, and the channel's exp(tot/2) (a at the
                 // last token): exp(G) = a exp(tot/2), exp(tot - G) = exp(tot/2) / a.
-                float xa[8];
+                float La[8], Ra[8], Qa[8], hh[8];
                 float span = 0.f;
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
-                    xa[m] = fmaf(-0.5f, Gt[m], G[ks][m]);
-                    span = fmaxf(span, fabsf(xa[m]));
+                    const float xa = fmaf(-0.5f, Gt[m], G[ks][m]);
+                    span = fmaxf(span, fabsf(xa));
+                    const float a = __builtin_amdgcn_exp2f(xa);
+                    const float ia = __builtin_amdgcn_exp2f(-xa);
+                    La[m] = kf[ks][m] * a;
+                    Ra[m] = kf[ks][m] * ia;
+                    if (!MAP) Qa[m] = qf[ks][m] * a;
+                    hh[m] = row_bcast16<15>(a);
                 }
-                if (__any(span > SAFE_SPAN)) {
-                    // Out of the reference's fp32 range: factors and diagonal Grams
-                    // from the raw log-gates of this k-step (read again).
-                    const auto rg = rsrc(g + (c0 * H + h) * D, valid_at(c0) * rowe * 4);
-                    const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
-                    const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
-                    float gr[8], et[8];
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        gr[m] = __uint_as_float(a0[m]);
-                        gr[4 + m] = __uint_as_float(a1[m]);
+                for (int m = 0; m < 8; ++m) {
+                    l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G) <= |k|
+                    rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
+                    if (!MAP) q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);
+                }
+                if (!__any(span > FAST_SPAN)) {  // wave-uniform
+                    h8 la, ra, qa;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        la[m] = static_cast<_Float16>(La[m]);
+                        ra[m] = static_cast<_Float16>(Ra[m]);
+                        if (!MAP) qa[m] = static_cast<_Float16>(Qa[m]);
                     }
-                    phase1_direct<!MAP>(kf[ks], qf[ks], gr, g4, l16[ks], q16[ks], rb16[ks], et, oa, op);
-                    direct = true;
-                    if (r == 15) {
-                        *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{et[0], et[1], et[2], et[3]};
-                        *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{et[4], et[5], et[6], et[7]};
-                    }
+                    accA = mfma16(la, ra, accA);
+                    if (!MAP) accP = mfma16(qa, ra, accP);
                 } else {
-                    float La[8], Ra[8], Qa[8], hh[8];
+                    // MFMA m contracts channel 8 g4 + m (k index g4).
 #pragma unroll
                     for (int m = 0; m < 8; ++m) {
-                        const float a = __builtin_amdgcn_exp2f(xa[m]);
-                        const float ia = __builtin_amdgcn_exp2f(-xa[m]);
-                        La[m] = kf[ks][m] * a;
-                        Ra[m] = kf[ks][m] * ia;
-                        if (!MAP) Qa[m] = qf[ks][m] * a;
-                        hh[m] = row_bcast16<15>(a);
+                        accA = mfma4(La[m], Ra[m], accA);
+                        if (!MAP) accP = mfma4(Qa[m], Ra[m], accP);
                     }
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G) <= |k|
-                        rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
-                        if (!MAP) q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);
-                    }
-                    if (!__any(span > FAST_SPAN)) {  // wave-uniform
-                        h8 la, ra, qa;
-#pragma unroll
-                        for (int m = 0; m < 8; ++m) {
-                            la[m] = static_cast<_Float16>(La[m]);
-                            ra[m] = static_cast<_Float16>(Ra[m]);
-                            if (!MAP) qa[m] = static_cast<_Float16>(Qa[m]);
-                        }
-                        accA = mfma16(la, ra, accA);
-                        if (!MAP) accP = mfma16(qa, ra, accP);
-                    } else {
-                        // MFMA m contracts channel 8 g4 + m (k index g4).
-#pragma unroll
-                        for (int m = 0; m < 8; ++m) {
-                            accA = mfma4(La[m], Ra[m], accA);
-                            if (!MAP) accP = mfma4(Qa[m], Ra[m], accP);
-                        }
-                    }
-                    if (r == 15) {  // exp(sum of g over the sub-block) = exp(tot/2)^2
-                        *reinterpret_cast<f4*>(&sm.etot[I][ch]) =
-                            f4{hh[0] * hh[0], hh[1] * hh[1], hh[2] * hh[2], hh[3] * hh[3]};
-                        *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) =
-                            f4{hh[4] * hh[4], hh[5] * hh[5], hh[6] * hh[6], hh[7] * hh[7]};
-                    }
+                    redo = redo || __any(span > SAFE_SPAN);
+                }
+                if (r == 15) {  // exp(sum of g over the sub-block) = exp(tot/2)^2
+                    *reinterpret_cast<f4*>(&sm.etot[I][ch]) =
+                        f4{hh[0] * hh[0], hh[1] * hh[1], hh[2] * hh[2], hh[3] * hh[3]};
+                    *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) =
+                        f4{hh[4] * hh[4], hh[5] * hh[5], hh[6] * hh[6], hh[7] * hh[7]};
                 }
                 if (I < NSB - 1) *reinterpret_cast<h8*>(&sm.rbs[I][r][ch]) = rb16[ks];
             }
@@ -600,13 +576,39 @@ void chunk_kernel(
                 sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
                 if (!MAP) sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
             }
-            if (direct) {  // entry-by-entry k-steps, by row (same wave: LDS in order)
-                f4* pa = reinterpret_cast<f4*>(&sm.gp[part][2 * I][r][4 * g4]);
-                *pa = *pa + oa;
-                if (!MAP) {
-                    f4* pp = reinterpret_cast<f4*>(&sm.gp[part][2 * I + 1][r][4 * g4]);
-                    *pp = *pp + op;
+            if (redo) {
+                // Exponents beyond the fp32 range of the half-total reference: the
+                // wave's phase 1 again, entry by entry from its raw inputs (read
+                // again, so nothing stays live for this rare case), over
+                // everything written above (the same wave's LDS writes complete
+                // in order).
+                const uint32_t vld = valid_at(c0);
+                const int64_t cb = (c0 * H + h) * D;
+                const auto rk = rsrc(k + cb, vld * rowe * 2), rq = rsrc(q + cb, MAP ? 0u : vld * rowe * 2);
+                const auto rg = rsrc(g + cb, vld * rowe * 4);
+                f4 oa = {0.f, 0.f, 0.f, 0.f}, op = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int ch = CPG * part + 32 * ks + 8 * g4;
+                    const int off = tok * rowe + ch;
+                    const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
+                    float gr[8], et[8], kr[8], qr[8];
+                    unpack_bf16x8(bload16(rk, 2 * off), kr);
+                    unpack_bf16x8(bload16(rq, 2 * off), qr);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        gr[m] = __uint_as_float(a0[m]);
+                        gr[4 + m] = __uint_as_float(a1[m]);
+                    }
+                    phase1_direct<!MAP>(kr, qr, gr, g4, l16[ks], q16[ks], rb16[ks], et, oa, op);
+                    if (r == 15) {
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{et[0], et[1], et[2], et[3]};
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{et[4], et[5], et[6], et[7]};
+                    }
+                    if (I < NSB - 1) *reinterpret_cast<h8*>(&sm.rbs[I][r][ch]) = rb16[ks];
                 }
+                *reinterpret_cast<f4*>(&sm.gp[part][2 * I][r][4 * g4]) = oa;
+                if (!MAP) *reinterpret_cast<f4*>(&sm.gp[part][2 * I + 1][r][4 * g4]) = op;
             }
         }
         __syncthreads();  // B1
@@ -1128,8 +1130,7 @@ void chunk_ws_kernel(
             auto phase1 = [&]() {
                 constexpr float FAST_SPAN = 8.f * LOG2E;
                 f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-                f4 oa = {0.f, 0.f, 0.f, 0.f}, op = {0.f, 0.f, 0.f, 0.f};
-                bool direct = false;
+                bool redo = false;  // wave-uniform: a k-step beyond the reference's range
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int ch = CPG * part + 32 * ks + 8 * g4;
@@ -1139,72 +1140,48 @@ void chunk_ws_kernel(
                     // Factors referenced to half the sub-block total: a = exp(G - tot/2),
                     // 1/a, and the channel's exp(tot/2), which is a at the last token.
                     // exp(G) = a exp(tot/2) and exp(tot - G) = exp(tot/2) / a.
-                    float xa[8];
+                    float xa[8], La[8], Ra[8], Qa[8], hh[8];
                     float span = 0.f;
 #pragma unroll
                     for (int m = 0; m < 8; ++m) {
                         xa[m] = fmaf(-0.5f, Gt[m], G[ks][m]);
                         span = fmaxf(span, fabsf(xa[m]));
+                        const float a = __builtin_amdgcn_exp2f(xa[m]);
+                        const float ia = __builtin_amdgcn_exp2f(-xa[m]);
+                        La[m] = kf[ks][m] * a;
+                        Ra[m] = kf[ks][m] * ia;
+                        Qa[m] = qf[ks][m] * a;
+                        hh[m] = row_bcast16<15>(a);
                     }
-                    if (__any(span > SAFE_SPAN)) {
-                        // Out of the reference's fp32 range: factors and diagonal
-                        // Grams from the raw log-gates of this k-step (read again).
-                        const int64_t cs = t0 + static_cast<int64_t>(c + 2) * C;
-                        const auto rg = rsrc(g + (cs * H + h) * D, valid_at(cs) * rowe * 4);
-                        const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
-                        const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
-                        float gr[8], et[8];
 #pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            gr[m] = __uint_as_float(a0[m]);
-                            gr[4 + m] = __uint_as_float(a1[m]);
+                    for (int m = 0; m < 8; ++m) {
+                        l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G)
+                        rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
+                        q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);   // q exp(G)
+                    }
+                    if (!__any(span > FAST_SPAN)) {
+                        h8 la, ra, qa;
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) {
+                            la[m] = static_cast<_Float16>(La[m]);
+                            ra[m] = static_cast<_Float16>(Ra[m]);
+                            qa[m] = static_cast<_Float16>(Qa[m]);
                         }
-                        phase1_direct<true>(kf[ks], qf[ks], gr, g4, l16[ks], q16[ks], rb16[ks], et, oa, op);
-                        direct = true;
-                        if (r == 15) {
-                            *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{et[0], et[1], et[2], et[3]};
-                            *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{et[4], et[5], et[6], et[7]};
-                        }
+                        accA = mfma16(la, ra, accA);
+                        accP = mfma16(qa, ra, accP);
                     } else {
-                        float La[8], Ra[8], Qa[8], hh[8];
 #pragma unroll
                         for (int m = 0; m < 8; ++m) {
-                            const float a = __builtin_amdgcn_exp2f(xa[m]);
-                            const float ia = __builtin_amdgcn_exp2f(-xa[m]);
-                            La[m] = kf[ks][m] * a;
-                            Ra[m] = kf[ks][m] * ia;
-                            Qa[m] = qf[ks][m] * a;
-                            hh[m] = row_bcast16<15>(a);
+                            accA = mfma4(La[m], Ra[m], accA);
+                            accP = mfma4(Qa[m], Ra[m], accP);
                         }
-#pragma unroll
-                        for (int m = 0; m < 8; ++m) {
-                            l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G)
-                            rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
-                            q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);   // q exp(G)
-                        }
-                        if (!__any(span > FAST_SPAN)) {
-                            h8 la, ra, qa;
-#pragma unroll
-                            for (int m = 0; m < 8; ++m) {
-                                la[m] = static_cast<_Float16>(La[m]);
-                                ra[m] = static_cast<_Float16>(Ra[m]);
-                                qa[m] = static_cast<_Float16>(Qa[m]);
-                            }
-                            accA = mfma16(la, ra, accA);
-                            accP = mfma16(qa, ra, accP);
-                        } else {
-#pragma unroll
-                            for (int m = 0; m < 8; ++m) {
-                                accA = mfma4(La[m], Ra[m], accA);
-                                accP = mfma4(Qa[m], Ra[m], accP);
-                            }
-                        }
-                        if (r == 15) {  // exp(tot) = exp(tot/2)^2
-                            *reinterpret_cast<f4*>(&sm.etot[I][ch]) =
-                                f4{hh[0] * hh[0], hh[1] * hh[1], hh[2] * hh[2], hh[3] * hh[3]};
-                            *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) =
-                                f4{hh[4] * hh[4], hh[5] * hh[5], hh[6] * hh[6], hh[7] * hh[7]};
-                        }
+                        redo = redo || __any(span > SAFE_SPAN);
+                    }
+                    if (r == 15) {  // exp(tot) = exp(tot/2)^2
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch]) =
+                            f4{hh[0] * hh[0], hh[1] * hh[1], hh[2] * hh[2], hh[3] * hh[3]};
+                        *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) =
+                            f4{hh[4] * hh[4], hh[5] * hh[5], hh[6] * hh[6], hh[7] * hh[7]};
                     }
                     if (I == 0) *reinterpret_cast<h8*>(&sm.rbs[r][ch]) = rb16[ks];
                 }
@@ -1213,11 +1190,40 @@ void chunk_ws_kernel(
                     sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
                     sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
                 }
-                if (direct) {  // entry-by-entry k-steps, by row (same wave: LDS in order)
-                    f4* pa = reinterpret_cast<f4*>(&sm.gp[part][2 * I][r][4 * g4]);
-                    f4* pp = reinterpret_cast<f4*>(&sm.gp[part][2 * I + 1][r][4 * g4]);
-                    *pa = *pa + oa;
-                    *pp = *pp + op;
+                if (redo) {
+                    // Exponents beyond the fp32 range of the half-total reference:
+                    // the wave's phase 1 again, entry by entry from its raw inputs
+                    // (read again, so nothing stays live for this rare case), over
+                    // everything written above (the same wave's LDS writes
+                    // complete in order).
+                    const int64_t cs = t0 + static_cast<int64_t>(c + 2) * C;
+                    const uint32_t vld = valid_at(cs);
+                    const int64_t cb = (cs * H + h) * D;
+                    const auto rk = rsrc(k + cb, vld * rowe * 2), rq = rsrc(q + cb, vld * rowe * 2);
+                    const auto rg = rsrc(g + cb, vld * rowe * 4);
+                    f4 oa = {0.f, 0.f, 0.f, 0.f}, op = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int ch = CPG * part + 32 * ks + 8 * g4;
+                        const int off = tok * rowe + ch;
+                        const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
+                        float gr[8], et[8], kr[8], qr[8];
+                        unpack_bf16x8(bload16(rk, 2 * off), kr);
+                        unpack_bf16x8(bload16(rq, 2 * off), qr);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            gr[m] = __uint_as_float(a0[m]);
+                            gr[4 + m] = __uint_as_float(a1[m]);
+                        }
+                        phase1_direct<true>(kr, qr, gr, g4, l16[ks], q16[ks], rb16[ks], et, oa, op);
+                        if (r == 15) {
+                            *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{et[0], et[1], et[2], et[3]};
+                            *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{et[4], et[5], et[6], et[7]};
+                        }
+                        if (I == 0) *reinterpret_cast<h8*>(&sm.rbs[r][ch]) = rb16[ks];
+                    }
+                    *reinterpret_cast<f4*>(&sm.gp[part][2 * I][r][4 * g4]) = oa;
+                    *reinterpret_cast<f4*>(&sm.gp[part][2 * I + 1][r][4 * g4]) = op;
                 }
             };
             if (gwork && I == 1) phase1();
