@@ -14,7 +14,11 @@ include/kda.h); this package is a thin binding over it:
     fused_recurrent_fwd(q, k, v, g, beta, scale, state) -> o
                                      a short run of tokens per sequence
                                      (T <= 64), state in place
+    chunk_fwd_noalloc(q, k, v, g, beta, scale, ...) -> (o, final_state)
+                                     chunk_fwd with the library's own
+                                     workspace (no device allocation)
 """
-from ._lib import (KDAError, abi_version, chunk_fwd, chunk_fwd_snapshots, decode_step,  # noqa: F401
+from ._lib import (KDAError, abi_version, chunk_fwd, chunk_fwd_noalloc, chunk_fwd_snapshots,  # noqa: F401
+                   decode_step,
                    fused_gate, fused_recurrent_fwd, lib, snapshot_rows, snapshots_workspace_size, status_str,
                    workspace_size)

@@ -25,7 +25,8 @@ VARIANTS = {"auto": 0, "recurrent": 1, "chunk": 2, "chunk_scan": 3, "chunk64": 4
 EXPORTS = ("kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd", "kda_decode_step", "kda_fused_recurrent_fwd",
            "kda_chunk_fwd_snapshots_workspace_size", "kda_chunk_fwd_snapshots",
-           "kda_chunk_fwd_gated", "kda_fused_gate")
+           "kda_chunk_fwd_gated", "kda_fused_gate", "kda_chunk_fwd_noalloc")
+NOALLOC_MAX_WORKSPACE = 32 << 20
 FUSED_RECURRENT_MAX_T = 64
 
 
@@ -67,6 +68,10 @@ def _load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_gated.restype = ctypes.c_int
     lib.kda_fused_gate.argtypes = [P, P, P, P, I32, I32, I32, I32, ctypes.c_int, P, P, P]
     lib.kda_fused_gate.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P,
+                                          I32, I32, I32, I32, I32, I32, ctypes.c_int, ctypes.c_int,
+                                          P, P, ctypes.c_int, P]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     return lib
 
 
@@ -151,7 +156,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               snapshot_interval: Optional[int] = None,
               snapshots: Optional[torch.Tensor] = None,
               out_gate: Optional[torch.Tensor] = None,
-              norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6):
+              norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-6,
+              _noalloc: bool = False):
     """kda_chunk_fwd on torch tensors.  q, k, g: [B, T, H, dk]; v: [B, T, H, dv];
     beta: [B, T, H]; initial_state [N, H, dk, dv] fp32 or None; cu_seqlens int32
     [N+1] (device tensor, CPU tensor, numpy array or list) or None.  A caller
@@ -210,6 +216,14 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
             VARIANTS[variant], _stream(dev))
         _check(code)
         return o, final_state, snapshots
+    if _noalloc:
+        code = lib.kda_chunk_fwd_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(initial_state),
+            _ptr(cu_dev), None if cu_host is None else ctypes.c_void_p(cu_host.data_ptr()),
+            B, T, H, dk, dv, N, _dt(q.dtype), _dt(o.dtype), _ptr(o), _ptr(final_state),
+            VARIANTS[variant], _stream(dev))
+        _check(code)
+        return o, final_state
     ws_bytes = workspace_size(B, T, H, dk, dv, N, q.dtype, variant, cu_host)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -233,6 +247,17 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         VARIANTS[variant], _stream(dev))
     _check(code)
     return o, final_state
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None, **kw):
+    """kda_chunk_fwd_noalloc: chunk_fwd whose workspace is the library's own
+    per-GPU device array (at most NOALLOC_MAX_WORKSPACE bytes), so the C call
+    allocates nothing; pass o and final_state to allocate nothing here either.
+    Calls on one GPU must not overlap.  No snapshots or gated output."""
+    for bad in ("workspace", "snapshot_interval", "snapshots", "out_gate", "norm_weight"):
+        if kw.get(bad) is not None:
+            raise ValueError(f"chunk_fwd_noalloc takes no {bad}")
+    return chunk_fwd(q, k, v, g, beta, scale, initial_state, cu_seqlens, _noalloc=True, **kw)
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

@@ -192,6 +192,32 @@ kda_status kda_fused_gate(const void* z, const void* w_up, const float* b_up, co
                           int32_t M, int32_t r, int32_t H, int32_t d_k, kda_dtype in_dtype,
                           float* g, float* beta, void* stream);
 
+/* Largest workspace kda_chunk_fwd_noalloc can provide (32 MiB per GPU). */
+#define KDA_CHUNK_FWD_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+
+/* kda_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * It takes no workspace: the workspace is a device array of
+ * KDA_CHUNK_FWD_NOALLOC_MAX_WORKSPACE bytes built into the library, one per
+ * GPU, held until the process ends.  The call itself allocates nothing.
+ * Every argument, output and error behaviour is that of kda_chunk_fwd, plus:
+ *  - if the workspace kda_chunk_fwd_workspace_size() gives for these
+ *    arguments exceeds the maximum, AUTO falls back to KDA_VARIANT_CHUNK
+ *    (one work item per sequence) when that fits; otherwise the call returns
+ *    KDA_ERR_WORKSPACE and launches nothing;
+ *  - all calls on one GPU share its array (its contents on entry do not
+ *    matter): calls that overlap on one GPU, from two streams or two host
+ *    threads, race and must be serialised by the caller;
+ *  - the first call on a device resolves that device's array address
+ *    (hipGetSymbolAddress) with the current device; the stream must belong
+ *    to the current device. */
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, float scale, const float* initial_state,
+                                 const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                 int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
+                                 int32_t N, kda_dtype in_dtype, kda_dtype out_dtype, void* o,
+                                 float* final_state, kda_variant variant, void* stream);
+
 /* Bytes of device workspace kda_chunk_fwd_snapshots needs (the same
  * arguments as kda_chunk_fwd_workspace_size plus the snapshot interval);
  * 0 for arguments it would reject. */

@@ -241,3 +241,16 @@ def test_fused_gate_validation():
     assert fgate(g=addr(0, 512)) == ALIAS                 # g over z
     assert fgate(beta=addr(3, 1024)) == ALIAS             # beta inside g
     assert fgate(M=0) == OK
+
+
+def test_noalloc_rejects_workspace_beyond_its_array():
+    """kda_chunk_fwd_noalloc checks the workspace size on the host before any
+    HIP call: an explicit segment scan over one long sequence needs more than
+    the library's array and is refused (fake pointers, nothing launched)."""
+    T, H = 1 << 20, 32
+    need = kda.workspace_size(1, T, H, 128, 128, 1, variant="chunk_scan")
+    assert need > _lib.NOALLOC_MAX_WORKSPACE
+    rc = kda.lib.kda_chunk_fwd_noalloc(addr(0), addr(1), addr(2), addr(3), addr(4), 0.1, None, None,
+                                       None, 1, T, H, 128, 128, 1, BF16, F32, addr(5), addr(6),
+                                       3, None)
+    assert rc == WS
