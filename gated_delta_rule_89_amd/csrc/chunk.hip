@@ -70,10 +70,10 @@ struct ChunkItem {
 
 // Scan over the segment maps of one sequence (all heads).
 struct ScanItem {
-    int32_t first_map;  // slot of the first segment's map
-    int32_t nmaps;      // number of maps (segments - 1)
+    int32_t first_seg;  // index of the sequence's first segment
+    int32_t nseg;       // its number of segments (a single one needs no scan)
     int32_t h0;         // row of h0 or -1 for zero
-    int32_t first_seg;  // staged-state slot of the first segment
+    int32_t hT;         // row of the final state or -1 for none
 };
 
 namespace chunkk {
@@ -317,6 +317,18 @@ __device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, int voff, f4 y,
     __builtin_amdgcn_raw_buffer_store_b64(p, r, voff, 0, 0);
 }
 
+// 4 consecutive values of one lane (16 bytes fp32, 8 bytes bf16), widened to fp32.
+__device__ __forceinline__ f4 load4(__amdgpu_buffer_rsrc_t r, int voff, float*) {
+    const u4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+    return f4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3])};
+}
+__device__ __forceinline__ f4 load4(__amdgpu_buffer_rsrc_t r, int voff, bf16_t*) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+    return f4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+              __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+}
+
 __device__ __forceinline__ h8 cat(h4 a, h4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -370,6 +382,21 @@ __device__ __forceinline__ void store_state(float* __restrict__ dst, const f4 (&
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) bstore(rd, vo, ((16 * rt + i) * D + 16 * ct) * 4, S[rt][ct][i] * un, dst);
+}
+
+// Adds the state columns a wave holds (as store_state) to a d_k x d_v matrix.
+template <int NCT>
+__device__ __forceinline__ void add_state(float* __restrict__ dst, const f4 (&S)[8][NCT], float un,
+                                          int g4, int r, int col) {
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float* p = dst + (16 * rt + 4 * g4 + i) * D + col + 16 * ct + r;
+                *p += S[rt][ct][i] * un;
+            }
 }
 
 // NW waves; each owns NCT 16-column tiles of the state; chunks of NSB
@@ -988,10 +1015,21 @@ struct alignas(16) Smem {
     float a[NSB][SB][20];                // A_JJ = Diag(beta) G_JJ, strictly lower, by row
     float etot[NSB][D];
     float beta[2][C];                    // beta of the chunks in phases 1-2 and 3 (by chunk parity)
+    int alive[NSW];                      // propagation modes: state wave still nonzero in fp16
 };
 }  // namespace ws
 
-template <typename Tout, bool SNAP, bool GATED>
+// Modes of the 12-wave kernel.  FULL: the chunked prefill of a sequence or
+// segment.  MAP and CORR propagate a d_k x d_k matrix X through a segment with
+// v = 0 (X <- Diag(Lambda) X + K-bar^T Delta, Delta = -T K~ X): MAP from the
+// identity, storing X at the end (the segment's state map); CORR from the
+// segment's true initial state, adding X's read-out scale (Q~ X + P Delta)
+// to o (and X to the state snapshots).  Both stop as soon as the fp16 copy
+// of X is zero on every state wave: with g <= 0 X can then only shrink and
+// every later product it feeds is exactly zero.
+enum { MODE_FULL = 0, MODE_MAP = 1, MODE_CORR = 2 };
+
+template <typename Tout, bool SNAP, bool GATED, int MODE = MODE_FULL>
 __global__ __launch_bounds__(ws::NW * 64) __attribute__((amdgpu_waves_per_eu(ws::NW / 4)))
 void chunk_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -999,8 +1037,11 @@ void chunk_ws_kernel(
     const float* __restrict__ beta, float scale, const ChunkItem* __restrict__ items, int H,
     const float* __restrict__ h0, const float* __restrict__ staged, Tout* __restrict__ o,
     float* __restrict__ out_state, float* __restrict__ snaps, int interval,
-    const uint16_t* __restrict__ ogate, const float* __restrict__ nweight, float neps) {
+    const uint16_t* __restrict__ ogate, const float* __restrict__ nweight, float neps,
+    float* __restrict__ bout, int* __restrict__ mflags) {
     using namespace ws;
+    static_assert(MODE == MODE_FULL || !GATED, "the gated epilogue needs the whole read-out");
+    constexpr bool PROP = MODE != MODE_FULL;
     __shared__ ws::Smem sm;
 
     const int tid = threadIdx.x;
@@ -1046,7 +1087,7 @@ void chunk_ws_kernel(
             const uint32_t vld = valid_at(cs);
             const int64_t cb = (cs * H + h) * D;
             const auto rk = rsrc(k + cb, vld * rowe * 2);
-            const auto rq = rsrc(q + cb, vld * rowe * 2);
+            const auto rq = rsrc(q + cb, MODE == MODE_MAP ? 0u : vld * rowe * 2);  // no read-out in MAP
             const auto rg = rsrc(g + cb, vld * rowe * 4);
             // beta is read by the channel-part-0 waves only (an empty range for the others)
             const auto rb = rsrc(beta + cs * H + h, part == 0 ? vld * H * 4 : 0u);
@@ -1062,6 +1103,7 @@ void chunk_ws_kernel(
             bt = bload4(rb, 4 * tok * H);
         };
         auto fetch_v = [&](int64_t cs) {  // v (and the output gate) in the staging layout
+            if (PROP) return;  // v = 0 when a matrix is propagated
             const auto rv = rsrc(v + (cs * H + h) * D, valid_at(cs) * rowe * 2);
             const auto rog = rsrc(ogate + (cs * H + h) * D, GATED ? valid_at(cs) * rowe * 2 : 0u);
 #pragma unroll
@@ -1230,7 +1272,7 @@ void chunk_ws_kernel(
             fetch_gate(t0 + static_cast<int64_t>(c + 3) * C);
             if (gwork && I == 0) phase1();
             __syncthreads();
-            if (gwork) {  // v (and the output gate) of chunk c + 2
+            if (gwork && !PROP) {  // v (and the output gate) of chunk c + 2
 #pragma unroll
                 for (int j = 0; j < VU; ++j) {
                     const int e = gtid + GT * j, vt = e >> 4, vc = (e & 15) * 8;
@@ -1304,6 +1346,9 @@ void chunk_ws_kernel(
             }
             fetch_v(t0 + static_cast<int64_t>(c + 3) * C);
             __syncthreads();
+            // propagation modes: stop with the state waves once X is zero in fp16
+            if (PROP && c + 1 >= 0 && c + 1 < nch && !(sm.alive[0] | sm.alive[1] | sm.alive[2] | sm.alive[3]))
+                break;
         }
     } else {
         // ---- state waves: S[16 rt + 4 g4 + i][col + 16 ct + r] * 2^ex in S[rt][ct][i]
@@ -1311,6 +1356,7 @@ void chunk_ws_kernel(
         f4 S[8][NCT];
         int ex = 0;
         h8 d16[NCT];      // fp16 Delta (B operand of P Delta, K-bar^T Delta), chunk-local
+        bool exited = false;  // propagation modes: X became zero in fp16
         {
             const float* src = nullptr;
             if (it.sin >= 0 && h0) src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
@@ -1318,8 +1364,11 @@ void chunk_ws_kernel(
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
-            if (src) {
+                for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)  // MAP starts from the identity
+                        S[rt][ct][i] = (MODE == MODE_MAP && 16 * rt + 4 * g4 + i == col + 16 * ct + r) ? 1.f : 0.f;
+            if (src && MODE != MODE_MAP) {
 #pragma unroll
                 for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -1365,7 +1414,7 @@ void chunk_ws_kernel(
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        vv[rt][ct][i] = bf16_to_f32(t.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
+                        vv[rt][ct][i] = PROP ? 0.f : bf16_to_f32(t.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
             float mv = 0.f;
 #pragma unroll
             for (int rt = 0; rt < NSB; ++rt)
@@ -1460,13 +1509,13 @@ void chunk_ws_kernel(
                         d16[ct][4 + m] = static_cast<_Float16>(d1[m]);
                     }
                 }
-                // o of chunk c, right after its Delta
+                // o of chunk c, right after its Delta (no read-out in MAP mode)
                 const float os = scale * ldexpf(1.f, -ex);
                 const int vlim = valid - 4 * g4;  // rows of this lane group still inside the chunk
                 const auto ro = rsrc(o + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * sizeof(Tout));
                 const int vo = static_cast<int>(((4 * g4) * rowe + col + r) * sizeof(Tout));
 #pragma unroll
-                for (int rt = 0; rt < NSB; ++rt) {
+                for (int rt = 0; rt < (MODE == MODE_MAP ? 0 : NSB); ++rt) {
                     h8 qf8[4];
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks)
@@ -1493,7 +1542,7 @@ void chunk_ws_kernel(
                         }
                     }
                 }
-                            if (GATED) {  // the output gate of this wave's epilogue rows, before its tile is reused
+                if (GATED) {  // the output gate of this wave's epilogue rows, before its tile is reused
                     const int el = epi_lane(), erow = 8 * (w & 3) + (el >> 3), ecol = 16 * (el & 7);
                     ogr[0] = *reinterpret_cast<const u4*>(&cur.og[erow][ecol]);
                     ogr[1] = *reinterpret_cast<const u4*>(&cur.og[erow][ecol + 8]);
@@ -1506,7 +1555,9 @@ void chunk_ws_kernel(
                     for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = mfma16(kb8, d16[ct], S[rt][ct] * lam);
                 }
                 if (snapping && it.p0 + (c0 + valid - t0) == sc.next) {
-                    store_state<NCT>(snaps + (sc.row * H + h) * D * D, S, ldexpf(1.f, -ex), g4, r, col);
+                    float* dst = snaps + (sc.row * H + h) * D * D;
+                    if (MODE == MODE_CORR) add_state<NCT>(dst, S, ldexpf(1.f, -ex), g4, r, col);
+                    else store_state<NCT>(dst, S, ldexpf(1.f, -ex), g4, r, col);
                     sc.next += interval;
                     ++sc.row;
                 }
@@ -1521,13 +1572,16 @@ void chunk_ws_kernel(
                     // o rows of chunk c from the LDS tile: this wave stores tokens
                     // 8 w .. 8 w + 7, two whole rows per 16-byte-per-lane store.
                     // Rows past the end of the sequence fall outside the buffer range.
+                    // CORR adds to the o the zero-start pass wrote; MAP has no o.
                     const auto ro = rsrc(o + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * sizeof(Tout));
                     const int el = epi_lane(), c4 = 4 * (el & 31);
 #pragma unroll
-                    for (int k2 = 0; k2 < 4; ++k2) {
+                    for (int k2 = 0; k2 < (MODE == MODE_MAP ? 0 : 4); ++k2) {
                         const int row = 8 * (w & 3) + 2 * k2 + (el >> 5);
-                        store4(ro, (row * rowe + c4) * static_cast<int>(sizeof(Tout)),
-                               *reinterpret_cast<const f4*>(&sm.otile[row][c4]), o);
+                        const int off = (row * rowe + c4) * static_cast<int>(sizeof(Tout));
+                        f4 y = *reinterpret_cast<const f4*>(&sm.otile[row][c4]);
+                        if (MODE == MODE_CORR) y += load4(ro, off, o);
+                        store4(ro, off, y, o);
                     }
                 }
                 if (GATED) {
@@ -1562,12 +1616,37 @@ void chunk_ws_kernel(
                     }
                 }
             }
-            if (c + 1 >= 0 && c + 1 < nch) prepare(nxt, GATED ? msw : state_max());  // v of chunk c + 1 staged two intervals ago
+            if (c + 1 >= 0 && c + 1 < nch) {  // v of chunk c + 1 staged two intervals ago
+                if (!PROP) {
+                    prepare(nxt, GATED ? msw : state_max());
+                } else {
+                    // X is dead on this wave once its fp16 copy (at the new exponent)
+                    // rounds to zero everywhere: max below 2^-25.
+                    const float m0 = state_max();
+                    const int e0 = ex;
+                    prepare(nxt, m0);
+                    if (l == 0) sm.alive[w] = m0 * ldexpf(1.f, ex - e0) >= 0x1p-25f ? 1 : 0;
+                }
+            }
             __syncthreads();
+            if (PROP && c + 1 >= 0 && c + 1 < nch && !(sm.alive[0] | sm.alive[1] | sm.alive[2] | sm.alive[3])) {
+                exited = true;
+                break;
+            }
         }
-        if (it.sout >= 0 && out_state) {
+        // Final state (FULL: sout >= 0 a row of the output, <= -2 a row of the
+        // segment-state buffer); MAP: the segment's map, or only its zero flag.
+        float* dst = nullptr;
+        if (MODE == MODE_FULL && it.sout >= 0 && out_state)
+            dst = out_state + (static_cast<int64_t>(it.sout) * H + h) * D * D;
+        else if (MODE == MODE_FULL && it.sout <= -2 && bout)
+            dst = bout + (static_cast<int64_t>(-it.sout - 2) * H + h) * D * D;
+        else if (MODE == MODE_MAP && it.sout >= 0) {
+            if (w == 0 && l == 0) mflags[static_cast<int64_t>(it.sout) * H + h] = exited ? 0 : 1;
+            if (!exited) dst = out_state + (static_cast<int64_t>(it.sout) * H + h) * D * D;
+        }
+        if (dst) {
             const float un = ldexpf(1.f, -ex);
-            float* dst = out_state + (static_cast<int64_t>(it.sout) * H + h) * D * D;
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -1581,17 +1660,23 @@ void chunk_ws_kernel(
 
 }
 
-// Initial states of every segment, staged in the workspace: S_0 = h0 (or
-// zero) and S_{j+1} = M_j S_j + B_j along each sequence, for every head.
-// Staging S_0 too means the segment pass never reads the caller's initial
-// state, so an in-place final state cannot race with it.  One workgroup of 4 waves per
-// (sequence, head); wave w owns state columns [32 w, 32 w + 32).  The 128 x 128
-// products run on split bf16 MFMA (hi + lo on both operands, three products),
-// which keeps about 16 significant bits per operand; accumulation is fp32.
+// The true initial state of every segment of a sequence cut into segments:
+// S_0 = h0 (or zero), S_{j+1} = B_j + M_j S_j, where B_j is segment j's
+// final state from a zero start and M_j its state map (absent when the map
+// pass found it zero in fp16, or not needed: M_0 with a zero h0, the last map
+// without a final state).  S_j (j >= 1, and S_0 when h0 is given) is staged
+// for the correction pass; the last one is the sequence's final state.  The
+// caller's initial state is read only here and before any final state is
+// written, so an in-place final state cannot race.  One workgroup of 4 waves
+// per (sequence, head); wave w owns state columns [32 w, 32 w + 32).  The
+// 128 x 128 products run on split bf16 MFMA (hi + lo on both operands, three
+// products), about 16 significant bits per operand, fp32 accumulation.
 __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
     const ScanItem* __restrict__ sitems, int H, const float* __restrict__ h0,
-    const float* __restrict__ maps, float* __restrict__ staged) {
+    const float* __restrict__ bst, const float* __restrict__ maps, const int* __restrict__ mflags,
+    float* __restrict__ staged, float* __restrict__ final_state) {
     const ScanItem it = sitems[blockIdx.x / H];
+    if (it.nseg < 2) return;  // whole workgroup: a single segment ran with its own states
     const int h = blockIdx.x % H;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g4 = l >> 4;
     const int col = 32 * w;
@@ -1604,8 +1689,7 @@ __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 S[rt][ct][i] = src ? src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] : 0.f;
-    auto stage = [&](int slot) {
-        float* dst = staged + (static_cast<int64_t>(slot) * H + h) * D * D;
+    auto put = [&](float* dst) {
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -1613,52 +1697,64 @@ __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] = S[rt][ct][i];
     };
-    stage(it.first_seg);
+    auto row_of = [&](const float* base, int64_t slot) { return base + (slot * H + h) * D * D; };
+    if (src) put(staged + (static_cast<int64_t>(it.first_seg) * H + h) * D * D);
 
-    for (int j = 0; j < it.nmaps; ++j) {
-        const float* mp = maps + (static_cast<int64_t>(it.first_map + j) * H + h) * D * (2 * D);
-        // B operands from S (k = rows of S, permuted as in the chunk kernel), split hi/lo.
-        b8 sh[4][2], sl[4][2];
+    for (int j = 0; j < it.nseg; ++j) {
+        const int64_t sj = it.first_seg + j;
+        const bool last = j + 1 == it.nseg;
+        if (last && it.hT < 0) break;  // no final state wanted
+        const float* bj = row_of(bst, sj);
+        const bool use_map = (j > 0 || src) && mflags[sj * H + h] != 0;  // wave-uniform
+        f4 acc[8][2];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const float x = m < 4 ? S[2 * ks][ct][m] : S[2 * ks + 1][ct][m - 4];
-                    sh[ks][ct][m] = static_cast<__bf16>(x);
-                    sl[ks][ct][m] = static_cast<__bf16>(x - static_cast<float>(sh[ks][ct][m]));
-                }
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt) {
-            f4 acc[2];
+        for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[ct][i] = mp[(16 * rt + 4 * g4 + i) * (2 * D) + col + 16 * ct + r];
-            const float* mrow = mp + (16 * rt + r) * (2 * D) + D;  // row of M
+                for (int i = 0; i < 4; ++i) acc[rt][ct][i] = bj[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
+        if (use_map) {
+            const float* mp = row_of(maps, sj);
+            // B operands from S (k = rows of S, permuted as in the chunk kernel), split hi/lo.
+            b8 sh[4][2], sl[4][2];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const f4 lo4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 4 * g4);
-                const f4 hi4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 16 + 4 * g4);
-                b8 ah, al;
+            for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const float x = m < 4 ? lo4[m] : hi4[m - 4];
-                    ah[m] = static_cast<__bf16>(x);
-                    al[m] = static_cast<__bf16>(x - static_cast<float>(ah[m]));
-                }
+                for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    acc[ct] = mfmab(ah, sh[ks][ct], acc[ct]);
-                    acc[ct] = mfmab(ah, sl[ks][ct], acc[ct]);
-                    acc[ct] = mfmab(al, sh[ks][ct], acc[ct]);
+                    for (int m = 0; m < 8; ++m) {
+                        const float x = m < 4 ? S[2 * ks][ct][m] : S[2 * ks + 1][ct][m - 4];
+                        sh[ks][ct][m] = static_cast<__bf16>(x);
+                        sl[ks][ct][m] = static_cast<__bf16>(x - static_cast<float>(sh[ks][ct][m]));
+                    }
+#pragma unroll
+            for (int rt = 0; rt < 8; ++rt) {
+                const float* mrow = mp + (16 * rt + r) * D;  // row of M
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const f4 lo4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 4 * g4);
+                    const f4 hi4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 16 + 4 * g4);
+                    b8 ah, al;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        const float x = m < 4 ? lo4[m] : hi4[m - 4];
+                        ah[m] = static_cast<__bf16>(x);
+                        al[m] = static_cast<__bf16>(x - static_cast<float>(ah[m]));
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        acc[rt][ct] = mfmab(ah, sh[ks][ct], acc[rt][ct]);
+                        acc[rt][ct] = mfmab(ah, sl[ks][ct], acc[rt][ct]);
+                        acc[rt][ct] = mfmab(al, sh[ks][ct], acc[rt][ct]);
+                    }
                 }
             }
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) S[rt][ct] = acc[ct];
         }
-        stage(it.first_seg + j + 1);
+#pragma unroll
+        for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) S[rt][ct] = acc[rt][ct];
+        put(last ? final_state + (static_cast<int64_t>(it.hT) * H + h) * D * D : staged + ((sj + 1) * H + h) * D * D);
     }
 }
 
@@ -1684,16 +1780,25 @@ __global__ void plan_sequences_kernel(const int32_t* __restrict__ cu, int N, int
     items[rank] = ChunkItem{a, b, has_h0 ? n : -1, has_hT ? n : -1, 0, snap_base ? snap_base[n] : -1, 0};
 }
 
-// Segments of every sequence (seg tokens each, the last one shorter), the
-// map items of all segments but the last, and one scan item per sequence.
+// Work items of the segmented path.  Each sequence is cut into segments of
+// seg tokens (the last one shorter); a sequence with a single segment runs as
+// one FULL item with its own initial and final states.  For the others,
+// segment j (state slot z, numbered over the split sequences only) gets: a
+// FULL item from a zero state writing its final state to row z of the
+// segment-state buffer (sout = -2 - z); a MAP item (sout = z) when its map is
+// needed (j > 0 or h0 given; j < last or a final state wanted), else an
+// empty one (no tokens, sout = -1); a CORR item from staged state z (sin = -2 - z) when
+// that state can be nonzero (j > 0 or h0 given), else an empty one (no
+// tokens).  Items are numbered over all segments; one scan item per sequence.
 // A single workgroup walks the sequences in blocks of 256 with a block scan.
 __global__ __launch_bounds__(256) void plan_segments_kernel(
     const int32_t* __restrict__ cu, int N, int T, int seg, int has_h0, int has_hT,
-    const int32_t* __restrict__ snap_base, ChunkItem* __restrict__ seg_items,
-    ChunkItem* __restrict__ map_items, ScanItem* __restrict__ scan_items) {
-    __shared__ int sc[256];
-    __shared__ int base;
-    if (threadIdx.x == 0) base = 0;
+    const int32_t* __restrict__ snap_base, ChunkItem* __restrict__ full_items,
+    ChunkItem* __restrict__ map_items, ChunkItem* __restrict__ corr_items,
+    ScanItem* __restrict__ scan_items) {
+    __shared__ int sc[256], sc2[256];
+    __shared__ int base, base2;
+    if (threadIdx.x == 0) base = base2 = 0;
     __syncthreads();
     for (int n0 = 0; n0 < N; n0 += 256) {
         const int n = n0 + threadIdx.x;
@@ -1705,31 +1810,47 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(
             const int64_t len = b - a;
             G = len > 0 ? static_cast<int>((len + seg - 1) / seg) : 1;
         }
+        const int Gs = G > 1 ? G : 0;  // state slots (split sequences only)
         sc[threadIdx.x] = G;
+        sc2[threadIdx.x] = Gs;
         __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of G
+        for (int off = 1; off < 256; off <<= 1) {  // inclusive scans of G and Gs
             const int x = threadIdx.x >= off ? sc[threadIdx.x - off] : 0;
+            const int y = threadIdx.x >= off ? sc2[threadIdx.x - off] : 0;
             __syncthreads();
             sc[threadIdx.x] += x;
+            sc2[threadIdx.x] += y;
             __syncthreads();
         }
-        const int segs_before = base + sc[threadIdx.x] - G;  // segments of earlier sequences
-        const int maps_before = segs_before - n;             // each earlier sequence has G - 1 maps
+        const int s0 = base + sc[threadIdx.x] - G;      // items of earlier sequences
+        const int z0 = base2 + sc2[threadIdx.x] - Gs;   // state slots of earlier sequences
         if (n < N) {
-            for (int gi = 0; gi < G; ++gi) {
-                const int64_t sa = a + static_cast<int64_t>(gi) * seg;
+            const int snap = snap_base ? snap_base[n] : -1;
+            const int h0row = has_h0 ? n : -1, hTrow = has_hT ? n : -1;
+            for (int j = 0; j < G; ++j) {
+                const int64_t sa = a + static_cast<int64_t>(j) * seg;
                 const int64_t sb = sa + seg < b ? sa + seg : b;
-                const int sin = -2 - (segs_before + gi);  // staged by the scan
-                const int sout = gi == G - 1 ? (has_hT ? n : -1) : -1;
-                seg_items[segs_before + gi] =
-                    ChunkItem{sa, sb, sin, sout, sa - a, snap_base ? snap_base[n] : -1, 0};
-                if (gi < G - 1)
-                    map_items[maps_before + gi] = ChunkItem{sa, sb, -1, maps_before + gi, sa - a, -1, 0};
+                const int si = s0 + j, zi = z0 + j;
+                if (G == 1) {
+                    full_items[si] = ChunkItem{sa, sb, h0row, hTrow, 0, snap, 0};
+                    map_items[si] = ChunkItem{sa, sa, -1, -1, 0, -1, 0};
+                    corr_items[si] = ChunkItem{sa, sa, -1, -1, 0, -1, 0};
+                    continue;
+                }
+                const bool live_in = j > 0 || has_h0;
+                full_items[si] = ChunkItem{sa, sb, -1, -2 - zi, sa - a, snap, 0};
+                map_items[si] = (live_in && (j + 1 < G || has_hT)) ? ChunkItem{sa, sb, -1, zi, sa - a, -1, 0}
+                                                                   : ChunkItem{sa, sa, -1, -1, sa - a, -1, 0};
+                corr_items[si] = live_in ? ChunkItem{sa, sb, -2 - zi, -1, sa - a, snap, 0}
+                                         : ChunkItem{sa, sa, -1, -1, sa - a, -1, 0};
             }
-            scan_items[n] = ScanItem{maps_before, G - 1, has_h0 ? n : -1, segs_before};
+            scan_items[n] = ScanItem{z0, G, h0row, hTrow};
         }
         __syncthreads();
-        if (threadIdx.x == 255) base += sc[255];
+        if (threadIdx.x == 255) {
+            base += sc[255];
+            base2 += sc2[255];
+        }
         __syncthreads();
     }
 }
@@ -1773,36 +1894,46 @@ __global__ __launch_bounds__(256) void snap_base_kernel(const int32_t* __restric
     }
 }
 
-// Host mirror of the segment plan (same formula as plan_segments_kernel).
-void count_segments(const int32_t* cu_host, int N, int T, int seg, int64_t* nseg, int64_t* nmap) {
-    int64_t s = 0, m = 0;
+// Host mirror of the segment plan (same formulas as plan_segments_kernel):
+// items (all segments), state slots (segments of split sequences) and the
+// number of split sequences.
+struct SegCount {
+    int64_t nseg, nslot, nsplit;
+};
+SegCount count_segments(const int32_t* cu_host, int N, int T, int seg) {
+    SegCount c{0, 0, 0};
     for (int n = 0; n < N; ++n) {
         const int64_t len = cu_host ? cu_host[n + 1] - cu_host[n] : T;
         const int64_t G = len > 0 ? (len + seg - 1) / seg : 1;
-        s += G;
-        m += G - 1;
+        c.nseg += G;
+        if (G > 1) {
+            c.nslot += G;
+            ++c.nsplit;
+        }
     }
-    *nseg = s;
-    *nmap = m;
+    return c;
 }
 
 struct ScanLayout {
-    size_t seg_items, map_items, scan_items, maps, staged, total;
+    size_t full_items, map_items, corr_items, scan_items, flags, bst, maps, staged, total;
 };
 
-ScanLayout scan_layout(int64_t nseg, int64_t nmap, int N, int H) {
+ScanLayout scan_layout(const SegCount& c, int N, int H) {
     ScanLayout L{};
+    const size_t state = static_cast<size_t>(c.nslot) * H * chunkk::D * chunkk::D * sizeof(float);
     size_t off = 0;
-    L.seg_items = off;
-    off = align256(off + nseg * sizeof(ChunkItem));
-    L.map_items = off;
-    off = align256(off + nmap * sizeof(ChunkItem));
-    L.scan_items = off;
-    off = align256(off + static_cast<size_t>(N) * sizeof(ScanItem));
-    L.maps = off;
-    off = align256(off + static_cast<size_t>(nmap) * H * chunkk::D * 2 * chunkk::D * sizeof(float));
-    L.staged = off;
-    off = align256(off + static_cast<size_t>(nseg) * H * chunkk::D * chunkk::D * sizeof(float));
+    auto take = [&](size_t& at, size_t bytes) {
+        at = off;
+        off = align256(off + bytes);
+    };
+    take(L.full_items, c.nseg * sizeof(ChunkItem));
+    take(L.map_items, c.nseg * sizeof(ChunkItem));
+    take(L.corr_items, c.nseg * sizeof(ChunkItem));
+    take(L.scan_items, static_cast<size_t>(N) * sizeof(ScanItem));
+    take(L.flags, static_cast<size_t>(c.nslot) * H * sizeof(int));
+    take(L.bst, state);
+    take(L.maps, state);
+    take(L.staged, state);
     L.total = off;
     return L;
 }
@@ -1835,15 +1966,18 @@ int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host) {
 size_t chunk_workspace_bytes(int B, int T, int H, int N, const int32_t* cu_host, bool scan) {
     if (!scan) return align256(static_cast<size_t>(N) * sizeof(ChunkItem));
     const int seg = chunk_segment_tokens(B, T, H, N, cu_host);
-    int64_t nseg, nmap;
-    count_segments(cu_host, N, T, seg, &nseg, &nmap);
-    return scan_layout(nseg, nmap, N, H).total;
+    return scan_layout(count_segments(cu_host, N, T, seg), N, H).total;
 }
 
 hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
     using namespace chunkk;
     char* ws = static_cast<char*>(a.ws);
-    auto launch_full = [&](const ChunkItem* items, int64_t nitems, const float* staged) {
+    // FULL items (mode 0), or the MAP (1) / CORR (2) propagation passes of the
+    // segmented path; bout and mflags are the segment-state buffer and the
+    // map flags.  fuse_gate: apply the gated RMSNorm in the o store.
+    auto launch_full = [&](const ChunkItem* items, int64_t nitems, const float* staged, int mode = 0,
+                           float* out_state = nullptr, float* bout = nullptr, int* mflags = nullptr,
+                           bool fuse_gate = true) {
         const dim3 grid(static_cast<uint32_t>(nitems * a.H));
         const auto q = static_cast<const uint16_t*>(a.q);
         const auto k = static_cast<const uint16_t*>(a.k);
@@ -1866,10 +2000,22 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
         }
         auto go = [&](auto kernel, auto* o) {
             hipLaunchKernelGGL(kernel, grid, dim3(ws::NW * 64), 0, a.stream, q, k, v, a.g, a.beta, a.scale,
-                               items, a.H, a.h0, staged, o, a.hT, a.snaps, a.snap_interval,
-                               static_cast<const uint16_t*>(a.ogate), a.nweight, a.neps);
+                               items, a.H, a.h0, staged, o, mode == MODE_MAP ? out_state : a.hT,
+                               a.snaps, a.snap_interval, static_cast<const uint16_t*>(a.ogate), a.nweight,
+                               a.neps, bout, mflags);
         };
-        const bool gt = a.ogate != nullptr;
+        if (mode == MODE_MAP) {
+            go(chunk_ws_kernel<float, false, false, MODE_MAP>, of);
+            return;
+        }
+        if (mode == MODE_CORR) {
+            if (a.out_bf16) sn ? go(chunk_ws_kernel<bf16_t, true, false, MODE_CORR>, ob)
+                               : go(chunk_ws_kernel<bf16_t, false, false, MODE_CORR>, ob);
+            else sn ? go(chunk_ws_kernel<float, true, false, MODE_CORR>, of)
+                    : go(chunk_ws_kernel<float, false, false, MODE_CORR>, of);
+            return;
+        }
+        const bool gt = a.ogate != nullptr && fuse_gate;
         if (a.out_bf16) {
             if (gt) go(chunk_ws_kernel<bf16_t, false, true>, ob);
             else if (sn) go(chunk_ws_kernel<bf16_t, true, false>, ob);
@@ -1888,27 +2034,37 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
         launch_full(items, a.N, nullptr);
         return hipGetLastError();
     }
+    // Segmented path: maps (stopping where they vanish), every segment from a
+    // zero state, the scan of the true segment states, then the corrections
+    // from those states (stopping where they vanish).
     const int seg = chunk_segment_tokens(a.B, a.T, a.H, a.N, a.cu_host);
-    int64_t nseg, nmap;
-    count_segments(a.cu_host, a.N, a.T, seg, &nseg, &nmap);
-    const ScanLayout L = scan_layout(nseg, nmap, a.N, a.H);
-    ChunkItem* seg_items = reinterpret_cast<ChunkItem*>(ws + L.seg_items);
+    const SegCount cnt = count_segments(a.cu_host, a.N, a.T, seg);
+    const ScanLayout L = scan_layout(cnt, a.N, a.H);
+    ChunkItem* full_items = reinterpret_cast<ChunkItem*>(ws + L.full_items);
     ChunkItem* map_items = reinterpret_cast<ChunkItem*>(ws + L.map_items);
+    ChunkItem* corr_items = reinterpret_cast<ChunkItem*>(ws + L.corr_items);
     ScanItem* scan_items = reinterpret_cast<ScanItem*>(ws + L.scan_items);
+    int* mflags = reinterpret_cast<int*>(ws + L.flags);
+    float* bst = reinterpret_cast<float*>(ws + L.bst);
     float* maps = reinterpret_cast<float*>(ws + L.maps);
     float* staged = reinterpret_cast<float*>(ws + L.staged);
     hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T, seg,
-                       a.h0 ? 1 : 0, a.hT ? 1 : 0, a.snap_base, seg_items, map_items, scan_items);
-    if (nmap > 0)
-        hipLaunchKernelGGL((chunk_kernel<8, 2, 2, true, 1, float>), dim3(static_cast<uint32_t>(nmap * a.H)),
-                           dim3(8 * 64), 0, a.stream, static_cast<const uint16_t*>(a.q),
-                           static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.g,
-                           a.beta, a.scale, map_items, a.H, static_cast<const float*>(nullptr),
-                           static_cast<const float*>(nullptr), static_cast<float*>(nullptr), maps,
-                           static_cast<float*>(nullptr), 0);
-    hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<uint32_t>(a.N) * a.H), dim3(256), 0,
-                       a.stream, scan_items, a.H, a.h0, maps, staged);
-    launch_full(seg_items, nseg, staged);
+                       a.h0 ? 1 : 0, a.hT ? 1 : 0, a.snap_base, full_items, map_items, corr_items,
+                       scan_items);
+    const bool split = cnt.nsplit > 0;
+    if (split) launch_full(map_items, cnt.nseg, nullptr, MODE_MAP, maps, nullptr, mflags);
+    launch_full(full_items, cnt.nseg, nullptr, MODE_FULL, nullptr, bst, nullptr, !split);
+    if (split) {
+        hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<uint32_t>(a.N) * a.H), dim3(256), 0,
+                           a.stream, scan_items, a.H, a.h0, bst, maps, mflags, staged, a.hT);
+        launch_full(corr_items, cnt.nseg, staged, MODE_CORR);
+        // the gated RMSNorm needs the corrected read-out: applied in place after
+        if (a.ogate) {
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            return launch_gate_norm(a);
+        }
+    }
     return hipGetLastError();
 }
 
