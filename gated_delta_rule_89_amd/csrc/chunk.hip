@@ -17,13 +17,15 @@
 //
 // so one chunk maps S to (Diag(Lambda_last) - K-bar^T W) S + K-bar^T U: a
 // diagonal-plus-low-rank transition, the structure named on that page.  A run
-// of chunks therefore maps S_in to M S_in + B; "map" mode of the kernel below
-// computes (B, M) for a segment by running the same pass on the 128 x 256
-// state [B | M] from [0 | I] (v drives only the B half).
+// of chunks therefore maps S_in to M S_in + B, with B the run's result from a
+// zero state and M the transitions' product; by linearity the read-out from
+// S_in is the zero-start read-out plus that of the propagated S_in alone
+// (v = 0).  Long sequences are cut into segments on that basis (the
+// propagation modes of the 12-wave kernel and segment_scan_kernel).
 //
 // Design on this GPU:
-//  * A chunk is NSB sub-blocks of 16 tokens (C = 16 NSB; 64 tokens in the
-//    full-mode kernel, 32 in map mode); a workgroup of NW waves owns one chain
+//  * A chunk is NSB sub-blocks of 16 tokens (C = 16 NSB: 32 tokens in the
+//    12-wave kernel, 64 in the single-role one); a workgroup owns one chain
 //    segment (one sequence, one head).  Gate-side work (cumulative gates,
 //    Grams, the triangular solves) is split over the waves by sub-block and
 //    channel part; the state pass is split by state columns (columns of S
@@ -62,7 +64,8 @@ namespace kda {
 struct ChunkItem {
     int64_t t0, t1;
     int32_t sin;   // initial state: >= 0 row of h0, <= -2 row (-sin - 2) of the staged states, -1 zero
-    int32_t sout;  // final state (or map slot in map mode): >= 0 row of the output, -1 none
+    int32_t sout;  // final state: >= 0 row of the output (the map slot in MAP mode),
+                   // <= -2 row (-sout - 2) of the segment-state buffer, -1 none
     int64_t p0;    // tokens of the sequence before t0
     int32_t snap;  // row of the sequence's first state snapshot, -1 none
     int32_t pad_;
@@ -399,11 +402,12 @@ __device__ __forceinline__ void add_state(float* __restrict__ dst, const f4 (&S)
             }
 }
 
-// NW waves; each owns NCT 16-column tiles of the state; chunks of NSB
-// sub-blocks.  Full mode: state = S (NW * 16 NCT = 128 columns), writes o and
-// the final state.  Map mode: state = [B | M] (256 columns), no o, writes the
-// segment's (B, M).  WPC workgroups share a CU (it sets the register budget).
-template <int NW, int NSB, int NCT, bool MAP, int WPC, typename Tout, bool SNAP = false>
+// Single-role chunked prefill: NW waves do the gate-side work of each chunk
+// and then its state pass, each wave owning NCT 16-column tiles of S
+// (NW * 16 NCT = 128 columns); chunks of NSB sub-blocks.  Writes o, the final
+// state and the snapshots.  WPC workgroups share a CU (it sets the register
+// budget).
+template <int NW, int NSB, int NCT, int WPC, typename Tout, bool SNAP = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4 * WPC)))
 void chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -422,7 +426,7 @@ void chunk_kernel(
     constexpr int NX = NSB * (NSB - 1) / 2;
     static_assert(NSB == 2 || NSB == 4, "chunks of 32 or 64 tokens");
     static_assert(NP >= 1 && NW % NSB == 0 && KS >= 1 && VU >= 1 && NW > NSB, "unsupported wave split");
-    static_assert(MAP ? NW * CPW == 2 * D : NW * CPW == D, "state columns must match the mode");
+    static_assert(NW * CPW == D, "the waves' columns cover the state");
     __shared__ Smem<NSB, NP> sm;
 
     const int tid = threadIdx.x;
@@ -436,28 +440,19 @@ void chunk_kernel(
     const ChunkItem it = items[blockIdx.x / H];
     const int h = blockIdx.x % H;
     const int64_t t0 = it.t0, t1 = it.t1;
-    const int colg = CPW * w;            // first state column (of 256 in map mode)
-    const bool mhalf = MAP && colg >= D; // this wave propagates M (no v)
-    const int col = colg & (D - 1);      // column inside S, B or M
+    const int col = CPW * w;  // first state column of this wave
 
     // State, kept as S * 2^ex: S[16 rt + 4 g4 + i][col + 16 ct + r] in S[rt][ct][i].
     f4 S[8][NCT];
     int ex = 0;
     {
         const float* src = nullptr;
-        if (!MAP) {
-            if (it.sin >= 0 && h0) src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
-            else if (it.sin <= -2) src = staged + (static_cast<int64_t>(-it.sin - 2) * H + h) * D * D;
-        }
+        if (it.sin >= 0 && h0) src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
+        else if (it.sin <= -2) src = staged + (static_cast<int64_t>(-it.sin - 2) * H + h) * D * D;
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * rt + 4 * g4 + i, cc = col + 16 * ct + r;
-                    S[rt][ct][i] = (mhalf && row == cc) ? 1.f : 0.f;
-                }
+            for (int ct = 0; ct < NCT; ++ct) S[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
         if (src) {
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
@@ -495,7 +490,7 @@ void chunk_kernel(
         for (int ks = 0; ks < KS; ++ks) {
             const int off = tok * rowe + CPG * part + 32 * ks + 8 * g4;
             kw[ks] = bload16(rk, 2 * off);
-            qw[ks] = MAP ? u4{0, 0, 0, 0} : bload16(rq, 2 * off);
+            qw[ks] = bload16(rq, 2 * off);
             const u4 a0 = bload16(rg, 4 * off), a1 = bload16(rg, 4 * off + 16);
             ga[ks] = f4{__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]), __uint_as_float(a0[3])};
             gb[ks] = f4{__uint_as_float(a1[0]), __uint_as_float(a1[1]), __uint_as_float(a1[2]), __uint_as_float(a1[3])};
@@ -512,7 +507,7 @@ void chunk_kernel(
     };
     fetch_gate(t0);
     fetch_v(t0);
-    const bool snapping = SNAP && !MAP && snaps != nullptr && it.snap >= 0;
+    const bool snapping = SNAP && snaps != nullptr && it.snap >= 0;
     SnapCursor sc{};
     if (snapping) sc.init(it, interval);
 
@@ -535,7 +530,7 @@ void chunk_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 unpack_bf16x8(kw[ks], kf[ks]);
-                if (!MAP) unpack_bf16x8(qw[ks], qf[ks]);
+                unpack_bf16x8(qw[ks], qf[ks]);
 #pragma unroll
                 for (int m = 0; m < 8; ++m)
                     G[ks][m] = row_scan16((m < 4 ? ga[ks][m] : gb[ks][m - 4]) * LOG2E);
@@ -562,14 +557,14 @@ void chunk_kernel(
                     const float ia = __builtin_amdgcn_exp2f(-xa);
                     La[m] = kf[ks][m] * a;
                     Ra[m] = kf[ks][m] * ia;
-                    if (!MAP) Qa[m] = qf[ks][m] * a;
+                    Qa[m] = qf[ks][m] * a;
                     hh[m] = row_bcast16<15>(a);
                 }
 #pragma unroll
                 for (int m = 0; m < 8; ++m) {
                     l16[ks][m] = static_cast<_Float16>(La[m] * hh[m]);   // k exp(G) <= |k|
                     rb16[ks][m] = static_cast<_Float16>(Ra[m] * hh[m]);  // k exp(tot - G)
-                    if (!MAP) q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);
+                    q16[ks][m] = static_cast<_Float16>(Qa[m] * hh[m]);
                 }
                 if (!__any(span > FAST_SPAN)) {  // wave-uniform
                     h8 la, ra, qa;
@@ -577,16 +572,16 @@ void chunk_kernel(
                     for (int m = 0; m < 8; ++m) {
                         la[m] = static_cast<_Float16>(La[m]);
                         ra[m] = static_cast<_Float16>(Ra[m]);
-                        if (!MAP) qa[m] = static_cast<_Float16>(Qa[m]);
+                        qa[m] = static_cast<_Float16>(Qa[m]);
                     }
                     accA = mfma16(la, ra, accA);
-                    if (!MAP) accP = mfma16(qa, ra, accP);
+                    accP = mfma16(qa, ra, accP);
                 } else {
                     // MFMA m contracts channel 8 g4 + m (k index g4).
 #pragma unroll
                     for (int m = 0; m < 8; ++m) {
                         accA = mfma4(La[m], Ra[m], accA);
-                        if (!MAP) accP = mfma4(Qa[m], Ra[m], accP);
+                        accP = mfma4(Qa[m], Ra[m], accP);
                     }
                     redo = redo || __any(span > SAFE_SPAN);
                 }
@@ -601,7 +596,7 @@ void chunk_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 sm.gp[part][2 * I][4 * g4 + i][r] = accA[i];  // beta of row i is applied in the sum
-                if (!MAP) sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
+                sm.gp[part][2 * I + 1][4 * g4 + i][r] = accP[i];
             }
             if (redo) {
                 // Exponents beyond the fp32 range of the half-total reference: the
@@ -611,7 +606,7 @@ void chunk_kernel(
                 // in order).
                 const uint32_t vld = valid_at(c0);
                 const int64_t cb = (c0 * H + h) * D;
-                const auto rk = rsrc(k + cb, vld * rowe * 2), rq = rsrc(q + cb, MAP ? 0u : vld * rowe * 2);
+                const auto rk = rsrc(k + cb, vld * rowe * 2), rq = rsrc(q + cb, vld * rowe * 2);
                 const auto rg = rsrc(g + cb, vld * rowe * 4);
                 f4 oa = {0.f, 0.f, 0.f, 0.f}, op = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -627,7 +622,7 @@ void chunk_kernel(
                         gr[m] = __uint_as_float(a0[m]);
                         gr[4 + m] = __uint_as_float(a1[m]);
                     }
-                    phase1_direct<!MAP>(kr, qr, gr, g4, l16[ks], q16[ks], rb16[ks], et, oa, op);
+                    phase1_direct<true>(kr, qr, gr, g4, l16[ks], q16[ks], rb16[ks], et, oa, op);
                     if (r == 15) {
                         *reinterpret_cast<f4*>(&sm.etot[I][ch]) = f4{et[0], et[1], et[2], et[3]};
                         *reinterpret_cast<f4*>(&sm.etot[I][ch + 4]) = f4{et[4], et[5], et[6], et[7]};
@@ -635,7 +630,7 @@ void chunk_kernel(
                     if (I < NSB - 1) *reinterpret_cast<h8*>(&sm.rbs[I][r][ch]) = rb16[ks];
                 }
                 *reinterpret_cast<f4*>(&sm.gp[part][2 * I][r][4 * g4]) = oa;
-                if (!MAP) *reinterpret_cast<f4*>(&sm.gp[part][2 * I + 1][r][4 * g4]) = op;
+                *reinterpret_cast<f4*>(&sm.gp[part][2 * I + 1][r][4 * g4]) = op;
             }
         }
         __syncthreads();  // B1
@@ -678,14 +673,14 @@ void chunk_kernel(
                 h8 kv = l16[ks], qv = q16[ks], bv = rb16[ks];
                 if (I > 0) {
                     kv *= fb;
-                    if (!MAP) qv *= fb;
+                    qv *= fb;
                 }
                 if (I < NSB - 1) bv *= fa;
                 // channels 8 g4 .. 8 g4 + 7 of the block go to two 4-wide runs
                 const int cb = ch & ~31, p0 = cb + (g4 < 2 ? 16 * g4 : 16 * g4 - 28), p1 = p0 + 8;
                 *reinterpret_cast<h4*>(&sm.kt[tok][p0]) = __builtin_shufflevector(kv, kv, 0, 1, 2, 3);
                 *reinterpret_cast<h4*>(&sm.kt[tok][p1]) = __builtin_shufflevector(kv, kv, 4, 5, 6, 7);
-                if (!MAP) {
+                {
                     *reinterpret_cast<h4*>(&sm.qt[tok][p0]) = __builtin_shufflevector(qv, qv, 0, 1, 2, 3);
                     *reinterpret_cast<h4*>(&sm.qt[tok][p1]) = __builtin_shufflevector(qv, qv, 4, 5, 6, 7);
                 }
@@ -711,7 +706,7 @@ void chunk_kernel(
                             rv *= fm;
                         }
                         ax[J] = mfma16(l16[ks], rv, ax[J]);
-                        if (!MAP) px[J] = mfma16(q16[ks], rv, px[J]);
+                        px[J] = mfma16(q16[ks], rv, px[J]);
                     }
                 }
             }
@@ -722,7 +717,7 @@ void chunk_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         sm.gp[part][2 * NSB + 2 * x][4 * g4 + i][r] = ax[J][i];  // raw (beta applied in the state pass)
-                        if (!MAP) sm.gp[part][2 * NSB + 2 * x + 1][4 * g4 + i][r] = px[J][i];
+                        sm.gp[part][2 * NSB + 2 * x + 1][4 * g4 + i][r] = px[J][i];
                     }
                 }
             }
@@ -772,13 +767,13 @@ void chunk_kernel(
             const int t2 = tid - 64 * NSB;
             constexpr int NT2 = NT - 64 * NSB;
             constexpr int NPB = NSB + NX + NKB;  // P blocks written: diagonal, cross, upper-in-k-block
-            constexpr int NQ = (MAP ? 0 : NPB * 64) + NX * 64;  // 4-entry quads
+            constexpr int NQ = NPB * 64 + NX * 64;  // 4-entry quads
 #pragma unroll
             for (int q0 = 0; q0 < NQ; q0 += NT2) {
                 const int qi = q0 + t2;
                 if (qi < NQ) {
                     const int blk = qi >> 6, i = (qi >> 2) & 15, m4 = (qi & 3) * 4;
-                    const bool isp = !MAP && blk < NPB;
+                    const bool isp = blk < NPB;
                     int tile = -1, bi = 0, bj = 0;
                     if (isp) {
                         if (blk < NSB) { bi = bj = blk; tile = 2 * blk + 1; }
@@ -789,7 +784,7 @@ void chunk_kernel(
                             tile = 2 * NSB + 2 * x + 1;
                         } else { bi = 2 * (blk - NSB - NX); bj = bi + 1; }  // upper block of a 32-token k block
                     } else {
-                        tile = 2 * NSB + 2 * (blk - (MAP ? 0 : NPB));
+                        tile = 2 * NSB + 2 * (blk - NPB);
                     }
                     f4 val = {0.f, 0.f, 0.f, 0.f};
                     if (tile >= 0) {
@@ -804,7 +799,7 @@ void chunk_kernel(
                         const int R = 16 * bi + i;
                         *reinterpret_cast<h4*>(&sm.p[R][kpos(16 * bj + m4)]) = hv;
                     } else {
-                        const int x = blk - (MAP ? 0 : NPB);
+                        const int x = blk - NPB;
                         h4 hv;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(-val[e]);
@@ -825,7 +820,7 @@ void chunk_kernel(
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        vv[rt][ct][i] = mhalf ? 0.f : bf16_to_f32(sm.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
+                        vv[rt][ct][i] = bf16_to_f32(sm.v[16 * rt + 4 * g4 + i][col + 16 * ct + r]);
             // Exponent for this chunk from max(|S|, |v|) over the wave's columns.
             float mv = 0.f;
 #pragma unroll
@@ -910,9 +905,9 @@ void chunk_kernel(
                 for (int ct = 0; ct < NCT; ++ct) d16[kb][ct] = cat(dh[2 * kb][ct], dh[2 * kb + 1][ct]);
 
             // O = scale (Q~ S + P Delta)
-            if (!MAP) {
+            {
                 const float os = scale * ldexpf(1.f, -ex);
-            const int vlim = valid - 4 * g4;  // rows of this lane group still inside the chunk
+                const int vlim = valid - 4 * g4;  // rows of this lane group still inside the chunk
                 const int64_t stride = static_cast<int64_t>(H) * D;
 #pragma unroll
                 for (int rt = 0; rt < NSB; ++rt) {
@@ -962,18 +957,17 @@ void chunk_kernel(
         }
     }
 
-    // Final state (full mode) or this segment's (B, M) (map mode, rows of 256).
+    // Final state.
     if (it.sout >= 0 && out_state) {
         const float un = ldexpf(1.f, -ex);
-        constexpr int64_t ld = MAP ? 2 * D : D;
-        float* dst = out_state + (static_cast<int64_t>(it.sout) * H + h) * D * ld;
+        float* dst = out_state + (static_cast<int64_t>(it.sout) * H + h) * D * D;
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dst[(16 * rt + 4 * g4 + i) * ld + colg + 16 * ct + r] = S[rt][ct][i] * un;
+                    dst[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] = S[rt][ct][i] * un;
     }
 }
 
@@ -1991,11 +1985,11 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
                                    items, a.H, a.h0, staged, o, a.hT, a.snaps, a.snap_interval);
             };
             if (a.out_bf16)
-                sn ? go(chunk_kernel<8, 4, 1, false, 1, bf16_t, true>, ob)
-                   : go(chunk_kernel<8, 4, 1, false, 1, bf16_t, false>, ob);
+                sn ? go(chunk_kernel<8, 4, 1, 1, bf16_t, true>, ob)
+                   : go(chunk_kernel<8, 4, 1, 1, bf16_t, false>, ob);
             else
-                sn ? go(chunk_kernel<8, 4, 1, false, 1, float, true>, of)
-                   : go(chunk_kernel<8, 4, 1, false, 1, float, false>, of);
+                sn ? go(chunk_kernel<8, 4, 1, 1, float, true>, of)
+                   : go(chunk_kernel<8, 4, 1, 1, float, false>, of);
             return;
         }
         auto go = [&](auto kernel, auto* o) {
