@@ -1353,8 +1353,17 @@ void chunk_ws_kernel(
         bool exited = false;  // propagation modes: X became zero in fp16
         {
             const float* src = nullptr;
-            if (it.sin >= 0 && h0) src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
-            else if (it.sin <= -2) src = staged + (static_cast<int64_t>(-it.sin - 2) * H + h) * D * D;
+            if (it.sin >= 0 && h0) {
+                src = h0 + (static_cast<int64_t>(it.sin) * H + h) * D * D;
+            } else if (it.sin <= -2) {
+                // CORR: a segment after one whose map vanished starts from that
+                // segment's zero-start final state (the scan staged nothing)
+                const int64_t z = -it.sin - 2;
+                if (MODE == MODE_CORR && it.p0 > 0 && mflags[(z - 1) * H + h] == 0)
+                    src = bout + ((z - 1) * H + h) * D * D;
+                else
+                    src = staged + (z * H + h) * D * D;
+            }
 #pragma unroll
             for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
@@ -1441,6 +1450,7 @@ void chunk_ws_kernel(
             return x;
         };
         u4 ogr[2];  // gated output: this lane's output gate, read in interval 1
+        f4 opre[4];  // CORR: this wave's o rows of chunk c, read an interval before the add
         for (int c = -2; c < nch; ++c) {
             const bool swork = c >= 0;        // run chunk c
             const int64_t c0 = t0 + static_cast<int64_t>(c) * C;
@@ -1462,6 +1472,15 @@ void chunk_ws_kernel(
                 for (int e = 0; e < 4; ++e) hv[e] = static_cast<_Float16>(sgn * val[e]);
                 if (w == 2) *reinterpret_cast<h4*>(&nxt.p[SB + i][kpos(m4)]) = hv;
                 else *reinterpret_cast<h4*>(&nxt.tb[2][i][m4]) = hv;
+            }
+            if (MODE == MODE_CORR && swork) {
+                const auto ro = rsrc(o + (c0 * H + h) * D, static_cast<uint32_t>(valid) * rowe * sizeof(Tout));
+                const int el = epi_lane(), c4 = 4 * (el & 31);
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) {
+                    const int row = 8 * (w & 3) + 2 * k2 + (el >> 5);
+                    opre[k2] = load4(ro, (row * rowe + c4) * static_cast<int>(sizeof(Tout)), o);
+                }
             }
             if (swork) {
                 f4 y[NSB][NCT];
@@ -1574,7 +1593,7 @@ void chunk_ws_kernel(
                         const int row = 8 * (w & 3) + 2 * k2 + (el >> 5);
                         const int off = (row * rowe + c4) * static_cast<int>(sizeof(Tout));
                         f4 y = *reinterpret_cast<const f4*>(&sm.otile[row][c4]);
-                        if (MODE == MODE_CORR) y += load4(ro, off, o);
+                        if (MODE == MODE_CORR) y += opre[k2];
                         store4(ro, off, y, o);
                     }
                 }
@@ -1656,13 +1675,15 @@ void chunk_ws_kernel(
 
 // The true initial state of every segment of a sequence cut into segments:
 // S_0 = h0 (or zero), S_{j+1} = B_j + M_j S_j, where B_j is segment j's
-// final state from a zero start and M_j its state map (absent when the map
-// pass found it zero in fp16, or not needed: M_0 with a zero h0, the last map
-// without a final state).  S_j (j >= 1, and S_0 when h0 is given) is staged
-// for the correction pass; the last one is the sequence's final state.  The
-// caller's initial state is read only here and before any final state is
-// written, so an in-place final state cannot race.  One workgroup of 4 waves
-// per (sequence, head); wave w owns state columns [32 w, 32 w + 32).  The
+// final state from a zero start and M_j its state map.  A map the map pass
+// found zero in fp16 (or did not compute: M_0 with a zero h0, the last map
+// without a final state) has flag 0 and then S_{j+1} = B_j: the correction
+// pass reads B_j itself, so only runs of nonzero maps are walked here, one
+// segment after the other, and their states staged.  S_0 = h0 is staged for
+// the first segment's correction, and the last state is the final state.
+// The caller's h0 is read only here, before any final state is written, so
+// an in-place final state cannot race.  One workgroup of 4 waves per
+// (sequence, head); wave w owns state columns [32 w, 32 w + 32).  The
 // 128 x 128 products run on split bf16 MFMA (hi + lo on both operands, three
 // products), about 16 significant bits per operand, fp32 accumulation.
 __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
@@ -1674,15 +1695,17 @@ __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
     const int h = blockIdx.x % H;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 15, g4 = l >> 4;
     const int col = 32 * w;
+    auto row_of = [&](const float* base, int64_t slot) { return base + (slot * H + h) * D * D; };
+    auto mrow_of = [&](float* base, int64_t slot) { return base + (slot * H + h) * D * D; };
     f4 S[8][2];
-    const float* src = (it.h0 >= 0 && h0) ? h0 + (static_cast<int64_t>(it.h0) * H + h) * D * D : nullptr;
+    auto load = [&](const float* src) {
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
+        for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[rt][ct][i] = src ? src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] : 0.f;
+                for (int i = 0; i < 4; ++i) S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
+    };
     auto put = [&](float* dst) {
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
@@ -1691,64 +1714,72 @@ __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] = S[rt][ct][i];
     };
-    auto row_of = [&](const float* base, int64_t slot) { return base + (slot * H + h) * D * D; };
-    if (src) put(staged + (static_cast<int64_t>(it.first_seg) * H + h) * D * D);
-
+    const float* hsrc = (it.h0 >= 0 && h0) ? h0 + (static_cast<int64_t>(it.h0) * H + h) * D * D : nullptr;
+    if (hsrc) {
+        load(hsrc);
+        put(mrow_of(staged, it.first_seg));
+    }
+    bool have = hsrc != nullptr;  // S holds S_j
     for (int j = 0; j < it.nseg; ++j) {
         const int64_t sj = it.first_seg + j;
         const bool last = j + 1 == it.nseg;
         if (last && it.hT < 0) break;  // no final state wanted
+        float* dst = last ? final_state + (static_cast<int64_t>(it.hT) * H + h) * D * D : mrow_of(staged, sj + 1);
+        if (mflags[sj * H + h] == 0) {  // wave-uniform: S_{j+1} = B_j
+            if (last) {
+                load(row_of(bst, sj));
+                put(dst);
+            }
+            have = false;
+            continue;
+        }
+        if (!have) load(row_of(bst, sj - 1));  // j >= 1 here: S_j = B_{j-1}
         const float* bj = row_of(bst, sj);
-        const bool use_map = (j > 0 || src) && mflags[sj * H + h] != 0;  // wave-uniform
-        f4 acc[8][2];
+        const float* mp = row_of(maps, sj);
+        // B operands from S (k = rows of S, permuted as in the chunk kernel), split hi/lo.
+        b8 sh[4][2], sl[4][2];
 #pragma unroll
-        for (int rt = 0; rt < 8; ++rt)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[rt][ct][i] = bj[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
-        if (use_map) {
-            const float* mp = row_of(maps, sj);
-            // B operands from S (k = rows of S, permuted as in the chunk kernel), split hi/lo.
-            b8 sh[4][2], sl[4][2];
+                for (int m = 0; m < 8; ++m) {
+                    const float x = m < 4 ? S[2 * ks][ct][m] : S[2 * ks + 1][ct][m - 4];
+                    sh[ks][ct][m] = static_cast<__bf16>(x);
+                    sl[ks][ct][m] = static_cast<__bf16>(x - static_cast<float>(sh[ks][ct][m]));
+                }
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+        for (int rt = 0; rt < 8; ++rt) {
+            f4 acc[2];
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        const float x = m < 4 ? S[2 * ks][ct][m] : S[2 * ks + 1][ct][m - 4];
-                        sh[ks][ct][m] = static_cast<__bf16>(x);
-                        sl[ks][ct][m] = static_cast<__bf16>(x - static_cast<float>(sh[ks][ct][m]));
-                    }
+                for (int i = 0; i < 4; ++i) acc[ct][i] = bj[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
+            const float* mrow = mp + (16 * rt + r) * D;  // row of M
 #pragma unroll
-            for (int rt = 0; rt < 8; ++rt) {
-                const float* mrow = mp + (16 * rt + r) * D;  // row of M
+            for (int ks = 0; ks < 4; ++ks) {
+                const f4 lo4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 4 * g4);
+                const f4 hi4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 16 + 4 * g4);
+                b8 ah, al;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const f4 lo4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 4 * g4);
-                    const f4 hi4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 16 + 4 * g4);
-                    b8 ah, al;
+                for (int m = 0; m < 8; ++m) {
+                    const float x = m < 4 ? lo4[m] : hi4[m - 4];
+                    ah[m] = static_cast<__bf16>(x);
+                    al[m] = static_cast<__bf16>(x - static_cast<float>(ah[m]));
+                }
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        const float x = m < 4 ? lo4[m] : hi4[m - 4];
-                        ah[m] = static_cast<__bf16>(x);
-                        al[m] = static_cast<__bf16>(x - static_cast<float>(ah[m]));
-                    }
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        acc[rt][ct] = mfmab(ah, sh[ks][ct], acc[rt][ct]);
-                        acc[rt][ct] = mfmab(ah, sl[ks][ct], acc[rt][ct]);
-                        acc[rt][ct] = mfmab(al, sh[ks][ct], acc[rt][ct]);
-                    }
+                for (int ct = 0; ct < 2; ++ct) {
+                    acc[ct] = mfmab(ah, sh[ks][ct], acc[ct]);
+                    acc[ct] = mfmab(ah, sl[ks][ct], acc[ct]);
+                    acc[ct] = mfmab(al, sh[ks][ct], acc[ct]);
                 }
             }
+            // row block rt of S is consumed (sh, sl hold it), so it is overwritten here
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) S[rt][ct] = acc[ct];
         }
-#pragma unroll
-        for (int rt = 0; rt < 8; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) S[rt][ct] = acc[rt][ct];
-        put(last ? final_state + (static_cast<int64_t>(it.hT) * H + h) * D * D : staged + ((sj + 1) * H + h) * D * D);
+        put(dst);
+        have = true;
     }
 }
 
@@ -1789,7 +1820,7 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(
     const int32_t* __restrict__ cu, int N, int T, int seg, int has_h0, int has_hT,
     const int32_t* __restrict__ snap_base, ChunkItem* __restrict__ full_items,
     ChunkItem* __restrict__ map_items, ChunkItem* __restrict__ corr_items,
-    ScanItem* __restrict__ scan_items) {
+    ScanItem* __restrict__ scan_items, int H, int* __restrict__ mflags) {
     __shared__ int sc[256], sc2[256];
     __shared__ int base, base2;
     if (threadIdx.x == 0) base = base2 = 0;
@@ -1832,6 +1863,7 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(
                     continue;
                 }
                 const bool live_in = j > 0 || has_h0;
+                for (int hh = 0; hh < H; ++hh) mflags[static_cast<int64_t>(zi) * H + hh] = 0;  // set by the map pass
                 full_items[si] = ChunkItem{sa, sb, -1, -2 - zi, sa - a, snap, 0};
                 map_items[si] = (live_in && (j + 1 < G || has_hT)) ? ChunkItem{sa, sb, -1, zi, sa - a, -1, 0}
                                                                    : ChunkItem{sa, sa, -1, -1, sa - a, -1, 0};
@@ -2044,14 +2076,14 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
     float* staged = reinterpret_cast<float*>(ws + L.staged);
     hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T, seg,
                        a.h0 ? 1 : 0, a.hT ? 1 : 0, a.snap_base, full_items, map_items, corr_items,
-                       scan_items);
+                       scan_items, a.H, mflags);
     const bool split = cnt.nsplit > 0;
     if (split) launch_full(map_items, cnt.nseg, nullptr, MODE_MAP, maps, nullptr, mflags);
     launch_full(full_items, cnt.nseg, nullptr, MODE_FULL, nullptr, bst, nullptr, !split);
     if (split) {
         hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<uint32_t>(a.N) * a.H), dim3(256), 0,
                            a.stream, scan_items, a.H, a.h0, bst, maps, mflags, staged, a.hT);
-        launch_full(corr_items, cnt.nseg, staged, MODE_CORR);
+        launch_full(corr_items, cnt.nseg, staged, MODE_CORR, nullptr, bst, mflags);
         // the gated RMSNorm needs the corrected read-out: applied in place after
         if (a.ogate) {
             const hipError_t e = hipGetLastError();
