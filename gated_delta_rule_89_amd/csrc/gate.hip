@@ -87,18 +87,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 64 ? 4
         }
     }
     // D layout of the transposed product: lane holds rows 4 g4 + i (channels)
-    // of column r16 (token) of each 16 x 16 tile
+    // of column r16 (token) of each 16 x 16 tile, so one tile covers 64 bytes
+    // of a token's g row.  Tiles 2j and 2j + 1 together cover 128 contiguous
+    // bytes (a whole cache line) per token: the second tile's values are
+    // rotated by 8 lanes inside each 16-lane row (DPP), and each store then
+    // writes whole lines of 8 tokens -- lanes r16 < 8 tile 2j of token r16
+    // and lanes r16 >= 8 tile 2j + 1 of token r16 - 8, or the other 8 tokens
+    // -- instead of half lines of 16 tokens (half as many write requests).
+    const bool lo = r16 < 8;
 #pragma unroll
-    for (int ct = 0; ct < DK / 16; ++ct) {
-        const int c = 16 * ct + 4 * g4;
-        const f4 bc = bias ? *reinterpret_cast<const f4*>(bias + h * DK + c) : f4{0.f, 0.f, 0.f, 0.f};
+    for (int cp = 0; cp < DK / 32; ++cp) {
+        const int ca = 32 * cp + 4 * g4, cb = ca + 16;
+        const f4 ba = bias ? *reinterpret_cast<const f4*>(bias + h * DK + ca) : f4{0.f, 0.f, 0.f, 0.f};
+        const f4 bb = bias ? *reinterpret_cast<const f4*>(bias + h * DK + cb) : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const int64_t m = m0 + 16 * rt + r16;
-            f4 out;
+            f4 ya, yb;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) out[i] = neg_softplus(acc[rt][ct][i] + bc[i]);
-            if (m < M) __builtin_nontemporal_store(out, reinterpret_cast<f4*>(g + m * N + h * DK + c));
+            for (int i = 0; i < 4; ++i) {
+                ya[i] = neg_softplus(acc[rt][2 * cp][i] + ba[i]);
+                const float b = neg_softplus(acc[rt][2 * cp + 1][i] + bb[i]);
+                yb[i] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), 0x128, 0xf, 0xf, false));  // row_ror:8
+            }
+            f4 x, y;  // x: tokens 0..7 of the tile, y: tokens 8..15
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = lo ? ya[i] : yb[i];
+                y[i] = lo ? yb[i] : ya[i];
+            }
+            const int t7 = r16 & 7;
+            const int64_t mx = m0 + 16 * rt + t7, my = mx + 8;
+            const int cx = lo ? ca : cb, cy = lo ? cb : ca;
+            if (mx < M) __builtin_nontemporal_store(x, reinterpret_cast<f4*>(g + mx * N + h * DK + cx));
+            if (my < M) __builtin_nontemporal_store(y, reinterpret_cast<f4*>(g + my * N + h * DK + cy));
         }
     }
 }
