@@ -143,27 +143,71 @@ hipError_t launch_decode(const DecodeArgs& a) {
 //
 // One wave owns CW (<= 32) columns of one state: lane l holds rows
 // R rg .. R rg + R - 1 (rg = l / TPR) of 4 columns (16-byte pieces, so a row
-// segment of the wave is CW * 4 contiguous bytes).  The two reductions over
-// the rows (S^T k and S^T q of the decayed state) stay inside the wave: DPP
-// row rotations inside each 16-lane row, then the row-pair swaps
-// v_permlane16_swap / v_permlane32_swap across rows.  Only the decay factors
-// pass through LDS (a slice per wave), so there is no barrier; the next
-// token's inputs are loaded before the current token's reductions.
-template <int TPR>
-__device__ __forceinline__ float sum_row_groups(float x) {
-    // lanes that share l % TPR; TPR in {4, 8}
-    if (TPR == 4) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+// segment of the wave is CW * 4 contiguous bytes).
+//
+// The decay is not applied to the registers token by token.  With G_t the
+// per-channel sum of the log-gates since a reference point and
+// E_t = Diag(exp G_t), the wave holds S' = E_t^-1 S.  Then
+//   (Diag(alpha_t) S_{t-1})^T k = S'^T (E_t k),  likewise for q,
+//   S_t = E_t (S' + (E_t^-1 k) u^T),
+// so a token costs three fp32 operations per state element (two dot
+// products and the rank-1 write) instead of four.  Every term of S' is
+// scaled back by exp(G_T - G_t) <= 1 when E_T is applied, so rounding stays
+// relative to the terms, as in the plain recurrence.  The per-channel
+// vectors E_t k, E_t^-1 k and E_t q are formed once per wave (NE channels
+// per lane) and shared through the wave's own slice of LDS: the lanes of a
+// row group hold the same rows, so forming them per lane would repeat the
+// work TPR times.  Once a channel's |G_t| passes FOLD (log2), E_t^-1 would
+// leave fp32 range: the wave folds E_t into its rows (the plain decay) and
+// restarts G from zero, which also turns a gate of -inf into an exact zero.
+// E_T is folded in before the state is written back.
+//
+// The two reductions over rows (and q . k over channels) stay inside the
+// wave: DPP row rotations inside each 16-lane row, then the row-pair swaps
+// v_permlane16_swap / v_permlane32_swap across rows.  Only this wave touches
+// its LDS slice and its LDS operations complete in order, so no barrier is
+// needed; the next token's inputs are loaded at the start of each token.
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the four 16-lane rows of the wave (lanes that share l % 16).
+__device__ __forceinline__ float sum_across_rows(float x) {
     const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
     const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
-template <int R, typename T>
-__device__ __forceinline__ void load_rows(const T* __restrict__ p, int64_t b, float (&x)[R]) {
-#pragma unroll
-    for (int i = 0; i < R; ++i) x[i] = ld(p, b + i);
+template <int TPR>
+__device__ __forceinline__ float sum_row_groups(float x) {
+    // lanes that share l % TPR; TPR in {4, 8}
+    if (TPR == 4) x = add_dpp<0x124>(x);  // row_ror:4
+    x = add_dpp<0x128>(x);                // row_ror:8
+    return sum_across_rows(x);
+}
+
+__device__ __forceinline__ float sum_wave(float x) {
+    x = add_dpp<0x121>(add_dpp<0x122>(add_dpp<0x124>(add_dpp<0x128>(x))));
+    return sum_across_rows(x);
+}
+
+// NE consecutive channels from element i (i a multiple of NE).
+template <int NE, typename T>
+__device__ __forceinline__ void load_chan(const T* __restrict__ p, int64_t i, float (&x)[NE]) {
+    static_assert(NE == 1 || NE == 2, "one or two channels per lane");
+    if constexpr (NE == 2 && std::is_same<T, bf16_t>::value) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(p + i);
+        x[0] = __uint_as_float(w << 16);
+        x[1] = __uint_as_float(w & 0xffff0000u);
+    } else if constexpr (NE == 2) {
+        const float2 w = *reinterpret_cast<const float2*>(p + i);
+        x[0] = w.x;
+        x[1] = w.y;
+    } else {
+        x[0] = ld(p, i);
+    }
 }
 
 template <int DK, int DV, typename Tin, typename Tout>
@@ -176,6 +220,10 @@ __global__ __launch_bounds__(256) void steps_kernel(
     constexpr int RG = 64 / TPR;             // row groups per wave
     constexpr int R = DK / RG;               // rows per lane
     constexpr int NCB = DV / CW;             // waves per state
+    constexpr int NE = DK > 64 ? DK / 64 : 1;  // channels per lane in the per-channel phase
+    constexpr int CL = DK / NE;                // lanes that hold channels
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr float FOLD = 64.f;  // bound on |G| (log2) before E is folded into the rows
     static_assert(TPR == 4 || TPR == 8, "4 or 8 lanes per row");
     static_assert(R >= 1 && DK % RG == 0, "rows split evenly over the row groups");
     const int l = threadIdx.x & 63;
@@ -186,82 +234,102 @@ __global__ __launch_bounds__(256) void steps_kernel(
     const int r0 = (l / TPR) * R;
     const int64_t n = nh / H, h = nh % H;
     float* S = state + nh * DK * DV + col;
+    const bool chan = CL == 64 || l < CL;
+    const int c0 = NE * l;
+
+    // The wave's LDS slice: E k, E^-1 k, E q, and E when it is folded.
+    __shared__ __align__(16) float xs[4][4][DK];
+    float(*const xw)[DK] = xs[threadIdx.x >> 6];
 
     f32x4 s[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) s[i] = *reinterpret_cast<const f32x4*>(S + (r0 + i) * DV);
 
-    // k is double-buffered (the update needs it after the reductions); q and
-    // g of the next token are loaded as soon as the dot products are done.
-    // The decay factors exp(g) of a token are computed once per wave, NE rows
-    // per lane, and shared through the wave's slice of LDS: the lanes of a row
-    // group hold the same rows, so computing them per lane would repeat each
-    // exponential TPR times.  Only this wave touches its slice, and its LDS
-    // operations complete in order, so no barrier is needed.
-    constexpr int NE = (DK + 63) / 64;  // decay rows per lane
-    __shared__ __align__(16) float eg_lds[4][DK];
-    float* const egw = eg_lds[threadIdx.x >> 6];
-    float kr[R], qr[R], ga[R], nk[R], gn[NE];
+    float kc[NE], qc[NE], gc[NE], nk[NE], nq[NE], ng[NE], G[NE];
     f32x4 vt, nv;
     float bt, nb;
-    auto fetch_k = [&](int t) {
+    auto fetch = [&](int t) {
         const int64_t tv = (n * T + t) * H + h;
-        load_rows<R>(k, tv * DK + r0, nk);
+        if (chan) {
+            load_chan<NE>(k, tv * DK + c0, nk);
+            load_chan<NE>(q, tv * DK + c0, nq);
+            load_chan<NE>(g, tv * DK + c0, ng);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NE; ++j) nk[j] = nq[j] = ng[j] = 0.f;
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) nv[c] = ld(v, tv * DV + col + c);
         nb = beta[tv];
     };
-    auto fetch_qg = [&](int t) {
-        const int64_t tv = (n * T + t) * H + h;
-        load_rows<R>(q, tv * DK + r0, qr);
+    // E of the current G into slot 3 and onto this lane's rows of S'.
+    auto fold = [&]() {
+        if (chan) {
 #pragma unroll
-        for (int j = 0; j < NE; ++j) gn[j] = (DK >= 64 || l < DK) ? g[tv * DK + l + 64 * j] : 0.f;
-    };
-    auto put_decay = [&]() {
+            for (int j = 0; j < NE; ++j) xw[3][c0 + j] = __builtin_amdgcn_exp2f(G[j]);
+        }
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int j = 0; j < NE; ++j)
-            if (DK >= 64 || l < DK) egw[l + 64 * j] = gate_exp(gn[j]);
+        for (int i = 0; i < R; ++i) s[i] *= xw[3][r0 + i];
+#pragma unroll
+        for (int j = 0; j < NE; ++j) G[j] = 0.f;
         __builtin_amdgcn_wave_barrier();
     };
-    fetch_k(0);
-    fetch_qg(0);
-    put_decay();
+#pragma unroll
+    for (int j = 0; j < NE; ++j) G[j] = 0.f;
+    if (T > 0) fetch(0);
     for (int t = 0; t < T; ++t) {
         const int64_t tv = (n * T + t) * H + h;
-        const int tn = t + 1 < T ? t + 1 : t;  // every iteration loads: exact load counting
 #pragma unroll
-        for (int i = 0; i < R; ++i) kr[i] = nk[i];
+        for (int j = 0; j < NE; ++j) {
+            kc[j] = nk[j];
+            qc[j] = nq[j];
+            gc[j] = ng[j];
+        }
         vt = nv;
         bt = nb;
-        fetch_k(tn);
-        f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
-        float qk = 0.f;
+        fetch(t + 1 < T ? t + 1 : t);  // every iteration loads: exact load counting
+        bool deep = false;
 #pragma unroll
-        for (int i = 0; i < R; ++i) ga[i] = egw[r0 + i];
+        for (int j = 0; j < NE; ++j) {
+            G[j] += gc[j] * LOG2E;
+            deep = deep || fabsf(G[j]) > FOLD;
+        }
+        if (__any(deep)) fold();
+        float qk = 0.f;
+        if (chan) {
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const float e = __builtin_amdgcn_exp2f(G[j]), ei = __builtin_amdgcn_exp2f(-G[j]);
+                xw[0][c0 + j] = kc[j] * e;
+                xw[1][c0 + j] = kc[j] * ei;
+                xw[2][c0 + j] = qc[j] * e;
+                qk += qc[j] * kc[j];
+            }
+        }
         __builtin_amdgcn_wave_barrier();
+        f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            s[i] *= ga[i];  // decay row
-            pk += s[i] * kr[i];
-            pq += s[i] * qr[i];
-            qk += qr[i] * kr[i];
+            pk += s[i] * xw[0][r0 + i];
+            pq += s[i] * xw[2][r0 + i];
         }
-        fetch_qg(tn);
+        qk = sum_wave(qk);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             pk[c] = sum_row_groups<TPR>(pk[c]);
             pq[c] = sum_row_groups<TPR>(pq[c]);
         }
-        qk = sum_row_groups<TPR>(qk);
         const f32x4 u = bt * (vt - pk);
 #pragma unroll
-        for (int i = 0; i < R; ++i) s[i] += kr[i] * u;  // rank-1 write
+        for (int i = 0; i < R; ++i) s[i] += xw[1][r0 + i] * u;  // rank-1 write
         if (l < TPR) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) st(o, tv * DV + col + c, scale * (pq[c] + qk * u[c]));
         }
-        put_decay();  // the next token's (this token's factors are read above)
+        __builtin_amdgcn_wave_barrier();  // this token's slice reads before the next token's writes
     }
+    fold();
 #pragma unroll
     for (int i = 0; i < R; ++i) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4*>(S + (r0 + i) * DV));
 }
