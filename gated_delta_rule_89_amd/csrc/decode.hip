@@ -356,6 +356,8 @@ static hipError_t launch_steps_d(const DecodeArgs& a) {
 }
 
 hipError_t launch_steps(const DecodeArgs& a) {
+    // the matrix-core form (its per-sub-chunk offsets are 32-bit: 8 H d_k 4 bytes)
+    if (a.dk == 128 && a.dv == 128 && a.H <= (1 << 20)) return launch_steps_mfma(a);
     return dispatch_head_sizes(a.dk, a.dv, [&](auto DK, auto DV) {
         return launch_steps_d<decltype(DK)::value, decltype(DV)::value>(a);
     });

@@ -75,6 +75,8 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStrea
 hipError_t launch_recurrent(const PrefillArgs& a);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_steps(const DecodeArgs& a);
+// d_k = d_v = 128: the run in 8-token sub-chunks on fp32 MFMA.
+hipError_t launch_steps_mfma(const DecodeArgs& a);
 // g = -softplus(z W + b) (bf16 MFMA up-projection), beta = sigmoid(u).
 hipError_t launch_fused_gate(const void* z, const void* w, const float* bias, const float* u,
                              int64_t M, int r, int H, float* g, float* beta, hipStream_t stream);
