@@ -35,91 +35,108 @@ __device__ __forceinline__ float neg_softplus(float x) {
     return -(fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + t) * LN2);
 }
 
-// One wave per (32 rows of z, head): its MFMA fragments come straight from
-// global memory (z rows and W rows are both contiguous along j; W is small
-// and stays in L2), so there is no LDS staging and no barrier.  A workgroup
-// holds the 4 waves of 4 consecutive heads over the same rows, which share
-// those rows of z in the caches.  The k loop is left rolled and the register
-// budget capped at 5 waves per SIMD (4 at rank 64, where 5 would spill):
-// unrolled, the compiler keeps every W fragment of the wave in flight at once
-// (142 registers, 3 waves per SIMD), which measured about 2% slower.
+// A workgroup takes one head and NB blocks of 4 x 32 rows of z (one 32-row
+// block per wave and step): the head's W rows (DK x R bf16) are read from L2
+// once into LDS, where every wave takes its MFMA fragments for all NB row
+// blocks.  (One wave per 32 rows reading W from L2 moved twice the bytes of
+// the g tile it writes, and the loads, not the stores, stalled the kernel.)
+// The z fragments come straight from global memory: rows of z are
+// contiguous along j, every fragment is one 16-byte read.  16-byte chunk cc
+// of W row r sits at chunk cc ^ (r & (R / 8 - 1)) (at most 16 chunks apart),
+// so the 16 rows one fragment read touches fall in different banks.  The k
+// loop stays rolled (unrolled, the compiler keeps every fragment in flight
+// and occupancy drops).
+constexpr int NB = 16;  // row blocks per workgroup
+
 template <int R>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 64 ? 4 : 5))) void fused_gate_kernel(const uint16_t* __restrict__ z,
-                                                         const uint16_t* __restrict__ w,
-                                                         const float* __restrict__ bias,
-                                                         const float* __restrict__ u, int64_t M, int H,
-                                                         float* __restrict__ g, float* __restrict__ beta) {
-    constexpr int RT = ROWS / 16;  // 16-row tiles per wave
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 256 ? 2 : 4))) void fused_gate_kernel(
+    const uint16_t* __restrict__ z, const uint16_t* __restrict__ w, const float* __restrict__ bias,
+    const float* __restrict__ u, int64_t M, int H, float* __restrict__ g, float* __restrict__ beta) {
+    constexpr int RT = ROWS / 16;
+    constexpr int CPR = R / 8;                      // 16-byte chunks per W row
+    constexpr int SW = CPR < 16 ? CPR - 1 : 15;     // swizzle mask
+    __shared__ u4 wl[DK * CPR];
     const int tid = threadIdx.x, l = tid & 63, r16 = l & 15, g4 = l >> 4;
-    const int h = blockIdx.y * 4 + (tid >> 6);
-    const int64_t m0 = static_cast<int64_t>(blockIdx.x) * ROWS;
-    const int64_t N = static_cast<int64_t>(H) * DK;  // row length of g
-    if (h >= H) return;  // whole wave
-    if (h == 0) {  // beta of these rows, once per row block
-        for (int e = l; e < ROWS * H; e += 64) {
-            const int64_t idx = m0 * H + e;
-            if (idx < M * H) beta[idx] = 1.f / (1.f + __builtin_amdgcn_exp2f(-u[idx] * 1.4426950408889634f));
+    const int h = blockIdx.y;
+    const int64_t N = static_cast<int64_t>(H) * DK;
+    {
+        const u4* wh = reinterpret_cast<const u4*>(w + static_cast<int64_t>(h) * DK * R);
+#pragma unroll
+        for (int j = 0; j < DK * CPR / 256; ++j) {
+            const int ci = tid + 256 * j, row = ci / CPR, cc = ci % CPR;
+            wl[row * CPR + (cc ^ (row & SW))] = wh[ci];
         }
     }
-    f4 acc[RT][DK / 16];  // acc[rt][ct]: channels 16 ct + 4 g4 + i of token 16 rt + r16
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < DK / 16; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* wh = w + static_cast<int64_t>(h) * DK * R;
-#pragma unroll 1
-    for (int ks = 0; ks < R / 32; ++ks) {
-        b8 zf[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int64_t m = m0 + 16 * rt + r16;
-            u4 val = {0, 0, 0, 0};
-            if (m < M) val = *reinterpret_cast<const u4*>(z + m * R + 32 * ks + 8 * g4);
-            zf[rt] = __builtin_bit_cast(b8, val);
-        }
-#pragma unroll
-        for (int ct = 0; ct < DK / 16; ++ct) {
-            const b8 wf = __builtin_bit_cast(
-                b8, *reinterpret_cast<const u4*>(wh + (16 * ct + r16) * R + 32 * ks + 8 * g4));
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, zf[rt], acc[rt][ct], 0, 0, 0);
-        }
-    }
-    // D layout of the transposed product: lane holds rows 4 g4 + i (channels)
-    // of column r16 (token) of each 16 x 16 tile, so one tile covers 64 bytes
-    // of a token's g row.  Tiles 2j and 2j + 1 together cover 128 contiguous
-    // bytes (a whole cache line) per token: the second tile's values are
-    // rotated by 8 lanes inside each 16-lane row (DPP), and each store then
-    // writes whole lines of 8 tokens -- lanes r16 < 8 tile 2j of token r16
-    // and lanes r16 >= 8 tile 2j + 1 of token r16 - 8, or the other 8 tokens
-    // -- instead of half lines of 16 tokens (half as many write requests).
+    __syncthreads();
     const bool lo = r16 < 8;
-#pragma unroll
-    for (int cp = 0; cp < DK / 32; ++cp) {
-        const int ca = 32 * cp + 4 * g4, cb = ca + 16;
-        const f4 ba = bias ? *reinterpret_cast<const f4*>(bias + h * DK + ca) : f4{0.f, 0.f, 0.f, 0.f};
-        const f4 bb = bias ? *reinterpret_cast<const f4*>(bias + h * DK + cb) : f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            f4 ya, yb;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ya[i] = neg_softplus(acc[rt][2 * cp][i] + ba[i]);
-                const float b = neg_softplus(acc[rt][2 * cp + 1][i] + bb[i]);
-                yb[i] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), 0x128, 0xf, 0xf, false));  // row_ror:8
+#pragma unroll 1
+    for (int nb = 0; nb < NB; ++nb) {
+        const int64_t m0 = (static_cast<int64_t>(blockIdx.x) * NB + nb) * (4 * ROWS) + (tid >> 6) * ROWS;
+        if (m0 >= M) break;  // whole wave; no barrier follows
+        if (h == 0) {  // beta of these rows, once per row block
+            for (int e = l; e < ROWS * H; e += 64) {
+                const int64_t idx = m0 * H + e;
+                if (idx < M * H) beta[idx] = 1.f / (1.f + __builtin_amdgcn_exp2f(-u[idx] * 1.4426950408889634f));
             }
-            f4 x, y;  // x: tokens 0..7 of the tile, y: tokens 8..15
+        }
+        f4 acc[RT][DK / 16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = lo ? ya[i] : yb[i];
-                y[i] = lo ? yb[i] : ya[i];
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < DK / 16; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int ks = 0; ks < R / 32; ++ks) {
+            b8 zf[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int64_t m = m0 + 16 * rt + r16;
+                u4 val = {0, 0, 0, 0};
+                if (m < M) val = *reinterpret_cast<const u4*>(z + m * R + 32 * ks + 8 * g4);
+                zf[rt] = __builtin_bit_cast(b8, val);
             }
-            const int t7 = r16 & 7;
-            const int64_t mx = m0 + 16 * rt + t7, my = mx + 8;
-            const int cx = lo ? ca : cb, cy = lo ? cb : ca;
-            if (mx < M) __builtin_nontemporal_store(x, reinterpret_cast<f4*>(g + mx * N + h * DK + cx));
-            if (my < M) __builtin_nontemporal_store(y, reinterpret_cast<f4*>(g + my * N + h * DK + cy));
+#pragma unroll
+            for (int ct = 0; ct < DK / 16; ++ct) {
+                const int row = 16 * ct + r16, cc = 4 * ks + g4;
+                const b8 wf = __builtin_bit_cast(b8, wl[row * CPR + (cc ^ (row & SW))]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, zf[rt], acc[rt][ct], 0, 0, 0);
+            }
+        }
+        // D layout of the transposed product: lane holds rows 4 g4 + i
+        // (channels) of column r16 (token) of each 16 x 16 tile, so one tile
+        // covers 64 bytes of a token's g row.  Tiles 2j and 2j + 1 together
+        // cover 128 contiguous bytes (a whole cache line) per token: the
+        // second tile's values are rotated by 8 lanes inside each 16-lane row
+        // (DPP), and each store then writes whole lines of 8 tokens -- lanes
+        // r16 < 8 tile 2j of token r16 and lanes r16 >= 8 tile 2j + 1 of token
+        // r16 - 8, or the other 8 tokens -- instead of half lines of 16 tokens.
+#pragma unroll
+        for (int cp = 0; cp < DK / 32; ++cp) {
+            const int ca = 32 * cp + 4 * g4, cb = ca + 16;
+            const f4 ba = bias ? *reinterpret_cast<const f4*>(bias + h * DK + ca) : f4{0.f, 0.f, 0.f, 0.f};
+            const f4 bb = bias ? *reinterpret_cast<const f4*>(bias + h * DK + cb) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                f4 ya, yb;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ya[i] = neg_softplus(acc[rt][2 * cp][i] + ba[i]);
+                    const float b = neg_softplus(acc[rt][2 * cp + 1][i] + bb[i]);
+                    yb[i] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), 0x128, 0xf, 0xf, false));
+                }
+                f4 x, y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[i] = lo ? ya[i] : yb[i];
+                    y[i] = lo ? yb[i] : ya[i];
+                }
+                const int t7 = r16 & 7;
+                const int64_t mx = m0 + 16 * rt + t7, my = mx + 8;
+                const int cx = lo ? ca : cb, cy = lo ? cb : ca;
+                if (mx < M) __builtin_nontemporal_store(x, reinterpret_cast<f4*>(g + mx * N + h * DK + cx));
+                if (my < M) __builtin_nontemporal_store(y, reinterpret_cast<f4*>(g + my * N + h * DK + cy));
+            }
         }
     }
 }
@@ -129,7 +146,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 64 ? 4
 hipError_t launch_fused_gate(const void* z, const void* w, const float* bias, const float* u,
                              int64_t M, int r, int H, float* g, float* beta, hipStream_t stream) {
     using namespace gatek;
-    const dim3 grid(static_cast<uint32_t>((M + ROWS - 1) / ROWS), static_cast<uint32_t>((H + 3) / 4));
+    const dim3 grid(static_cast<uint32_t>((M + 4 * ROWS * NB - 1) / (4 * ROWS * NB)), static_cast<uint32_t>(H));
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(z),
                            static_cast<const uint16_t*>(w), bias, u, M, H, g, beta);
