@@ -68,7 +68,8 @@ struct ChunkItem {
                    // <= -2 row (-sout - 2) of the segment-state buffer, -1 none
     int64_t p0;    // tokens of the sequence before t0
     int32_t snap;  // row of the sequence's first state snapshot, -1 none
-    int32_t pad_;
+    int32_t fin;   // FULL, last segment of a split sequence: row of the final state,
+                   // written here instead of the segment-state row when its map vanished
 };
 
 // Scan over the segment maps of one sequence (all heads).
@@ -83,6 +84,14 @@ namespace chunkk {
 
 constexpr int SB = 16;    // tokens per sub-block
 constexpr int CSEG = 64;  // segment boundaries are multiples of every chunk size
+// Exponent headroom of the propagated matrices: X (scaled into [2^9, 2^10)
+// at its start) is dropped once its fp16 copy at no more than 2^6 above its
+// first exponent rounds to zero, i.e. once max|X| < 2^-25-6-9 max|X_0|:
+// 2^-40 of the map or initial state it started from, far below the fp32
+// resolution of anything that state contributes to at full strength.
+#ifndef PROP_HEADROOM
+#define PROP_HEADROOM 6
+#endif
 constexpr int D = 128;    // head size (d_k = d_v)
 constexpr int QP = 136;   // row stride (halves) of [token][channel] tiles
 constexpr int GP = 20;    // row stride (floats) of 16x16 Gram tiles (16-byte rows)
@@ -1349,6 +1358,10 @@ void chunk_ws_kernel(
         const int col = 32 * (w & 3);
         f4 S[8][NCT];
         int ex = 0;
+        // Propagation modes: the exponent may rise at most PROP_HEADROOM above
+        // the one X starts at, so X's fp16 copy -- and with it the pass --
+        // stops once max|X| has fallen below about 2^-40 of its start.
+        int ex_cap = 1 << 20;
         h8 d16[NCT];      // fp16 Delta (B operand of P Delta, K-bar^T Delta), chunk-local
         bool exited = false;  // propagation modes: X became zero in fp16
         {
@@ -1425,7 +1438,11 @@ void chunk_ws_kernel(
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(vv[rt][ct][i]));
-            const int nex = value_exponent(fmaxf(msw * ldexpf(1.f, -ex), wave_max_nonneg(mv)), ex);
+            int nex = value_exponent(fmaxf(msw * ldexpf(1.f, -ex), wave_max_nonneg(mv)), ex);
+            if (PROP) {
+                if (ex_cap == (1 << 20)) ex_cap = nex + PROP_HEADROOM;  // X's first exponent
+                nex = nex < ex_cap ? nex : ex_cap;
+            }
             if (nex != ex) {
                 const float f = ldexpf(1.f, nex - ex);
 #pragma unroll
@@ -1652,6 +1669,9 @@ void chunk_ws_kernel(
         float* dst = nullptr;
         if (MODE == MODE_FULL && it.sout >= 0 && out_state)
             dst = out_state + (static_cast<int64_t>(it.sout) * H + h) * D * D;
+        else if (MODE == MODE_FULL && it.sout <= -2 && it.fin >= 0 && out_state && mflags &&
+                 mflags[static_cast<int64_t>(-it.sout - 2) * H + h] == 0)
+            dst = out_state + (static_cast<int64_t>(it.fin) * H + h) * D * D;  // final = B (map vanished)
         else if (MODE == MODE_FULL && it.sout <= -2 && bout)
             dst = bout + (static_cast<int64_t>(-it.sout - 2) * H + h) * D * D;
         else if (MODE == MODE_MAP && it.sout >= 0) {
@@ -1689,7 +1709,7 @@ void chunk_ws_kernel(
 __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
     const ScanItem* __restrict__ sitems, int H, const float* __restrict__ h0,
     const float* __restrict__ bst, const float* __restrict__ maps, const int* __restrict__ mflags,
-    float* __restrict__ staged, float* __restrict__ final_state) {
+    float* __restrict__ staged, float* __restrict__ final_state, int inplace) {
     const ScanItem it = sitems[blockIdx.x / H];
     if (it.nseg < 2) return;  // whole workgroup: a single segment ran with its own states
     const int h = blockIdx.x % H;
@@ -1715,25 +1735,40 @@ __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
                 for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] = S[rt][ct][i];
     };
     const float* hsrc = (it.h0 >= 0 && h0) ? h0 + (static_cast<int64_t>(it.h0) * H + h) * D * D : nullptr;
-    if (hsrc) {
+    bool have = false;  // S holds S_j
+    if (inplace && hsrc) {  // the final states overwrite h0: stage it for the correction pass
         load(hsrc);
         put(mrow_of(staged, it.first_seg));
+        have = true;
     }
-    bool have = hsrc != nullptr;  // S holds S_j
     for (int j = 0; j < it.nseg; ++j) {
         const int64_t sj = it.first_seg + j;
         const bool last = j + 1 == it.nseg;
         if (last && it.hT < 0) break;  // no final state wanted
         float* dst = last ? final_state + (static_cast<int64_t>(it.hT) * H + h) * D * D : mrow_of(staged, sj + 1);
-        if (mflags[sj * H + h] == 0) {  // wave-uniform: S_{j+1} = B_j
-            if (last) {
+        // a vanished map (wave-uniform): S_{j+1} = B_j, which the correction
+        // pass reads from the segment-state buffer and (unless in place) the
+        // full pass already wrote as the final state
+        if (mflags[sj * H + h] == 0) {
+            if (last && inplace) {
                 load(row_of(bst, sj));
                 put(dst);
             }
             have = false;
             continue;
         }
-        if (!have) load(row_of(bst, sj - 1));  // j >= 1 here: S_j = B_{j-1}
+        if (!have) {
+            if (j > 0) {
+                load(row_of(bst, sj - 1));  // S_j = B_{j-1}
+            } else if (hsrc) {
+                load(hsrc);  // S_0 = h0
+            } else {
+#pragma unroll
+                for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) S[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
         const float* bj = row_of(bst, sj);
         const float* mp = row_of(maps, sj);
         // B operands from S (k = rows of S, permuted as in the chunk kernel), split hi/lo.
@@ -1802,7 +1837,7 @@ __global__ void plan_sequences_kernel(const int32_t* __restrict__ cu, int N, int
             rank += (lm > len) || (lm == len && m < n);
         }
     }
-    items[rank] = ChunkItem{a, b, has_h0 ? n : -1, has_hT ? n : -1, 0, snap_base ? snap_base[n] : -1, 0};
+    items[rank] = ChunkItem{a, b, has_h0 ? n : -1, has_hT ? n : -1, 0, snap_base ? snap_base[n] : -1, -1};
 }
 
 // Work items of the segmented path.  Each sequence is cut into segments of
@@ -1810,18 +1845,49 @@ __global__ void plan_sequences_kernel(const int32_t* __restrict__ cu, int N, int
 // one FULL item with its own initial and final states.  For the others,
 // segment j (state slot z, numbered over the split sequences only) gets: a
 // FULL item from a zero state writing its final state to row z of the
-// segment-state buffer (sout = -2 - z); a MAP item (sout = z) when its map is
-// needed (j > 0 or h0 given; j < last or a final state wanted), else an
-// empty one (no tokens, sout = -1); a CORR item from staged state z (sin = -2 - z) when
-// that state can be nonzero (j > 0 or h0 given), else an empty one (no
-// tokens).  Items are numbered over all segments; one scan item per sequence.
-// A single workgroup walks the sequences in blocks of 256 with a block scan.
+// segment-state buffer (sout = -2 - z), or, for the last segment, to the
+// final state when its map vanished (fin); a MAP item (sout = z) when its
+// map is needed (j > 0 or h0 given; j < last or a final state wanted), else
+// an empty one (no tokens, sout = -1); a CORR item when the segment's
+// initial state can be nonzero (j > 0 or h0 given) -- from h0 for j = 0,
+// else from staged state z (sin = -2 - z) -- else an empty one.  Items are
+// numbered over all segments; one scan item per sequence.
+//
+// A single workgroup walks the sequences in blocks of 256: a block scan of
+// the segment counts places every sequence's items, then the segments are
+// written one per thread, sequence after sequence.
+__device__ __forceinline__ void write_segment(int j, int G, int64_t a, int64_t b, int seg, int si, int zi,
+                                              int h0row, int hTrow, int snap, int H, int has_h0,
+                                              int has_hT, int inplace, ChunkItem* __restrict__ full_items,
+                                              ChunkItem* __restrict__ map_items,
+                                              ChunkItem* __restrict__ corr_items, int* __restrict__ mflags) {
+    const int64_t sa = a + static_cast<int64_t>(j) * seg;
+    const int64_t sb = sa + seg < b ? sa + seg : b;
+    if (G == 1) {
+        full_items[si] = ChunkItem{sa, sb, h0row, hTrow, 0, snap, -1};
+        map_items[si] = ChunkItem{sa, sa, -1, -1, 0, -1, -1};
+        corr_items[si] = ChunkItem{sa, sa, -1, -1, 0, -1, -1};
+        return;
+    }
+    const bool live_in = j > 0 || has_h0;
+    const bool lastj = j + 1 == G;
+    for (int hh = 0; hh < H; ++hh) mflags[static_cast<int64_t>(zi) * H + hh] = 0;  // set by the map pass
+    // in place (the final states overwrite h0): h0 is read from its staged
+    // copy and every final state is written by the scan, after that copy
+    full_items[si] = ChunkItem{sa, sb, -1, -2 - zi, sa - a, snap, (lastj && !inplace) ? hTrow : -1};
+    map_items[si] = (live_in && (!lastj || has_hT)) ? ChunkItem{sa, sb, -1, zi, sa - a, -1, -1}
+                                                    : ChunkItem{sa, sa, -1, -1, sa - a, -1, -1};
+    corr_items[si] = live_in ? ChunkItem{sa, sb, (j == 0 && !inplace) ? h0row : -2 - zi, -1, sa - a, snap, -1}
+                             : ChunkItem{sa, sa, -1, -1, sa - a, -1, -1};
+}
+
 __global__ __launch_bounds__(256) void plan_segments_kernel(
-    const int32_t* __restrict__ cu, int N, int T, int seg, int has_h0, int has_hT,
+    const int32_t* __restrict__ cu, int N, int T, int seg, int has_h0, int has_hT, int inplace,
     const int32_t* __restrict__ snap_base, ChunkItem* __restrict__ full_items,
     ChunkItem* __restrict__ map_items, ChunkItem* __restrict__ corr_items,
     ScanItem* __restrict__ scan_items, int H, int* __restrict__ mflags) {
-    __shared__ int sc[256], sc2[256];
+    __shared__ int sc[256], sc2[256], gs[256];
+    __shared__ int64_t sa_[256], sb_[256];
     __shared__ int base, base2;
     if (threadIdx.x == 0) base = base2 = 0;
     __syncthreads();
@@ -1838,6 +1904,9 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(
         const int Gs = G > 1 ? G : 0;  // state slots (split sequences only)
         sc[threadIdx.x] = G;
         sc2[threadIdx.x] = Gs;
+        gs[threadIdx.x] = G;
+        sa_[threadIdx.x] = a;
+        sb_[threadIdx.x] = b;
         __syncthreads();
         for (int off = 1; off < 256; off <<= 1) {  // inclusive scans of G and Gs
             const int x = threadIdx.x >= off ? sc[threadIdx.x - off] : 0;
@@ -1847,30 +1916,17 @@ __global__ __launch_bounds__(256) void plan_segments_kernel(
             sc2[threadIdx.x] += y;
             __syncthreads();
         }
-        const int s0 = base + sc[threadIdx.x] - G;      // items of earlier sequences
-        const int z0 = base2 + sc2[threadIdx.x] - Gs;   // state slots of earlier sequences
-        if (n < N) {
-            const int snap = snap_base ? snap_base[n] : -1;
-            const int h0row = has_h0 ? n : -1, hTrow = has_hT ? n : -1;
-            for (int j = 0; j < G; ++j) {
-                const int64_t sa = a + static_cast<int64_t>(j) * seg;
-                const int64_t sb = sa + seg < b ? sa + seg : b;
-                const int si = s0 + j, zi = z0 + j;
-                if (G == 1) {
-                    full_items[si] = ChunkItem{sa, sb, h0row, hTrow, 0, snap, 0};
-                    map_items[si] = ChunkItem{sa, sa, -1, -1, 0, -1, 0};
-                    corr_items[si] = ChunkItem{sa, sa, -1, -1, 0, -1, 0};
-                    continue;
-                }
-                const bool live_in = j > 0 || has_h0;
-                for (int hh = 0; hh < H; ++hh) mflags[static_cast<int64_t>(zi) * H + hh] = 0;  // set by the map pass
-                full_items[si] = ChunkItem{sa, sb, -1, -2 - zi, sa - a, snap, 0};
-                map_items[si] = (live_in && (j + 1 < G || has_hT)) ? ChunkItem{sa, sb, -1, zi, sa - a, -1, 0}
-                                                                   : ChunkItem{sa, sa, -1, -1, sa - a, -1, 0};
-                corr_items[si] = live_in ? ChunkItem{sa, sb, -2 - zi, -1, sa - a, snap, 0}
-                                         : ChunkItem{sa, sa, -1, -1, sa - a, -1, 0};
-            }
-            scan_items[n] = ScanItem{z0, G, h0row, hTrow};
+        if (n < N)
+            scan_items[n] = ScanItem{base2 + sc2[threadIdx.x] - Gs, G, has_h0 ? n : -1, has_hT ? n : -1};
+        const int nb = N - n0 < 256 ? N - n0 : 256;
+        for (int m = 0; m < nb; ++m) {  // sequence n0 + m: its segments over the threads
+            const int Gm = gs[m];
+            const int s0 = base + sc[m] - Gm, z0 = base2 + sc2[m] - (Gm > 1 ? Gm : 0);
+            const int nm = n0 + m;
+            for (int j = threadIdx.x; j < Gm; j += 256)
+                write_segment(j, Gm, sa_[m], sb_[m], seg, s0 + j, z0 + j, has_h0 ? nm : -1,
+                              has_hT ? nm : -1, snap_base ? snap_base[nm] : -1, H, has_h0, has_hT,
+                              inplace, full_items, map_items, corr_items, mflags);
         }
         __syncthreads();
         if (threadIdx.x == 255) {
@@ -1974,6 +2030,11 @@ hipError_t launch_snap_base(const int32_t* cu, int N, int T, int interval, int32
     return hipGetLastError();
 }
 
+#ifndef MIN_SEG64
+#define MIN_SEG64 4
+#endif
+constexpr int kMinSegChunks64 = MIN_SEG64;  // shortest segment, in 64-token units
+
 int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host) {
     // Long sequences are cut so that four segments (workgroups) per CU of a
     // 256-CU part exist over all heads: a whole number of rounds of resident
@@ -1985,7 +2046,7 @@ int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host) {
     if (target_items < 1) target_items = 1;
     int64_t seg = (total + target_items - 1) / target_items;
     seg = (seg + chunkk::CSEG - 1) / chunkk::CSEG * chunkk::CSEG;
-    if (seg < 8 * chunkk::CSEG) seg = 8 * chunkk::CSEG;
+    if (seg < kMinSegChunks64 * chunkk::CSEG) seg = kMinSegChunks64 * chunkk::CSEG;
     return static_cast<int>(seg > (1 << 30) ? (1 << 30) : seg);
 }
 
@@ -2074,15 +2135,20 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
     float* bst = reinterpret_cast<float*>(ws + L.bst);
     float* maps = reinterpret_cast<float*>(ws + L.maps);
     float* staged = reinterpret_cast<float*>(ws + L.staged);
+    // final states written over the initial ones (the same or overlapping rows)
+    const size_t sbytes = static_cast<size_t>(a.N) * a.H * D * D * sizeof(float);
+    const bool inplace = a.h0 && a.hT &&
+                         reinterpret_cast<const char*>(a.h0) < reinterpret_cast<const char*>(a.hT) + sbytes &&
+                         reinterpret_cast<const char*>(a.hT) < reinterpret_cast<const char*>(a.h0) + sbytes;
     hipLaunchKernelGGL(plan_segments_kernel, dim3(1), dim3(256), 0, a.stream, a.cu, a.N, a.T, seg,
-                       a.h0 ? 1 : 0, a.hT ? 1 : 0, a.snap_base, full_items, map_items, corr_items,
-                       scan_items, a.H, mflags);
+                       a.h0 ? 1 : 0, a.hT ? 1 : 0, inplace ? 1 : 0, a.snap_base, full_items, map_items,
+                       corr_items, scan_items, a.H, mflags);
     const bool split = cnt.nsplit > 0;
     if (split) launch_full(map_items, cnt.nseg, nullptr, MODE_MAP, maps, nullptr, mflags);
-    launch_full(full_items, cnt.nseg, nullptr, MODE_FULL, nullptr, bst, nullptr, !split);
+    launch_full(full_items, cnt.nseg, nullptr, MODE_FULL, nullptr, bst, mflags, !split);
     if (split) {
         hipLaunchKernelGGL(segment_scan_kernel, dim3(static_cast<uint32_t>(a.N) * a.H), dim3(256), 0,
-                           a.stream, scan_items, a.H, a.h0, bst, maps, mflags, staged, a.hT);
+                           a.stream, scan_items, a.H, a.h0, bst, maps, mflags, staged, a.hT, inplace ? 1 : 0);
         launch_full(corr_items, cnt.nseg, staged, MODE_CORR, nullptr, bst, mflags);
         // the gated RMSNorm needs the corrected read-out: applied in place after
         if (a.ogate) {
