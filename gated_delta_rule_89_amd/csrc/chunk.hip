@@ -1706,6 +1706,8 @@ void chunk_ws_kernel(
 // (sequence, head); wave w owns state columns [32 w, 32 w + 32).  The
 // 128 x 128 products run on split bf16 MFMA (hi + lo on both operands, three
 // products), about 16 significant bits per operand, fp32 accumulation.
+constexpr int SCAN_FLAGS = 1024;
+
 __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
     const ScanItem* __restrict__ sitems, int H, const float* __restrict__ h0,
     const float* __restrict__ bst, const float* __restrict__ maps, const int* __restrict__ mflags,
@@ -1741,15 +1743,24 @@ __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
         put(mrow_of(staged, it.first_seg));
         have = true;
     }
+    // the map flags of up to SCAN_FLAGS segments at a time, read in parallel
+    // (read one after the other, each waited for a full memory round trip)
+    __shared__ int fl[SCAN_FLAGS];
     for (int j = 0; j < it.nseg; ++j) {
         const int64_t sj = it.first_seg + j;
+        if (j % SCAN_FLAGS == 0) {
+            __syncthreads();
+            const int nb = it.nseg - j < SCAN_FLAGS ? it.nseg - j : SCAN_FLAGS;
+            for (int x = threadIdx.x; x < nb; x += 256) fl[x] = mflags[(sj + x) * H + h];
+            __syncthreads();
+        }
         const bool last = j + 1 == it.nseg;
         if (last && it.hT < 0) break;  // no final state wanted
         float* dst = last ? final_state + (static_cast<int64_t>(it.hT) * H + h) * D * D : mrow_of(staged, sj + 1);
         // a vanished map (wave-uniform): S_{j+1} = B_j, which the correction
         // pass reads from the segment-state buffer and (unless in place) the
         // full pass already wrote as the final state
-        if (mflags[sj * H + h] == 0) {
+        if (fl[j % SCAN_FLAGS] == 0) {
             if (last && inplace) {
                 load(row_of(bst, sj));
                 put(dst);
