@@ -1720,21 +1720,31 @@ __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
     auto row_of = [&](const float* base, int64_t slot) { return base + (slot * H + h) * D * D; };
     auto mrow_of = [&](float* base, int64_t slot) { return base + (slot * H + h) * D * D; };
     f4 S[8][2];
+    // A state row block through a buffer resource over one 64 KB state: the
+    // lane's part of the offset in a vector register, the element's row and
+    // column block in the scalar offset (no 64-bit address per element).
+    constexpr uint32_t SB = D * D * sizeof(float);
+    const int vo = ((4 * g4) * D + col + r) * 4;
+    auto soff = [](int rt, int ct, int i) { return ((16 * rt + i) * D + 16 * ct) * 4; };
     auto load = [&](const float* src) {
+        const auto rs = rsrc(src, SB);
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[rt][ct][i] = src[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
+                for (int i = 0; i < 4; ++i)
+                    S[rt][ct][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo, soff(rt, ct, i), 0));
     };
     auto put = [&](float* dst) {
+        const auto rs = rsrc(dst, SB);
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r] = S[rt][ct][i];
+                for (int i = 0; i < 4; ++i)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[rt][ct][i]), rs, vo, soff(rt, ct, i), 0);
     };
     const float* hsrc = (it.h0 >= 0 && h0) ? h0 + (static_cast<int64_t>(it.h0) * H + h) * D * D : nullptr;
     bool have = false;  // S holds S_j
@@ -1782,47 +1792,40 @@ __global__ __launch_bounds__(256, 1) void segment_scan_kernel(
         }
         const float* bj = row_of(bst, sj);
         const float* mp = row_of(maps, sj);
-        // B operands from S (k = rows of S, permuted as in the chunk kernel), split hi/lo.
-        b8 sh[4][2], sl[4][2];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const float x = m < 4 ? S[2 * ks][ct][m] : S[2 * ks + 1][ct][m - 4];
-                    sh[ks][ct][m] = static_cast<__bf16>(x);
-                    sl[ks][ct][m] = static_cast<__bf16>(x - static_cast<float>(sh[ks][ct][m]));
-                }
+        // S_{j+1} = B_j + M_j S_j in fp32 MFMA (16x16x4): the K-step (mt, i)
+        // takes rows 16 mt + 4 g4 + i of S, i.e. S[mt][ct][i] as it is held,
+        // and the A operand the same 4 consecutive columns of M's row, one
+        // 16-byte read.
+        const auto rb = rsrc(bj, SB), rm = rsrc(mp, SB);
+        const int mo = (r * D + 4 * g4) * 4;  // lane part of row 16 rt + r, columns 16 mt + 4 g4 ..
+        f4 N[8][2];
 #pragma unroll
         for (int rt = 0; rt < 8; ++rt) {
             f4 acc[2];
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[ct][i] = bj[(16 * rt + 4 * g4 + i) * D + col + 16 * ct + r];
-            const float* mrow = mp + (16 * rt + r) * D;  // row of M
+                for (int i = 0; i < 4; ++i)
+                    acc[ct][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, vo, soff(rt, ct, i), 0));
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const f4 lo4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 4 * g4);
-                const f4 hi4 = *reinterpret_cast<const f4*>(mrow + 32 * ks + 16 + 4 * g4);
-                b8 ah, al;
+            for (int mt = 0; mt < 8; ++mt) {  // row 16 rt + r of M
+                const u4 mw = __builtin_amdgcn_raw_buffer_load_b128(rm, mo, (16 * rt * D + 16 * mt) * 4, 0);
+                const f4 am = {__uint_as_float(mw[0]), __uint_as_float(mw[1]), __uint_as_float(mw[2]),
+                               __uint_as_float(mw[3])};
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const float x = m < 4 ? lo4[m] : hi4[m - 4];
-                    ah[m] = static_cast<__bf16>(x);
-                    al[m] = static_cast<__bf16>(x - static_cast<float>(ah[m]));
-                }
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    acc[ct] = mfmab(ah, sh[ks][ct], acc[ct]);
-                    acc[ct] = mfmab(ah, sl[ks][ct], acc[ct]);
-                    acc[ct] = mfmab(al, sh[ks][ct], acc[ct]);
-                }
+                    for (int ct = 0; ct < 2; ++ct)
+                        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[i], S[mt][ct][i], acc[ct], 0, 0, 0);
             }
-            // row block rt of S is consumed (sh, sl hold it), so it is overwritten here
+            N[rt][0] = acc[0];
+            N[rt][1] = acc[1];
+            __builtin_amdgcn_sched_barrier(0);  // one row block's loads in flight at a time
+        }
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) S[rt][ct] = acc[ct];
+        for (int rt = 0; rt < 8; ++rt) {
+            S[rt][0] = N[rt][0];
+            S[rt][1] = N[rt][1];
         }
         put(dst);
         have = true;
