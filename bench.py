@@ -324,9 +324,12 @@ def main():
         vm = time_launches(lambda: kda.fused_recurrent_fwd(vx.q, vx.k, vx.v, vx.g, vx.beta,
                                                            vx.scale, vst, o=vo), stream, 10)
         vb = steps_alg_bytes(Nv, Tv, Hv, dkv, vx.v.shape[-1])
+        vt = measured_traffic("steps", "short runs: 256 sequences x 8 tokens x 32 heads, d=128, state in place")
         line["extras"] = {"fused_recurrent": {
             "us_per_launch": vm * 1e3, "gbs": vb / (vm * 1e-3) / 1e9,
             "frac": vb / (vm * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": vb,
+            "traffic_gb": None if vt is None else vt / 1e9,
+            "frac_of_measured_stream": vb / (vm * 1e-3) / 1e9 / stream_gbs,
             "config": f"{Nv} sequences x {Tv} tokens x {Hv} heads, d={dkv}, state in place"}}
         # The gate inputs from their projections for every token of the workload
         # (kda_fused_gate, bf16 MFMA up-projection of rank 128).
@@ -344,6 +347,8 @@ def main():
             "frac": fb / (fm * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": fb,
             "tflops": ff / (fm * 1e-3) / 1e12,
             "frac_of_measured_write": fb / (fm * 1e-3) / 1e9 / write_gbs,
+            "traffic_gb": (lambda t: None if t is None else t / 1e9)(measured_traffic(
+                "gate", f"fused gate: {tokens} tokens, rank {rk}, H={H}, d_k={dk}")),
             "config": f"{tokens} tokens, rank {rk} up to {H} x {dk} log-gates (fp32) + beta"}
         del zq, uq
         if args.workload == "varlen":
