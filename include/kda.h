@@ -295,11 +295,14 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const fl
  *              overlap any input or the state.
  * 0 <= T <= KDA_FUSED_RECURRENT_MAX_T (longer runs return
  * KDA_ERR_UNSUPPORTED: kda_chunk_fwd is the path for them).  N = 0, H = 0 or
- * T = 0 is a successful no-op.  Speed: the state stays in fp32 registers and
- * every token costs a full pass of vector arithmetic over it, so for bf16
- * inputs with d_k = d_v = 128 and runs of about 16 tokens or more,
- * kda_chunk_fwd (B = N, no cu_seqlens, initial_state = final_state = the
- * state) is faster, within the bf16 tolerance rather than fp32 agreement
+ * T = 0 is a successful no-op.  Arithmetic is fp32 throughout: with
+ * d_k = d_v = 128 the run is taken 8 tokens at a time in the chunk form of
+ * the same section on fp32 matrix cores, otherwise token by token, and the
+ * results agree with kda_decode_step to fp32 rounding.  Speed: the state is
+ * read and written once, but every 8 tokens cost a pass of fp32 products over
+ * it, so for bf16 inputs with d_k = d_v = 128 and runs of about 24 tokens or
+ * more, kda_chunk_fwd (B = N, no cu_seqlens, initial_state = final_state =
+ * the state) is faster, within the bf16 tolerance rather than fp32 agreement
  * with kda_decode_step. */
 kda_status kda_fused_recurrent_fwd(const void* q, const void* k, const void* v, const float* g,
                                    const float* beta, float scale, float* state, int32_t N,
