@@ -56,7 +56,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 256 ? 
     constexpr int CPR = R / 8;                      // 16-byte chunks per W row
     constexpr int SW = CPR < 16 ? CPR - 1 : 15;     // swizzle mask
     __shared__ u4 wl[DK * CPR];
+    __shared__ __align__(16) float bl[DK];  // the head's bias (zeros without one)
     const int tid = threadIdx.x, l = tid & 63, r16 = l & 15, g4 = l >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the z buffer base is scalar
     const int h = blockIdx.y;
     const int64_t N = static_cast<int64_t>(H) * DK;
     {
@@ -66,12 +68,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 256 ? 
             const int ci = tid + 256 * j, row = ci / CPR, cc = ci % CPR;
             wl[row * CPR + (cc ^ (row & SW))] = wh[ci];
         }
+        if (tid < DK) bl[tid] = bias ? bias[h * DK + tid] : 0.f;
     }
     __syncthreads();
     const bool lo = r16 < 8;
 #pragma unroll 1
     for (int nb = 0; nb < NB; ++nb) {
-        const int64_t m0 = (static_cast<int64_t>(blockIdx.x) * NB + nb) * (4 * ROWS) + (tid >> 6) * ROWS;
+        const int64_t m0 = (static_cast<int64_t>(blockIdx.x) * NB + nb) * (4 * ROWS) + wave * ROWS;
         if (m0 >= M) break;  // whole wave; no barrier follows
         if (h == 0) {  // beta of these rows, once per row block
             for (int e = l; e < ROWS * H; e += 64) {
@@ -80,28 +83,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 256 ? 
             }
         }
         f4 acc[RT][DK / 16];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < DK / 16; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-        for (int ks = 0; ks < R / 32; ++ks) {
+        // this wave's rows of z and of g through range-checked buffers: rows past
+        // M read zeros and their stores are dropped
+        const int64_t rows = M - m0 < ROWS ? M - m0 : ROWS;
+        const auto rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(z + m0 * R), 0,
+                                                          static_cast<int>(rows * R * 2), 0x00020000);
+        const auto rg = __builtin_amdgcn_make_buffer_rsrc(g + m0 * N + h * DK, 0,
+                                                          static_cast<int>(((rows - 1) * N + DK) * 4), 0x00020000);
+        // k-step ks; with first, the MFMA takes a zero accumulator operand
+        auto kstep = [&](int ks, bool first) {
             b8 zf[RT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const int64_t m = m0 + 16 * rt + r16;
-                u4 val = {0, 0, 0, 0};
-                if (m < M) val = *reinterpret_cast<const u4*>(z + m * R + 32 * ks + 8 * g4);
-                zf[rt] = __builtin_bit_cast(b8, val);
-            }
+            for (int rt = 0; rt < RT; ++rt)
+                zf[rt] = __builtin_bit_cast(
+                    b8, __builtin_amdgcn_raw_buffer_load_b128(rz, ((16 * rt + r16) * R + 32 * ks + 8 * g4) * 2, 0, 0));
 #pragma unroll
             for (int ct = 0; ct < DK / 16; ++ct) {
                 const int row = 16 * ct + r16, cc = 4 * ks + g4;
                 const b8 wf = __builtin_bit_cast(b8, wl[row * CPR + (cc ^ (row & SW))]);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, zf[rt], acc[rt][ct], 0, 0, 0);
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        wf, zf[rt], first ? f4{0.f, 0.f, 0.f, 0.f} : acc[rt][ct], 0, 0, 0);
             }
+        };
+        if constexpr (R >= 128) {  // (at lower ranks the peeled step costs registers)
+            kstep(0, true);
+#pragma unroll 1
+            for (int ks = 1; ks < R / 32; ++ks) kstep(ks, false);
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < DK / 16; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int ks = 0; ks < R / 32; ++ks) kstep(ks, false);
         }
         // D layout of the transposed product: lane holds rows 4 g4 + i
         // (channels) of column r16 (token) of each 16 x 16 tile, so one tile
@@ -114,8 +130,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 256 ? 
 #pragma unroll
         for (int cp = 0; cp < DK / 32; ++cp) {
             const int ca = 32 * cp + 4 * g4, cb = ca + 16;
-            const f4 ba = bias ? *reinterpret_cast<const f4*>(bias + h * DK + ca) : f4{0.f, 0.f, 0.f, 0.f};
-            const f4 bb = bias ? *reinterpret_cast<const f4*>(bias + h * DK + cb) : f4{0.f, 0.f, 0.f, 0.f};
+            const f4 ba = *reinterpret_cast<const f4*>(&bl[ca]);
+            const f4 bb = *reinterpret_cast<const f4*>(&bl[cb]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 f4 ya, yb;
@@ -123,7 +139,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 256 ? 
                 for (int i = 0; i < 4; ++i) {
                     ya[i] = neg_softplus(acc[rt][2 * cp][i] + ba[i]);
                     const float b = neg_softplus(acc[rt][2 * cp + 1][i] + bb[i]);
-                    yb[i] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), 0x128, 0xf, 0xf, false));
+                    yb[i] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), 0x128, 0xf, 0xf, true));
                 }
                 f4 x, y;
 #pragma unroll
@@ -132,10 +148,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 256 ? 
                     y[i] = lo ? yb[i] : ya[i];
                 }
                 const int t7 = r16 & 7;
-                const int64_t mx = m0 + 16 * rt + t7, my = mx + 8;
+                const int tx = 16 * rt + t7, ty = tx + 8;  // rows of the block
                 const int cx = lo ? ca : cb, cy = lo ? cb : ca;
-                if (mx < M) __builtin_nontemporal_store(x, reinterpret_cast<f4*>(g + mx * N + h * DK + cx));
-                if (my < M) __builtin_nontemporal_store(y, reinterpret_cast<f4*>(g + my * N + h * DK + cy));
+                // non-temporal (cache policy nt), rows past M dropped by the range check
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, x), rg, (tx * static_cast<int>(N) + cx) * 4, 0, 2);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, y), rg, (ty * static_cast<int>(N) + cy) * 4, 0, 2);
             }
         }
     }
