@@ -315,7 +315,7 @@ kda_status kda_fused_gate(const void* z, const void* w_up, const float* b_up, co
         return KDA_ERR_UNSUPPORTED;
     if (M == 0 || H == 0) return KDA_OK;
     if (!z || !w_up || !u || !g || !beta) return KDA_ERR_NULL;
-    if (static_cast<int64_t>(H) * d_k > INT32_MAX / 2) return KDA_ERR_SHAPE;
+    if (H > 65535) return KDA_ERR_SHAPE;  // one grid row per head; 32-bit row offsets within 32 rows of g
     for (const void* p : {z, w_up, static_cast<const void*>(g)})
         if (!aligned(p, 16)) return KDA_ERR_ALIGN;
     if (!aligned(b_up, 16) || !aligned(u, 4) || !aligned(beta, 4)) return KDA_ERR_ALIGN;

@@ -356,8 +356,9 @@ static hipError_t launch_steps_d(const DecodeArgs& a) {
 }
 
 hipError_t launch_steps(const DecodeArgs& a) {
-    // the matrix-core form (its per-sub-chunk offsets are 32-bit: 8 H d_k 4 bytes)
-    if (a.dk == 128 && a.dv == 128 && a.H <= (1 << 20)) return launch_steps_mfma(a);
+    // the matrix-core form: its per-sub-chunk buffer ranges and offsets
+    // (up to 8 H d_k 4 bytes) stay below 2^31 for H <= 2^18
+    if (a.dk == 128 && a.dv == 128 && a.H <= (1 << 18)) return launch_steps_mfma(a);
     return dispatch_head_sizes(a.dk, a.dv, [&](auto DK, auto DV) {
         return launch_steps_d<decltype(DK)::value, decltype(DV)::value>(a);
     });

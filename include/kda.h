@@ -186,8 +186,9 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, cons
  *  g       [M, H, d_k] fp32, written (the layout kda_chunk_fwd reads)
  *  beta    [M, H] fp32, written
  * Only in_dtype = KDA_BF16 with d_k = 128 is supported (else
- * KDA_ERR_UNSUPPORTED).  g and beta must not overlap the inputs or each
- * other.  M = 0 or H = 0 is a successful no-op. */
+ * KDA_ERR_UNSUPPORTED); H above 65535 returns KDA_ERR_SHAPE.  g and beta
+ * must not overlap the inputs or each other.  M = 0 or H = 0 is a
+ * successful no-op. */
 kda_status kda_fused_gate(const void* z, const void* w_up, const float* b_up, const float* u,
                           int32_t M, int32_t r, int32_t H, int32_t d_k, kda_dtype in_dtype,
                           float* g, float* beta, void* stream);

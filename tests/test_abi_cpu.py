@@ -234,7 +234,7 @@ def fgate(z=None, w=None, b=None, u=None, M=100, r=128, H=2, dk=128, ind=BF16, g
 
 def test_fused_gate_validation():
     assert fgate(ind=5) == DTYPE
-    assert fgate(M=-1) == SHAPE
+    assert fgate(M=-1) == SHAPE and fgate(H=65536) == SHAPE
     assert fgate(ind=F32) == UNSUP and fgate(dk=64) == UNSUP and fgate(r=100) == UNSUP
     assert fgate(u=P(0)) == NULL and fgate(g=P(0)) == NULL
     assert fgate(b=P(BASE + 2)) == ALIGN and fgate(w=addr(1, 8)) == ALIGN
