@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP32_PEAK_TFLOPS = 157.3
 
 
 def prefill_alg_bytes(tokens, H, dk, dv, N, in_bytes=2, out_bytes=4, h0=True, final=True):
@@ -387,6 +388,30 @@ def main():
                 "snapshots": nsn, "gbs": sb / (sm * 1e-3) / 1e9,
                 "frac": sb / (sm * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": sb,
                 "config": f"{args.workload} prefill with the state every {iv} tokens"}
+    if args.workload == "varlen" and not args.no_extras:
+        # fp32 inputs of the same shape (full mantissas) through AUTO, which
+        # takes the fp32 chunk kernel (8-token sub-chunks on fp32 MFMA).  Its
+        # figure of merit is the fp32 matrix rate: the chunk form's 6 d_k d_v
+        # FLOPs per token and head ([K~; Q~] S and the state update) against
+        # the fp32 MFMA peak.
+        fx = synth.make_inputs("varlen_f32", device=dev)
+        fo = torch.empty(B, T, H, dv, device=dev, dtype=torch.float32)
+        fws = torch.empty(max(1, kda.workspace_size(B, T, H, dk, dv, N, fx.q.dtype, "auto", cu_host)),
+                          dtype=torch.uint8, device=dev)
+        fm32 = time_launches(lambda: kda.chunk_fwd(fx.q, fx.k, fx.v, fx.g, fx.beta, fx.scale, fx.h0, cu_dev,
+                                                   o=fo, final_state=fin, workspace=fws,
+                                                   cu_seqlens_host=cu_host), stream, 5)
+        f32b = prefill_alg_bytes(tokens, H, dk, dv, N, in_bytes=4)
+        f32f = 6.0 * tokens * H * dk * dv
+        line["extras"]["chunk_fp32"] = {
+            "ms_per_launch": fm32, "tokens_per_s": tokens / (fm32 * 1e-3),
+            "tflops": f32f / (fm32 * 1e-3) / 1e12,
+            "frac_of_fp32_mfma_peak": f32f / (fm32 * 1e-3) / (MFMA_FP32_PEAK_TFLOPS * 1e12),
+            "gbs": f32b / (fm32 * 1e-3) / 1e9, "frac": f32b / (fm32 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "alg_bytes": f32b, "alg_flops": f32f,
+            "config": f"varlen shape with fp32 q/k/v: {N} sequences, {tokens} tokens, H={H}, "
+                      f"d_k=d_v={dk}, fp32 o and states (AUTO: fp32 chunk kernel)"}
+        del fx, fo, fws
     if args.workload == "varlen" and not args.no_long:
         # The long-context workload (one sequence of 1,048,576 tokens, H=32)
         # through the same entry point (AUTO: the segment scan), timed like the

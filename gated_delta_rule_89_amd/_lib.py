@@ -21,7 +21,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_SEQLENS", 6: "KDA_ERR_ALIAS",
           7: "KDA_ERR_ALIGN", 8: "KDA_ERR_WORKSPACE", 9: "KDA_ERR_HIP"}
 F32, BF16 = 0, 1
-VARIANTS = {"auto": 0, "recurrent": 1, "chunk": 2, "chunk_scan": 3, "chunk64": 4}
+VARIANTS = {"auto": 0, "recurrent": 1, "chunk": 2, "chunk_scan": 3, "chunk64": 4, "chunk8": 5}
 EXPORTS = ("kda_abi_version", "kda_status_str", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd", "kda_decode_step", "kda_fused_recurrent_fwd",
            "kda_chunk_fwd_snapshots_workspace_size", "kda_chunk_fwd_snapshots",

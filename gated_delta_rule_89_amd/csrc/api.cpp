@@ -55,7 +55,7 @@ int cu_count() {
 kda_variant resolve_variant(kda_variant v, int32_t B, int32_t T, int32_t H, int32_t dk, int32_t dv,
                             int32_t N, kda_dtype in, const int32_t* cu_host) {
     if (v != KDA_VARIANT_AUTO) return v;
-    if (!chunk_supported(dk, dv, in)) return KDA_VARIANT_RECURRENT;
+    if (!chunk_supported(dk, dv, in)) return KDA_VARIANT_CHUNK8;
     int64_t longest = 0, chunks = 0;
     for (int32_t n = 0; n < N; ++n) {
         const int64_t len = cu_host ? cu_host[n + 1] - cu_host[n] : T;
@@ -72,6 +72,7 @@ kda_variant resolve_variant(kda_variant v, int32_t B, int32_t T, int32_t H, int3
 size_t workspace_for(kda_variant v, int32_t B, int32_t T, int32_t H, int32_t N, const int32_t* cu_host) {
     if (v == KDA_VARIANT_CHUNK || v == KDA_VARIANT_CHUNK_SCAN || v == KDA_VARIANT_CHUNK64)
         return kda::chunk_workspace_bytes(B, T, H, N, cu_host, v == KDA_VARIANT_CHUNK_SCAN);
+    if (v == KDA_VARIANT_CHUNK8) return kda::chunk8_workspace_bytes(N);
     return 0;
 }
 
@@ -117,7 +118,7 @@ size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k
                                     int32_t N, const int32_t* cu_seqlens_host, kda_dtype in_dtype,
                                     kda_variant variant) {
     if (B < 0 || T < 0 || H < 0 || N < 0 || !head_size_ok(d_k) || !head_size_ok(d_v) ||
-        !dtype_ok(in_dtype) || variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK64)
+        !dtype_ok(in_dtype) || variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK8)
         return 0;
     if (cu_seqlens_host ? (B != 1 || !seqlens_ok(cu_seqlens_host, N, T)) : N != B) return 0;
     const kda_variant v = resolve_variant(variant, B, T, H, d_k, d_v, N, in_dtype, cu_seqlens_host);
@@ -144,7 +145,7 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     if (snap_mode && snap_interval % 64 != 0) return KDA_ERR_UNSUPPORTED;
     if (B < 0 || T < 0 || H < 0 || N < 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_SHAPE;
     if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDA_ERR_UNSUPPORTED;
-    if (variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK64) return KDA_ERR_UNSUPPORTED;
+    if (variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK8) return KDA_ERR_UNSUPPORTED;
     if ((cu_seqlens == nullptr) != (cu_seqlens_host == nullptr)) return KDA_ERR_NULL;
     if (cu_seqlens) {
         if (B != 1) return KDA_ERR_SHAPE;
@@ -265,11 +266,13 @@ kda_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         case KDA_VARIANT_CHUNK: e = kda::launch_chunk(a, false, false); break;
         case KDA_VARIANT_CHUNK_SCAN: e = kda::launch_chunk(a, true, false); break;
         case KDA_VARIANT_CHUNK64: e = kda::launch_chunk(a, false, true); break;
+        case KDA_VARIANT_CHUNK8: e = kda::launch_chunk8(a); break;
         default: return KDA_ERR_UNSUPPORTED;
     }
     // The 12-wave kernel (CHUNK, CHUNK_SCAN) fuses the gated RMSNorm into its o
     // store; the other variants write o and the epilogue rewrites it in place.
-    if (e == hipSuccess && gated && (var == KDA_VARIANT_RECURRENT || var == KDA_VARIANT_CHUNK64))
+    if (e == hipSuccess && gated &&
+        (var == KDA_VARIANT_RECURRENT || var == KDA_VARIANT_CHUNK64 || var == KDA_VARIANT_CHUNK8))
         e = kda::launch_gate_norm(a);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -296,7 +299,7 @@ size_t kda_chunk_fwd_snapshots_workspace_size(int32_t B, int32_t T, int32_t H, i
                                               kda_variant variant, int32_t snap_interval) {
     if (snap_interval <= 0 || snap_interval % 64 != 0) return 0;
     if (B < 0 || T < 0 || H < 0 || N < 0 || !head_size_ok(d_k) || !head_size_ok(d_v) ||
-        !dtype_ok(in_dtype) || variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK64)
+        !dtype_ok(in_dtype) || variant < KDA_VARIANT_AUTO || variant > KDA_VARIANT_CHUNK8)
         return 0;
     if (cu_seqlens_host ? (B != 1 || !seqlens_ok(cu_seqlens_host, N, T)) : N != B) return 0;
     const kda_variant v = resolve_variant(variant, B, T, H, d_k, d_v, N, in_dtype, cu_seqlens_host);

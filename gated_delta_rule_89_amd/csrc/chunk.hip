@@ -60,18 +60,6 @@
 
 namespace kda {
 
-// One workgroup's work: tokens [t0, t1) of one sequence, for head blockIdx % H.
-struct ChunkItem {
-    int64_t t0, t1;
-    int32_t sin;   // initial state: >= 0 row of h0, <= -2 row (-sin - 2) of the staged states, -1 zero
-    int32_t sout;  // final state: >= 0 row of the output (the map slot in MAP mode),
-                   // <= -2 row (-sout - 2) of the segment-state buffer, -1 none
-    int64_t p0;    // tokens of the sequence before t0
-    int32_t snap;  // row of the sequence's first state snapshot, -1 none
-    int32_t fin;   // FULL, last segment of a split sequence: row of the final state,
-                   // written here instead of the segment-state row when its map vanished
-};
-
 // Scan over the segment maps of one sequence (all heads).
 struct ScanItem {
     int32_t first_seg;  // index of the sequence's first segment
@@ -2038,6 +2026,13 @@ ScanLayout scan_layout(const SegCount& c, int N, int H) {
 
 int chunk_chains_per_cu() { return kWpc; }
 
+hipError_t launch_plan_sequences(const PrefillArgs& a, ChunkItem* items) {
+    const int lpt = (a.cu && a.N > 1 && a.N <= kLptMaxSeqs) ? 1 : 0;
+    hipLaunchKernelGGL(chunkk::plan_sequences_kernel, dim3((a.N + 255) / 256), dim3(256), 0, a.stream, a.cu, a.N, a.T,
+                       lpt, a.h0 ? 1 : 0, a.hT ? 1 : 0, a.snap_base, items);
+    return hipGetLastError();
+}
+
 hipError_t launch_snap_base(const int32_t* cu, int N, int T, int interval, int32_t* out,
                             hipStream_t stream) {
     hipLaunchKernelGGL(snap_base_kernel, dim3(1), dim3(256), 0, stream, cu, N, T, interval, out);
@@ -2129,9 +2124,8 @@ hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64) {
     };
     if (!scan) {
         ChunkItem* items = reinterpret_cast<ChunkItem*>(ws);
-        const int lpt = (a.cu && a.N > 1 && a.N <= kLptMaxSeqs) ? 1 : 0;
-        hipLaunchKernelGGL(plan_sequences_kernel, dim3((a.N + 255) / 256), dim3(256), 0, a.stream,
-                           a.cu, a.N, a.T, lpt, a.h0 ? 1 : 0, a.hT ? 1 : 0, a.snap_base, items);
+        const hipError_t e = launch_plan_sequences(a, items);
+        if (e != hipSuccess) return e;
         launch_full(items, a.N, nullptr);
         return hipGetLastError();
     }

@@ -1,0 +1,412 @@
+// Chunked prefill for every supported head size (d_k, d_v in {16, 32, 64,
+// 128}) and both input dtypes, in fp32 arithmetic throughout: the chunk form
+// of the recurrence ("Understanding Kimi Delta Attention", section
+// "Understanding the Chunkwise Algorithm") on sub-chunks of 8 tokens, every
+// product on fp32 MFMA (16x16x4) with fp32 accumulation, so that results
+// agree with the token-by-token recurrence (section "The KDA Recurrence") to
+// fp32 rounding.  The matrix-core prefill on fp16 operands serves bf16 inputs
+// at d_k = d_v = 128; this kernel serves fp32 inputs and the other head sizes.
+//
+// For a sub-chunk with start state S (d_k x d_v), per-channel cumulative
+// log-gates G_t from the sub-chunk start and gamma_t = exp(G_t):
+//   K~ = k gamma,  Q~ = q gamma,  K^ = k / gamma,  K- = k gamma_C / gamma
+//   A_ts = beta_t K~_t . K^_s  (s < t),   P_ts = Q~_t . K^_s  (s <= t)
+//   U = (I + A)^-1 Diag(beta) (V - K~ S)
+//   o = scale (Q~ S + P U),   S <- Diag(gamma_C) S + K-^T U
+//
+// Columns of the state evolve independently once the gate-side products
+// (A, T, P) are known, so each (sequence, head) chain is split over XS
+// workgroups of 4 waves, each owning W = d_v / XS columns and forming the
+// gate side itself; each walks the sequence with its columns in MFMA
+// accumulators.  Within a workgroup: for W = 128 wave w owns columns
+// 32 w .. 32 w + 31 as two 16-column tiles (column 32 w + 2 n + nt of tile nt
+// at tile column n); for W <= 64 wave w < W / 16 owns columns 16 w .. 16 w + 15
+// as one tile.  Lane l holds rows 16 mt + 4 (l / 16) + i of
+// tile column l % 16 (the MFMA D layout).  Read as the B operand of the next
+// sub-chunk's [K~; Q~] S product, register i of row tile mt is the K-step
+// over channels 16 mt + 4 (l / 16) + i, and the A operand supplies the same
+// order (a lane's 4 K-steps of a tile are 4 consecutive channels, one 16-byte
+// LDS read).  The 16 rows of [K~; Q~] are permuted (row 4 j + i: K~ of
+// tokens j and 4 + j for i = 0, 1, Q~ of j and 4 + j for i = 2, 3) so that
+// the D tile of that product holds, in lane group g, exactly the tokens g and
+// 4 + g that the next two products take as B-operand K-steps.
+//
+// Per sub-chunk: (A) wave w forms the gate factors of the 32-channel block w
+// (when d_k has one), writes the operand rows to LDS and its partial Grams
+// over those channels (up to 8 MFMAs), then fetches the next sub-chunk's
+// inputs into registers; barrier.  (B) each wave that owns state columns sums
+// the partials, forms T = (I + A)^-1 = (I + N)(I + N^2)(I + N^4) with
+// N = -A (strictly lower 8 x 8, N^8 = 0) and P T, then runs [K~; Q~] S,
+// [T; P T] X with X = Diag(beta)(V - K~ S), which gives U and o together, and
+// the state update; barrier.
+//
+// Strong forgetting: K^ = k / gamma leaves fp32 range when a channel forgets
+// nearly everything inside the sub-chunk.  A block whose gate total passes
+// 2^-110 forms its partial Grams entry by entry, with exp(G_t - G_s) <= 1
+// taken from the exponents themselves.  Per-token log-gates below -100 are
+// taken as -100 (alpha = e^-100 vanishes next to any fp32 state entry), so
+// that every exponent difference stays finite.
+#include "kda_internal.h"
+#include "mfma_f32.h"
+
+namespace kda {
+namespace c8 {
+
+using namespace f32m;
+
+constexpr int C = 8;      // tokens per sub-chunk
+constexpr int KBS = 10;   // stride of the K-^T rows (8 token slots; 10 spreads the banks)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float GMIN = -144.26950408889634f;  // -100 nats in log2 units
+constexpr float SAFE = 110.f;                 // -G_C (log2) up to which K^ stays in range
+
+template <int DK>
+struct Smem {
+    float kq[16][DK + 4];    // [K~; Q~] rows in the permuted order
+    float kc[C][DK + 4];     // K^ by token
+    float kb[DK][KBS];       // K-^T: channel row, token t at slot 2 (t % 4) + t / 4
+    float gc[DK];            // gamma_C
+    float beta[C];
+    float gp[4][16][16];     // the blocks' partial Grams: [row of [K~; Q~]][token s]
+    float mat[4][4][C * C];  // per wave: the 8 x 8 products
+    float raw[4][3][C][32];  // per block, direct Grams only: k, q, G (log2) of its channels
+};
+
+template <int DK, int DV, int XS, typename Tin, typename Tout>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((DK == 128 && DV / XS == 128) ? 3 : 4)))
+void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+                   const float* __restrict__ g, const float* __restrict__ beta, float scale,
+                   const ChunkItem* __restrict__ items, int H, const float* __restrict__ h0,
+                   Tout* __restrict__ o, float* __restrict__ hT, float* __restrict__ snaps, int interval) {
+    constexpr int MT = DK / 16;                 // row tiles of the state
+    constexpr int CB = DK < 32 ? DK : 32;       // channels of a phase-A block
+    constexpr int NBLK = DK / CB;               // blocks: wave w < NBLK takes block w
+    constexpr int MI = CB / 16;                 // 16-channel K tiles of a block
+    constexpr int W = DV / XS;                  // state columns of this workgroup
+    constexpr int NT = W == 128 ? 2 : 1;        // state tiles per wave
+    constexpr int NWB = W / (16 * NT);          // waves holding state columns
+    __shared__ __align__(16) Smem<DK> sm;
+
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = l & 15, g4 = l >> 4;
+    const int chain = blockIdx.x / XS;  // the XS workgroups of a chain are adjacent
+    const ChunkItem it = items[chain / H];
+    const int h = chain % H;
+    const int64_t t0 = it.t0, t1 = it.t1;
+    const bool bw = NWB == 4 || w < NWB;   // wave owns state columns
+    const bool aw = NBLK == 4 || w < NBLK; // wave forms a channel block
+    // tile nt holds column col + nt
+    const int col = (blockIdx.x % XS) * W + (NT == 2 ? 32 * w + 2 * r16 : 16 * w + r16);
+    const int cl = l & 31, hs = l >> 5;    // phase A: channel 32 w + cl, tokens 4 hs .. 4 hs + 3
+    const bool al = aw && cl < CB;
+    const int cw = 32 * w + cl;
+    const int a8 = l >> 3, b8 = l & 7;     // lane (row, column) of the 8 x 8 matrices
+    float* const mw = &sm.mat[w][0][0];
+    constexpr int64_t SD = static_cast<int64_t>(DK) * DV;
+
+    f4 acc[MT][NT];  // acc[mt][nt][i] = S[16 mt + 4 g4 + i][col + nt]
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+    if (bw && it.sin >= 0) {
+        const float* S0 = h0 + (static_cast<int64_t>(it.sin) * H + h) * SD + col;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mt + 4 * g4 + i;
+                if (NT == 2) {
+                    const f2 x = *reinterpret_cast<const f2*>(S0 + row * DV);
+                    acc[mt][0][i] = x[0];
+                    acc[mt][NT - 1][i] = x[1];
+                } else {
+                    acc[mt][0][i] = S0[row * DV];
+                }
+            }
+    }
+
+    // Inputs of the next sub-chunk, fetched while the current one is computed.
+    // Token t of a sub-chunk is at element t H d + c from its first token; the
+    // buffers end after its last real token, so later tokens read zeros.
+    float kx[4] = {0.f, 0.f, 0.f, 0.f}, qx[4] = {0.f, 0.f, 0.f, 0.f}, gx[4] = {0.f, 0.f, 0.f, 0.f};
+    float vx[2][NT] = {}, bx = 0.f;
+    auto fetch = [&](int64_t s0) {
+        const int64_t left = t1 - s0;
+        const uint32_t span = static_cast<uint32_t>(left < C ? left : C) * H;  // (token, head) rows
+        const int64_t first = s0 * H + h;
+        if (al) {
+            const auto rk = rsrc(k + first * DK, span * DK * sizeof(Tin));
+            const auto rq = rsrc(q + first * DK, span * DK * sizeof(Tin));
+            const auto rg = rsrc(g + first * DK, span * DK * 4u);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e = static_cast<uint32_t>(4 * hs + j) * H * DK + cw;
+                kx[j] = bld(rk, e, k);
+                qx[j] = bld(rq, e, q);
+                gx[j] = bld(rg, e, g);
+            }
+        }
+        if (bw) {
+            const auto rv = rsrc(v + first * DV, span * DV * sizeof(Tin));
+            const uint32_t eg = static_cast<uint32_t>(g4) * H * DV + col;
+            const uint32_t e4 = static_cast<uint32_t>(4 + g4) * H * DV + col;
+            if (NT == 2) {
+                const f2 a = bld2(rv, eg, v), b = bld2(rv, e4, v);
+                vx[0][0] = a[0];
+                vx[0][NT - 1] = a[1];
+                vx[1][0] = b[0];
+                vx[1][NT - 1] = b[1];
+            } else {
+                vx[0][0] = bld(rv, eg, v);
+                vx[1][0] = bld(rv, e4, v);
+            }
+        }
+        bx = bld(rsrc(beta + first, span * 4u), (l & 7) * H, beta);
+    };
+    if (t0 < t1) fetch(t0);
+
+    int64_t next_snap = interval;
+    int64_t snap_row = it.snap;
+    for (int64_t s0 = t0; s0 < t1; s0 += C) {
+        // ---- (A) gate factors of channel cw, tokens 4 hs + j ----
+        if (aw) {
+            float G2[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) G2[j] = fmaxf(gx[j] * LOG2E, GMIN);
+            G2[1] += G2[0];
+            G2[2] += G2[1];
+            G2[3] += G2[2];
+            // lanes 0-31 hold tokens 0-3 and lanes 32-63 tokens 4-7 of the same channels
+            const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(G2[3]), __float_as_uint(G2[3]),
+                                                            false, false);
+            const float lo = __uint_as_float(p[0]), hi = __uint_as_float(p[1]);
+            const float GC = lo + hi;
+            if (hs) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) G2[j] += lo;
+            }
+            const bool direct = __any(-GC > SAFE);
+            if (al) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float e = __builtin_amdgcn_exp2f(G2[j]);
+                    sm.kq[4 * j + hs][cw] = kx[j] * e;
+                    sm.kq[4 * j + 2 + hs][cw] = qx[j] * e;
+                    sm.kc[4 * hs + j][cw] = kx[j] * __builtin_amdgcn_exp2f(-G2[j]);
+                    sm.kb[cw][2 * j + hs] = kx[j] * __builtin_amdgcn_exp2f(GC - G2[j]);
+                }
+                if (!hs) sm.gc[cw] = __builtin_amdgcn_exp2f(GC);
+                if (direct) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        sm.raw[w][0][4 * hs + j][cl] = kx[j];
+                        sm.raw[w][1][4 * hs + j][cl] = qx[j];
+                        sm.raw[w][2][4 * hs + j][cl] = G2[j];
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();  // this wave's rows of the tiles are written
+
+            // partial Grams over this block's channels: D[4 g4 + i][s = r16]
+            f4 gacc = {0.f, 0.f, 0.f, 0.f};
+            if (!direct) {
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) {
+                    const int c0 = 32 * w + 16 * mi + 4 * g4;
+                    const f4 av = *reinterpret_cast<const f4*>(&sm.kq[r16][c0]);
+                    f4 bv = *reinterpret_cast<const f4*>(&sm.kc[r16 & 7][c0]);
+                    if (r16 >= C) bv = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) gacc = mfma4(av[i], bv[i], gacc);
+                }
+            } else {
+                // entry by entry: row 4 g4 + i is K~ (i < 2) or Q~ of token
+                // g4 + 4 (i & 1); column s = r16; exp(G_t - G_s) <= 1 where used
+                const int s = r16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = g4 + 4 * (i & 1);
+                    const bool use = s < C && ((i < 2) ? s < t : s <= t);
+                    float acc1 = 0.f;
+                    if (use) {
+                        const float* xt = sm.raw[w][i < 2 ? 0 : 1][t];
+                        const float* gt = sm.raw[w][2][t];
+                        const float* ks = sm.raw[w][0][s];
+                        const float* gs = sm.raw[w][2][s];
+#pragma unroll 4
+                        for (int c = 0; c < CB; ++c)
+                            acc1 += xt[c] * ks[c] * __builtin_amdgcn_exp2f(fminf(gt[c] - gs[c], 0.f));
+                    }
+                    gacc[i] = acc1;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.gp[w][4 * g4 + i][r16] = gacc[i];
+        }
+        if (w == 0 && l < C) sm.beta[l] = bx;
+        float vc[2][NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            vc[0][nt] = vx[0][nt];
+            vc[1][nt] = vx[1][nt];
+        }
+        if (s0 + C < t1) fetch(s0 + C);
+        __syncthreads();
+
+        // ---- (B) ----
+        if (bw) {
+            // N = -A and P on lane (a8, b8); T = (I + N)(I + N^2)(I + N^4); P T
+            {
+                const int rk = 4 * (a8 & 3) + (a8 >> 2);  // row of K~ of token a8 in [K~; Q~]
+                float gk = 0.f, gq = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NBLK; ++ww) {
+                    gk += sm.gp[ww][rk][b8];
+                    gq += sm.gp[ww][rk + 2][b8];
+                }
+                const float nab = b8 < a8 ? -sm.beta[a8] * gk : 0.f;
+                const float pab = b8 <= a8 ? gq : 0.f;
+                solve8(mw, nab, pab, a8, b8, l);
+            }
+
+            // [K~; Q~] S
+            f4 y[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) y[nt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const f4 av = *reinterpret_cast<const f4*>(&sm.kq[r16][16 * mt + 4 * g4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) y[nt] = mfma4(av[i], acc[mt][nt][i], y[nt]);
+            }
+
+            // X = Diag(beta)(V - K~ S) for tokens g4 and 4 + g4; [T; P T] X
+            const float bg = sm.beta[g4], b4 = sm.beta[4 + g4];
+            // A operand of [T; P T]: row r16 = 4 g' + i' (i' < 2: T, else P T; token g' + 4 (i' & 1))
+            const int ra = (r16 >> 2) + 4 * (r16 & 1);
+            const float* const Mt = (r16 & 2) ? mw + 128 : mw + 64;
+            const float m0 = Mt[8 * ra + g4], m1 = Mt[8 * ra + 4 + g4];
+            f4 z[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const float xg = bg * (vc[0][nt] - y[nt][0]);
+                const float x4 = b4 * (vc[1][nt] - y[nt][1]);
+                z[nt] = f4{0.f, 0.f, y[nt][2], y[nt][3]};
+                z[nt] = mfma4(m0, xg, z[nt]);
+                z[nt] = mfma4(m1, x4, z[nt]);
+            }
+            // o of tokens g4 and 4 + g4 (rows 2 and 3)
+            {
+                const int64_t left = t1 - s0;
+                const uint32_t span = static_cast<uint32_t>(left < C ? left : C) * H;
+                const auto ro = rsrc(o + (s0 * H + h) * DV, span * DV * sizeof(Tout));
+                const uint32_t eg = static_cast<uint32_t>(g4) * H * DV + col;
+                const uint32_t e4 = static_cast<uint32_t>(4 + g4) * H * DV + col;
+                if (NT == 2) {
+                    bst2(ro, eg, f2{scale * z[0][2], scale * z[NT - 1][2]}, o);
+                    bst2(ro, e4, f2{scale * z[0][3], scale * z[NT - 1][3]}, o);
+                } else {
+                    bst(ro, eg, scale * z[0][2], o);
+                    bst(ro, e4, scale * z[0][3], o);
+                }
+            }
+
+            // S <- Diag(gamma_C) S + K-^T U  (U of tokens g4, 4 + g4 in rows 0, 1)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const f4 gv = *reinterpret_cast<const f4*>(&sm.gc[16 * mt + 4 * g4]);
+                const f2 kv = *reinterpret_cast<const f2*>(&sm.kb[16 * mt + r16][2 * g4]);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    acc[mt][nt] *= gv;
+                    acc[mt][nt] = mfma4(kv[0], z[nt][0], acc[mt][nt]);
+                    acc[mt][nt] = mfma4(kv[1], z[nt][1], acc[mt][nt]);
+                }
+            }
+
+            // the state after each `interval` tokens of the sequence
+            const int64_t done = (s0 + C < t1 ? s0 + C : t1) - t0;
+            if (snaps && done == next_snap) {
+                float* dst = snaps + (snap_row * H + h) * SD + col;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * mt + 4 * g4 + i;
+                        if (NT == 2)
+                            *reinterpret_cast<f2*>(dst + row * DV) = f2{acc[mt][0][i], acc[mt][NT - 1][i]};
+                        else
+                            dst[row * DV] = acc[mt][0][i];
+                    }
+                next_snap += interval;
+                ++snap_row;
+            }
+        }
+        __syncthreads();  // the tiles are rewritten by the next sub-chunk
+    }
+
+    if (bw && it.sout >= 0) {
+        float* S1 = hT + (static_cast<int64_t>(it.sout) * H + h) * SD + col;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * mt + 4 * g4 + i;
+                if (NT == 2)
+                    *reinterpret_cast<f2*>(S1 + row * DV) = f2{acc[mt][0][i], acc[mt][NT - 1][i]};
+                else
+                    S1[row * DV] = acc[mt][0][i];
+            }
+    }
+}
+
+// Workgroups per chain: two column halves for d_v = 128, where a chain's
+// sub-chunk is dominated by matrix-core time on its critical path (the
+// varlen workload in fp32: 17.5 -> 15.2 ms).  For d_v <= 64 the sub-chunk
+// is bound by the latency of its dependent steps, which a split does not
+// shorten, and the duplicated gate side costs more than it saves.
+#ifndef CHUNK8_SPLIT
+#define CHUNK8_SPLIT 2
+#endif
+template <int DV>
+constexpr int split_of() {
+    return DV == 128 ? CHUNK8_SPLIT : 1;
+}
+
+template <int DK, int DV, typename Tin, typename Tout>
+hipError_t launch_t(const PrefillArgs& a, const ChunkItem* items) {
+    constexpr int XS = split_of<DV>();
+    hipLaunchKernelGGL((chunk8_kernel<DK, DV, XS, Tin, Tout>), dim3(static_cast<uint32_t>(a.N) * a.H * XS), dim3(256), 0,
+                       a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
+                       static_cast<const Tin*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
+                       static_cast<Tout*>(a.o), a.hT, a.snaps, a.snap_interval);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_d(const PrefillArgs& a, const ChunkItem* items) {
+    if (a.in_bf16)
+        return a.out_bf16 ? launch_t<DK, DV, bf16_t, bf16_t>(a, items) : launch_t<DK, DV, bf16_t, float>(a, items);
+    return a.out_bf16 ? launch_t<DK, DV, float, bf16_t>(a, items) : launch_t<DK, DV, float, float>(a, items);
+}
+
+}  // namespace c8
+
+size_t chunk8_workspace_bytes(int N) {
+    return (static_cast<size_t>(N) * sizeof(ChunkItem) + 255) / 256 * 256;
+}
+
+hipError_t launch_chunk8(const PrefillArgs& a) {
+    ChunkItem* items = static_cast<ChunkItem*>(a.ws);
+    const hipError_t e = launch_plan_sequences(a, items);
+    if (e != hipSuccess) return e;
+    return dispatch_head_sizes(a.dk, a.dv, [&](auto DK, auto DV) {
+        return c8::launch_d<decltype(DK)::value, decltype(DV)::value>(a, items);
+    });
+}
+
+}  // namespace kda

@@ -34,6 +34,19 @@ struct PrefillArgs {
     hipStream_t stream;
 };
 
+// One workgroup's work in the chunked kernels: tokens [t0, t1) of one
+// sequence, for head blockIdx % H.
+struct ChunkItem {
+    int64_t t0, t1;
+    int32_t sin;   // initial state: >= 0 row of h0, <= -2 row (-sin - 2) of the staged states, -1 zero
+    int32_t sout;  // final state: >= 0 row of the output (the map slot in MAP mode),
+                   // <= -2 row (-sout - 2) of the segment-state buffer, -1 none
+    int64_t p0;    // tokens of the sequence before t0
+    int32_t snap;  // row of the sequence's first state snapshot, -1 none
+    int32_t fin;   // FULL, last segment of a split sequence: row of the final state,
+                   // written here instead of the segment-state row when its map vanished
+};
+
 struct DecodeArgs {
     const void* q;
     const void* k;
@@ -86,12 +99,20 @@ hipError_t launch_gate_norm(const PrefillArgs& a);
 // Chunked MFMA prefill (bf16 inputs, d_k = d_v = 128).  With scan = true long
 // sequences are cut into segments whose (B, M) maps are composed by a scan.
 // cu_host may be null (then the N sequences are rows of length T).
-int chunk_chains_per_cu();
+int chunk_chains_per_cu();  // full-mode chunk workgroups resident per CU
+// Row of each sequence's first snapshot (floor(length / interval) each).
 hipError_t launch_snap_base(const int32_t* cu, int N, int T, int interval, int32_t* out,
-                            hipStream_t stream);  // full-mode chunk workgroups resident per CU
+                            hipStream_t stream);
 int chunk_segment_tokens(int B, int T, int H, int N, const int32_t* cu_host);
 size_t chunk_workspace_bytes(int B, int T, int H, int N, const int32_t* cu_host, bool scan);
 // scan: segment-scan path; c64: single-role kernel on 64-token chunks.
 hipError_t launch_chunk(const PrefillArgs& a, bool scan, bool c64);
+// One item per sequence (whole sequence, its own h0/hT rows and first
+// snapshot row), longest first when cu is given and N is at most 16384.
+hipError_t launch_plan_sequences(const PrefillArgs& a, ChunkItem* items);
+// Any supported head size and input dtype: the chunk form on 8-token
+// sub-chunks in fp32 MFMA.  Workspace: chunk8_workspace_bytes(N).
+size_t chunk8_workspace_bytes(int N);
+hipError_t launch_chunk8(const PrefillArgs& a);
 
 }  // namespace kda

@@ -80,13 +80,20 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *  CHUNK64    chunkwise kernel on 64-token chunks (four 16-token
  *             sub-blocks), 8 waves per (sequence, head) doing the gate-side
  *             and then the state work of each chunk; same inputs as CHUNK.
- *             Never chosen by AUTO. */
+ *             Never chosen by AUTO.
+ *  CHUNK8     chunkwise kernel in fp32 arithmetic throughout (fp32 MFMA,
+ *             8-token sub-chunks), one workgroup of 4 waves per (sequence,
+ *             head); any supported head size, fp32 or bf16 inputs, results
+ *             within fp32 rounding of the token-by-token recurrence.  AUTO
+ *             takes it for the arguments CHUNK does not support (fp32
+ *             inputs, d_k or d_v other than 128). */
 typedef enum kda_variant {
     KDA_VARIANT_AUTO = 0,
     KDA_VARIANT_RECURRENT = 1,
     KDA_VARIANT_CHUNK = 2,
     KDA_VARIANT_CHUNK_SCAN = 3,
-    KDA_VARIANT_CHUNK64 = 4
+    KDA_VARIANT_CHUNK64 = 4,
+    KDA_VARIANT_CHUNK8 = 5
 } kda_variant;
 
 /* ABI version (KDA_ABI_VERSION of the built library). */
@@ -154,7 +161,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
  *  norm_weight [d_v] fp32, shared by all heads; an input.
  *  norm_eps    >= 0 and finite (else KDA_ERR_SHAPE).
  * The 12-wave chunk kernel (CHUNK, CHUNK_SCAN) applies this in its o store;
- * RECURRENT and CHUNK64 write o and then rewrite it in place.  The
+ * RECURRENT, CHUNK64 and CHUNK8 write o and then rewrite it in place.  The
  * workspace is that of kda_chunk_fwd_workspace_size(); every other argument
  * and error behaviour is that of kda_chunk_fwd. */
 kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const float* g,

@@ -78,6 +78,9 @@ WORKLOADS = {
                        g_mu=-2.0, g_sigma=2.0, h0_std=0.02, seed=4, n_seqs=64),
     "long": Workload("long", H=32, dk=128, dv=128, T=1048576, in_dtype=torch.bfloat16,
                      g_mu=-3.0, g_sigma=2.0, h0_std=0.0, seed=5),
+    # the varlen workload's distributions with fp32 q/k/v (full mantissas)
+    "varlen_f32": Workload("varlen_f32", H=32, dk=128, dv=128, T=262144, in_dtype=torch.float32,
+                           g_mu=-2.0, g_sigma=2.0, h0_std=0.02, seed=8, n_seqs=64),
 }
 
 
@@ -193,7 +196,7 @@ def make_inputs(name: str, device="cpu", T: Optional[int] = None, H: Optional[in
     cu = None
     if lens is not None:
         cu = cu_seqlens_from_lengths(lens)
-    elif name == "varlen":
+    elif name in ("varlen", "varlen_f32"):
         if T is None and n_seqs is None:
             cu = cu_seqlens_from_lengths(varlen_lengths())
         else:

@@ -90,11 +90,17 @@ def test_chunk_validation():
     assert chunk(cu=addr(8), cu_host=bad2, N=2) == SEQ
     keep3, bad3 = host_cu([1, 30, 64])
     assert chunk(cu=addr(8), cu_host=bad3, N=2) == SEQ
-    # aliasing: o over q; final over q; final partially over the initial state
-    assert chunk(o=addr(0)) == ALIAS
-    assert chunk(fin=addr(1)) == ALIAS
-    assert chunk(h0=addr(6), fin=addr(6, 1024)) == ALIAS
-    assert chunk(o=addr(7), fin=addr(7, 4096)) == ALIAS
+    # AUTO takes the fp32 chunked kernel for these fp32 d = 16 inputs: it needs
+    # the item list, checked before the aliasing
+    assert chunk() == WS
+    assert chunk(variant=5, ws=addr(9), ws_bytes=64) == WS
+    # aliasing (the recurrent variant needs no workspace): o over q; final
+    # over q; final partially over the initial state; workspace over o
+    assert chunk(o=addr(0), variant=1) == ALIAS
+    assert chunk(fin=addr(1), variant=1) == ALIAS
+    assert chunk(h0=addr(6), fin=addr(6, 1024), variant=1) == ALIAS
+    assert chunk(o=addr(7), fin=addr(7, 4096), variant=1) == ALIAS
+    assert chunk(o=addr(7), ws=addr(7, 256), ws_bytes=256) == ALIAS
 
 
 def test_workspace_size_rejects_bad_arguments():
@@ -118,6 +124,8 @@ def test_workspace_size_grows_with_segments():
     assert 0 < plain < 4096 and scan > 4 * 128 * 128 * 4
     assert ws(1, 100100, 4, 128, 128, 2, cu, BF16, 1) == 0
     assert ws(1, 100100, 4, 128, 128, 2, cu, BF16, 4) == plain     # CHUNK64: item list only
+    assert ws(1, 100100, 4, 128, 128, 2, cu, BF16, 5) == plain     # CHUNK8: item list only
+    assert ws(1, 100100, 4, 16, 64, 2, cu, F32, 0) == plain        # AUTO on fp32: CHUNK8
 
 
 def decode(q=None, k=None, v=None, g=None, beta=None, state=None, N=4, H=2, dk=16, dv=16,

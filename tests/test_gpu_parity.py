@@ -42,11 +42,11 @@ def run_prefill(x, variant="auto", **kw):
     return o, f
 
 
-VARIANTS = ["auto", "recurrent", "chunk", "chunk_scan", "chunk64"]
+VARIANTS = ["auto", "recurrent", "chunk", "chunk_scan", "chunk64", "chunk8"]
 CHUNKED = ["chunk", "chunk64"]  # the two chunkwise kernels (32- and 64-token chunks)
 
 
-@pytest.mark.parametrize("variant", ["auto", "recurrent"])
+@pytest.mark.parametrize("variant", ["auto", "recurrent", "chunk8"])
 def test_tiny_fp32(variant):
     say(f"tiny fp32 T=64 d=16 variant={variant}")
     x = synth.make_inputs("tiny")
@@ -80,9 +80,11 @@ def test_varlen_ragged(variant):
     assert torch.equal(f[1].cpu(), x.h0[1])
 
 
-@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 16), (16, 128), (128, 128)])
-def test_head_sizes_fp32(dk, dv):
-    say(f"recurrent fp32 dk={dk} dv={dv} B=2 T=37 H=2")
+@pytest.mark.parametrize("variant", ["recurrent", "chunk8"])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 16), (16, 128), (128, 128),
+                                   (64, 64), (32, 32), (128, 64), (64, 128)])
+def test_head_sizes_fp32(dk, dv, variant):
+    say(f"{variant} fp32 dk={dk} dv={dv} B=2 T=37 H=2")
     rng = np.random.default_rng(dk * 1000 + dv)
     B, T, H = 2, 37, 2
     q = torch.tensor(rng.standard_normal((B, T, H, dk)), dtype=torch.float32)
@@ -95,7 +97,7 @@ def test_head_sizes_fp32(dk, dv):
     h0 = torch.tensor(0.1 * rng.standard_normal((B, H, dk, dv)), dtype=torch.float32)
     dev = torch.device("cuda")
     o, f = _kda().chunk_fwd(q.to(dev), k.to(dev), v.to(dev), g.to(dev), beta.to(dev), 0.3,
-                            h0.to(dev), variant="recurrent")
+                            h0.to(dev), variant=variant)
     o_ref, f_ref = ref.kda_forward(q, k, v, g, beta, 0.3, h0)
     assert_parity(o, o_ref, torch.float32, "o")
     assert_parity(f, f_ref, torch.float32, "final")
@@ -215,7 +217,8 @@ def test_fused_recurrent_empty_and_rejects_long_runs():
 
 
 @pytest.mark.parametrize("variant,interval", [("chunk", 64), ("chunk", 192), ("chunk64", 128),
-                                              ("recurrent", 64), ("chunk_scan", 256)])
+                                              ("recurrent", 64), ("chunk_scan", 256), ("chunk8", 64),
+                                              ("chunk8", 192)])
 def test_snapshots_varlen(variant, interval):
     say(f"snapshots variant={variant} interval={interval} (ragged varlen, H=2)")
     lens = [1, 63, 64, 65, 200, 384, 700, 1030] if variant != "chunk_scan" else [64, 2500, 4096, 130]
@@ -295,7 +298,7 @@ def _gate_inputs(x, seed=7):
     return gate, w
 
 
-@pytest.mark.parametrize("variant", ["chunk", "chunk_scan", "chunk64", "recurrent"])
+@pytest.mark.parametrize("variant", ["chunk", "chunk_scan", "chunk64", "recurrent", "chunk8"])
 def test_gated_rmsnorm_output(variant):
     say(f"gated RMSNorm output variant={variant} (ragged varlen, H=2)")
     lens = [1, 31, 33, 64, 200, 700] if variant != "chunk_scan" else [64, 2500, 130]
@@ -313,8 +316,9 @@ def test_gated_rmsnorm_output(variant):
     assert_parity(f, f_ref, x.q.dtype, "final")
 
 
-def test_gated_rmsnorm_fp32_recurrent_and_bf16_out():
-    say("gated RMSNorm, fp32 inputs (recurrent, d=32/64), fp32 and bf16 outputs")
+@pytest.mark.parametrize("variant", ["recurrent", "chunk8"])
+def test_gated_rmsnorm_fp32_and_bf16_out(variant):
+    say(f"gated RMSNorm, fp32 inputs ({variant}, d=32/64), fp32 and bf16 outputs")
     rng = np.random.default_rng(3)
     B, T, H, dk, dv = 2, 40, 3, 32, 64
     q = torch.tensor(rng.standard_normal((B, T, H, dk)), dtype=torch.float32)
@@ -328,9 +332,10 @@ def test_gated_rmsnorm_fp32_recurrent_and_bf16_out():
     args = [t.to(dev) for t in (q, k, v, g, beta)]
     o_ref, _ = ref.kda_forward(q, k, v, g, beta, 0.3)
     y_ref = ref.rms_norm_gate(o_ref, gate, w, 1e-6)
-    y, _ = _kda().chunk_fwd(*args, 0.3, out_gate=gate.to(dev), norm_weight=w.to(dev), norm_eps=1e-6)
+    y, _ = _kda().chunk_fwd(*args, 0.3, out_gate=gate.to(dev), norm_weight=w.to(dev), norm_eps=1e-6,
+                            variant=variant)
     yb, _ = _kda().chunk_fwd(*args, 0.3, out_gate=gate.to(dev), norm_weight=w.to(dev), norm_eps=1e-6,
-                             out_dtype=torch.bfloat16)
+                             out_dtype=torch.bfloat16, variant=variant)
     torch.cuda.synchronize()
     assert max_abs(y, y_ref) <= 1e-4
     # bf16 output: o is written in bf16 and rewritten in place, so each value
@@ -606,7 +611,7 @@ def strong_forget_gates(shape, seed):
     return g
 
 
-@pytest.mark.parametrize("variant", GATE_VARIANTS + ["auto", "recurrent"])
+@pytest.mark.parametrize("variant", GATE_VARIANTS + ["auto", "recurrent", "chunk8"])
 def test_chunk_strong_forget(variant):
     """Full forgetting on some channels and tokens, none on others, compared
     with the oracle; a random initial state shows whether it is wiped."""
@@ -658,6 +663,77 @@ def test_chunk_matches_recurrent_varlen():
     oc, fc = run_prefill(x, "chunk")
     orc, frc = run_prefill(x, "recurrent")
     assert rel_rms(oc, orc) <= 2e-2 and rel_rms(fc, frc) <= 2e-2
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (16, 16), (32, 128), (128, 32), (64, 16)])
+def test_chunk8_varlen_fp32(dk, dv):
+    """fp32 inputs with full mantissas through packed sequences (empty, one
+    token, ragged 8-token tails, several thousand tokens) on the fp32 chunk
+    kernel: o and the final states within the fp32 bound, the empty
+    sequence's state copied exactly."""
+    lens = [300, 0, 77, 2500, 64, 1, 130, 9]
+    say(f"chunk8 fp32 varlen lens={lens} H=3 dk={dk} dv={dv}")
+    x = synth.make_inputs("varlen_f32", lens=lens, H=3)
+    if (dk, dv) != (128, 128):
+        w = synth.WORKLOADS["varlen_f32"]
+        n = int(x.cu_seqlens[-1])
+        q, k, v, beta, g = synth.draw_tokens(n, 3, dk, dv, torch.float32, w.g_mu, w.g_sigma, 41)
+        x = synth.KDAInputs(q[None], k[None], v[None], g[None], beta[None], dk ** -0.5,
+                            synth.draw_state(len(lens), 3, dk, dv, w.h0_std, 41), x.cu_seqlens)
+    o, f = run_prefill(x, "chunk8")
+    o_ref, f_ref = oracle_prefill(x)
+    eo = assert_parity(o, o_ref, torch.float32, "o")
+    ef = assert_parity(f, f_ref, torch.float32, "final")
+    say(f"  o max-abs {eo:.2e} final max-abs {ef:.2e}")
+    assert torch.equal(f[1].cpu(), x.h0[1])
+
+
+def test_chunk8_strong_forget_fp32():
+    """The strong-forget gates (alpha = 0 tokens, e^-20 and e^-60 channels,
+    g = -1e30) on fp32 inputs: the entry-by-entry Gram path keeps the fp32
+    bound."""
+    lens = [900, 33, 2100, 64]
+    say(f"chunk8 fp32 strong-forget varlen lens={lens} H=2")
+    x = synth.make_inputs("varlen_f32", lens=lens, H=2, seed=43)
+    x.g = strong_forget_gates(x.g.shape, 47)
+    o, f = run_prefill(x, "chunk8")
+    o_ref, f_ref = oracle_prefill(x)
+    eo = assert_parity(o, o_ref, torch.float32, "o")
+    ef = assert_parity(f, f_ref, torch.float32, "final")
+    say(f"  o max-abs {eo:.2e} final max-abs {ef:.2e}")
+
+
+def test_chunk8_in_place_and_short_runs():
+    """The final state written over the initial one, and agreement with the
+    short-run entry point (same sub-chunk arithmetic, state in place)."""
+    say("chunk8 in place; equals fused_recurrent_fwd on 8-token runs")
+    x = synth.make_inputs("verify", n_seqs=6, H=4, T=8)
+    dev = torch.device("cuda")
+    xd = x.to(dev)
+    kda = _kda()
+    st = xd.h0.clone()
+    o1 = kda.fused_recurrent_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, st)
+    st2 = xd.h0.clone()
+    o2, f2 = kda.chunk_fwd(xd.q, xd.k, xd.v, xd.g, xd.beta, x.scale, st2, final_state=st2,
+                           variant="chunk8")
+    torch.cuda.synchronize()
+    assert f2.data_ptr() == st2.data_ptr()
+    assert max_abs(o2, o1) <= 1e-5 and max_abs(st2, st) <= 1e-5
+    o_ref, s_ref = ref.kda_fused_recurrent(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0)
+    assert max_abs(o2, o_ref) <= 1e-4 and max_abs(st2, s_ref) <= 1e-4
+
+
+def test_chunk8_fp32_workload_sized():
+    """fp32 varlen over 16 sequences (65536 tokens, H=4, log-uniform lengths
+    from 256 to 16384), compared whole with the oracle."""
+    lens = synth.varlen_lengths(16, 65536, lo=256, hi=16384)
+    say(f"chunk8 fp32 varlen 16 sequences, 65536 tokens, H=4")
+    x = synth.make_inputs("varlen_f32", lens=lens, H=4)
+    o, f = run_prefill(x)  # AUTO takes the fp32 chunk kernel
+    o_ref, f_ref = oracle_prefill(x)
+    eo = assert_parity(o, o_ref, torch.float32, "o")
+    ef = assert_parity(f, f_ref, torch.float32, "final")
+    say(f"  o max-abs {eo:.2e} final max-abs {ef:.2e}")
 
 
 @pytest.mark.parametrize("T,H", [(20000, 2), (1500, 3)])
