@@ -79,14 +79,24 @@ def time_launches(fn, stream, reps, warmup=2):
 
 
 def code_sha256(path):
-    """sha256 of a C/HIP source with comments and whitespace removed, so that
-    only changes to the code itself count as a change of the kernel."""
+    """sha256 of a C/HIP source and the headers it includes from its own
+    directory (recursively, each once), with comments and whitespace removed,
+    so that only changes to the code itself count as a change of the kernel."""
     import hashlib
     import re
-    src = open(path, encoding="utf-8").read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", "", src)
-    return hashlib.sha256(re.sub(r"\s+", "", src).encode()).hexdigest()
+    h = hashlib.sha256()
+    todo, seen = [os.path.abspath(path)], set()
+    while todo:
+        p = todo.pop(0)
+        if p in seen or not os.path.exists(p):
+            continue
+        seen.add(p)
+        src = open(p, encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update(re.sub(r"\s+", "", src).encode())
+        todo += [os.path.join(os.path.dirname(p), f) for f in re.findall(r'#include\s+"([^"]+)"', src)]
+    return h.hexdigest()
 
 
 def measured_traffic(key, workload_label):

@@ -822,6 +822,22 @@ def test_varlen_workload_full_size():
 
 
 @pytest.mark.timeout(900)
+def test_varlen_f32_workload_full_size():
+    """The varlen shape with fp32 q/k/v (64 sequences, 262144 tokens, H=32)
+    through AUTO, which takes the fp32 chunk kernel, against the C oracle on
+    every chain at the fp32 bound: max-abs over all of o and all 2048 final
+    states."""
+    say("varlen fp32 full size 262144 tokens H=32 (fp32 chunk kernel), every chain against the oracle")
+    dev = torch.device("cuda")
+    x = synth.make_inputs("varlen_f32", device=dev)
+    o, f = _kda().chunk_fwd(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0, x.cu_seqlens)
+    torch.cuda.synchronize()
+    eo, ef = stream_compare(x, o, f, n_threads=THREADS, log=say, absolute=True)
+    say(f"  varlen fp32 full size: max|do| {eo:.2e}  max|dS| {ef:.2e}")
+    assert eo <= 1e-4 and ef <= 1e-4
+
+
+@pytest.mark.timeout(900)
 def test_long_workload_full_size():
     """The full long workload (one sequence of 1,048,576 tokens, H=32) through
     AUTO (the segment scan), against the C oracle on every token and head: the

@@ -48,10 +48,13 @@ def test_single_wrong_value_is_seen(where):
     else:  # the empty sequence keeps its initial state
         f[1, 0, 0, 0] += 0.05 * rms_f
     eo, ef = stream_compare(x, o, f, window=64, log=lambda m: None)
+    ao, af = stream_compare(x, o, f, window=64, log=lambda m: None, absolute=True)
     if where.startswith("o"):
         assert 0.04 < eo < 0.06 and ef < 1e-12
+        assert abs(ao - 0.05 * rms_o) < 1e-12 * rms_o and af < 1e-12
     else:
         assert eo < 1e-12 and 0.04 < ef < 0.06
+        assert ao < 1e-12 and abs(af - 0.05 * rms_f) < 1e-12 * rms_f
 
 
 def test_accum_matches_whole_tensor_criterion():
