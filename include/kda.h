@@ -82,11 +82,12 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *             and then the state work of each chunk; same inputs as CHUNK.
  *             Never chosen by AUTO.
  *  CHUNK8     chunkwise kernel in fp32 arithmetic throughout (fp32 MFMA,
- *             8-token sub-chunks), one workgroup of 4 waves per (sequence,
- *             head); any supported head size, fp32 or bf16 inputs, results
- *             within fp32 rounding of the token-by-token recurrence.  AUTO
- *             takes it for the arguments CHUNK does not support (fp32
- *             inputs, d_k or d_v other than 128). */
+ *             8-token sub-chunks), workgroups of state, gate and solve waves
+ *             pipelined over sub-chunks, one or more per (sequence, head)
+ *             by state columns; any supported head size, fp32 or bf16
+ *             inputs, results within fp32 rounding of the token-by-token
+ *             recurrence.  AUTO takes it for the arguments CHUNK does not
+ *             support (fp32 inputs, d_k or d_v other than 128). */
 typedef enum kda_variant {
     KDA_VARIANT_AUTO = 0,
     KDA_VARIANT_RECURRENT = 1,
