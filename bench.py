@@ -419,6 +419,9 @@ def main():
             "frac_of_fp32_mfma_peak": f32f / (fm32 * 1e-3) / (MFMA_FP32_PEAK_TFLOPS * 1e12),
             "gbs": f32b / (fm32 * 1e-3) / 1e9, "frac": f32b / (fm32 * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "alg_bytes": f32b, "alg_flops": f32f,
+            "traffic_gb": (lambda t: None if t is None else t / 1e9)(measured_traffic(
+                "chunk8", f"fp32 chunk kernel: varlen shape with fp32 q/k/v, {N} sequences, {tokens} tokens, "
+                          f"H={H}, d={dk}")),
             "config": f"varlen shape with fp32 q/k/v: {N} sequences, {tokens} tokens, H={H}, "
                       f"d_k=d_v={dk}, fp32 o and states (AUTO: fp32 chunk kernel)"}
         del fx, fo, fws
