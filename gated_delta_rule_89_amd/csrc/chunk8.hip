@@ -103,7 +103,7 @@ template <int DK, int DV, typename Tin, typename Tout>
 __global__ __launch_bounds__((64 * Cfg<DK, DV>::NW)) __attribute__((amdgpu_waves_per_eu(Cfg<DK, DV>::WPE)))
 void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
                    const float* __restrict__ g, const float* __restrict__ beta, float scale,
-                   const ChunkItem* __restrict__ items, int H, const float* __restrict__ h0,
+                   const ChunkItem* __restrict__ items, int H, int nchains, const float* __restrict__ h0,
                    Tout* __restrict__ o, float* __restrict__ hT, float* __restrict__ snaps, int interval) {
     constexpr int MT = DK / 16;                 // row tiles of the state
     constexpr int CB = DK < 32 ? DK : 32;       // channels of a gate block
@@ -125,7 +125,15 @@ void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     const bool state = w < NS;                // then the gate waves and the solve wave
     const int gw = w - NS;
     const int r16 = l & 15, g4 = l >> 4;
-    const int chain = blockIdx.x / XS;         // the XS workgroups of a chain are adjacent
+    // Workgroups go to the 8 XCDs in turn (block b to XCD b % 8).  The XS
+    // column groups of a chain are placed 8 blocks apart, on one XCD, so that
+    // their identical k, q and g reads share its L2; chains still start in
+    // the longest-first order of the items.  The grid is rounded up to a
+    // multiple of 8 XS blocks; the extra ones have no chain.
+    const int round8 = static_cast<int>(blockIdx.x) / 8;
+    const int chain = XS == 1 ? static_cast<int>(blockIdx.x) : (round8 / XS) * 8 + static_cast<int>(blockIdx.x) % 8;
+    const int xs = XS == 1 ? 0 : round8 % XS;
+    if (chain >= nchains) return;
     const ChunkItem it = items[chain / H];
     const int h = chain % H;
     const int64_t t0 = it.t0, t1 = it.t1;
@@ -133,7 +141,7 @@ void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     const int n = static_cast<int>((t1 - t0 + C - 1) / C);  // sub-chunks
     const bool bw = state;
     // tile nt holds column col + nt
-    const int col = (blockIdx.x % XS) * W + (NT == 2 ? 32 * w + 2 * r16 : 16 * w + r16);
+    const int col = xs * W + (NT == 2 ? 32 * w + 2 * r16 : 16 * w + r16);
     const int cl = l & 31, hs = l >> 5;        // gate block: channel 32 gw + cl, tokens 4 hs .. 4 hs + 3
     const bool aw = !state && gw < NBLK;
     const bool al = aw && cl < CB;
@@ -457,9 +465,12 @@ void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
 template <int DK, int DV, typename Tin, typename Tout>
 hipError_t launch_t(const PrefillArgs& a, const ChunkItem* items) {
     using K = Cfg<DK, DV>;
-    hipLaunchKernelGGL((chunk8_kernel<DK, DV, Tin, Tout>), dim3(static_cast<uint32_t>(a.N) * a.H * (DV / K::W)),
+    constexpr int XS = DV / K::W;
+    const uint32_t nch = static_cast<uint32_t>(a.N) * a.H;
+    const uint32_t blocks = XS == 1 ? nch : (nch + 7) / 8 * 8 * XS;
+    hipLaunchKernelGGL((chunk8_kernel<DK, DV, Tin, Tout>), dim3(blocks),
                        dim3(64 * K::NW), 0, a.stream, static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k),
-                       static_cast<const Tin*>(a.v), a.g, a.beta, a.scale, items, a.H, a.h0,
+                       static_cast<const Tin*>(a.v), a.g, a.beta, a.scale, items, a.H, static_cast<int>(nch), a.h0,
                        static_cast<Tout*>(a.o), a.hT, a.snaps, a.snap_interval);
     return hipGetLastError();
 }
