@@ -688,6 +688,28 @@ def test_chunk8_varlen_fp32(dk, dv):
     assert torch.equal(f[1].cpu(), x.h0[1])
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 64), (32, 128), (128, 16)])
+def test_chunk8_bf16_inputs_other_head_sizes(dk, dv):
+    """bf16 q/k/v at head sizes the fp16 kernel does not take: AUTO runs the
+    fp32 chunk kernel.  Its arithmetic is fp32, so o (fp32) meets the fp32
+    bound of the oracle on the same widened inputs, and a bf16 o is each
+    value rounded once: within 2^-8 of the oracle's (plus 1e-6)."""
+    lens = [700, 1, 64, 129]
+    say(f"AUTO bf16 in dk={dk} dv={dv} lens={lens} H=2, fp32 and bf16 o")
+    w = synth.WORKLOADS["varlen"]
+    cu = synth.cu_seqlens_from_lengths(lens)
+    q, k, v, beta, g = synth.draw_tokens(int(cu[-1]), 2, dk, dv, torch.bfloat16, w.g_mu, w.g_sigma, 53)
+    x = synth.KDAInputs(q[None], k[None], v[None], g[None], beta[None], dk ** -0.5,
+                        synth.draw_state(len(lens), 2, dk, dv, w.h0_std, 53), cu)
+    o, f = run_prefill(x)
+    ob, fb = run_prefill(x, out_dtype=torch.bfloat16)
+    o_ref, f_ref = oracle_prefill(x)
+    assert max_abs(o, o_ref) <= 1e-4 and max_abs(f, f_ref) <= 1e-4
+    assert torch.equal(fb, f)
+    err = np.abs(ob.float().cpu().numpy() - np.asarray(o_ref))
+    assert bool(np.all(err <= 2.0 ** -8 * np.abs(np.asarray(o_ref)) + 1e-6)), float(np.max(err))
+
+
 def test_chunk8_strong_forget_fp32():
     """The strong-forget gates (alpha = 0 tokens, e^-20 and e^-60 channels,
     g = -1e30) on fp32 inputs: the entry-by-entry Gram path keeps the fp32

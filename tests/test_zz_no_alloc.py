@@ -41,7 +41,7 @@ def _both(x, variant, ref_variant=None):
     return o, f, o_ref, f_ref
 
 
-@pytest.mark.parametrize("variant", ["auto", "chunk", "chunk_scan", "chunk64", "recurrent"])
+@pytest.mark.parametrize("variant", ["auto", "chunk", "chunk_scan", "chunk64", "recurrent", "chunk8"])
 def test_noalloc_matches_chunk_fwd_on_two_calls(variant):
     cases = [("varlen", dict(lens=[3000, 77, 1500, 0, 640], H=4, seed=31)),
              ("varlen", dict(lens=[700, 33], H=2, seed=37))]
@@ -54,6 +54,21 @@ def test_noalloc_matches_chunk_fwd_on_two_calls(variant):
                                   n_threads=THREADS)
         assert_parity(o, oo, torch.bfloat16, "o")
         assert_parity(f, ff, torch.bfloat16, "final")
+
+
+def test_noalloc_fp32_inputs_on_two_calls():
+    """fp32 inputs (AUTO takes the fp32 chunk kernel, whose item list lives
+    in the library's array): equal to kda_chunk_fwd and within the fp32 bound
+    of the oracle on two consecutive calls, the second smaller."""
+    for kw in (dict(lens=[2000, 9, 513, 0], H=3, seed=43), dict(lens=[300], H=2, seed=47)):
+        say(f"noalloc fp32 auto {kw}")
+        x = synth.make_inputs("varlen_f32", **kw)
+        o, f, o_ref, f_ref = _both(x, "auto")
+        assert torch.equal(o, o_ref) and torch.equal(f, f_ref)
+        oo, ff = cref.kda_forward(x.q, x.k, x.v, x.g, x.beta, x.scale, x.h0, x.cu_seqlens,
+                                  n_threads=THREADS)
+        assert_parity(o, oo, torch.float32, "o")
+        assert_parity(f, ff, torch.float32, "final")
 
 
 def test_noalloc_auto_falls_back_when_the_scan_does_not_fit():
