@@ -89,7 +89,7 @@ template <int DK, int DV>
 struct Cfg {
     static constexpr int W = DK == 128 ? (DV >= 64 ? 64 : DV) : (DV < 32 ? DV : 32);
     static constexpr bool DED = !(DK == 128 && W == 64);
-    static constexpr int OCC = DK == 128 ? (W == 64 ? 2 : 1) : (DK == 64 ? 0 : 2);
+    static constexpr int OCC = DK == 128 ? (W == 64 ? 2 : 1) : (DK == 64 ? (DV == 16 ? 1 : 0) : (DV == 128 ? 0 : 2));
     static constexpr int NS = W == 128 ? 4 : W / 16;                   // state waves
     static constexpr int NBLK = DK < 32 ? 1 : DK / 32;                 // gate waves
     static constexpr int NW = NS + NBLK + (DED ? 1 : 0);               // waves
