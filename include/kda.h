@@ -107,7 +107,10 @@ const char* kda_status_str(kda_status status);
  * lengths and variant (0 is a valid answer).  N is the number of sequences
  * (B, or the length of cu_seqlens minus one); cu_seqlens_host is the host
  * copy of cu_seqlens or NULL, exactly as later passed to kda_chunk_fwd.
- * Returns 0 for arguments kda_chunk_fwd would reject. */
+ * RECURRENT needs none; every chunked variant (AUTO included, for any
+ * dtype and head size) needs at least a list of one small item per
+ * sequence, CHUNK_SCAN also room for the segment maps.  Returns 0 for
+ * arguments kda_chunk_fwd would reject. */
 size_t kda_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t d_k, int32_t d_v,
                                     int32_t N, const int32_t* cu_seqlens_host, kda_dtype in_dtype,
                                     kda_variant variant);
