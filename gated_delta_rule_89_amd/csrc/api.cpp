@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 
@@ -35,18 +36,19 @@ bool chunk_supported(int32_t dk, int32_t dv, kda_dtype in) {
     return in == KDA_BF16 && dk == 128 && dv == 128;
 }
 
-// Compute units of the current device, cached per device id.
+// Compute units of the current device, cached per device id (threads that
+// race on the first call store the same value).
 int cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // AUTO: the chunked kernel, with the segment scan when the longest sequence
