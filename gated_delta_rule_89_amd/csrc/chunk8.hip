@@ -34,15 +34,15 @@
 //   gate waves (one per 32-channel block): the factors of their block,
 //     written to LDS as operand rows, and the partial Grams over those
 //     channels (up to 8 MFMAs).
-//   the solve wave (a wave of its own, or the last gate wave): sums the
-//     partial Grams and forms T = (I + A)^-1 = (I + N)(I + N^2)(I + N^4) with
-//     N = -A (strictly lower 8 x 8, N^8 = 0) and P T by 8 x 8 products.
-// Iteration i runs the three as a pipeline with one barrier: the state waves
-// take sub-chunk i ([K~; Q~] S, [T; P T] X with X = Diag(beta)(V - K~ S),
-// which gives U and o together, and the state update), the solve wave
-// sub-chunk i + 1, the gate waves sub-chunk i + 2.  Operand tiles are kept
-// for three sub-chunks, partial Grams and solves for two, and every input is
-// fetched two sub-chunks ahead.
+//   the solve (state wave 0, after its own products): sums the partial
+//     Grams and forms T = (I + A)^-1 = (I + N)(I + N^2)(I + N^4) with N = -A
+//     (strictly lower 8 x 8, N^8 = 0) and P T by 8 x 8 products.
+// Iteration i runs them as a pipeline with one barrier: the state waves take
+// sub-chunk i ([K~; Q~] S, [T; P T] X with X = Diag(beta)(V - K~ S), which
+// gives U and o together, and the state update), then state wave 0 solves
+// sub-chunk i + 1; the gate waves take sub-chunk i + 2.  Operand tiles are
+// kept for three sub-chunks, partial Grams and solves for two, and every
+// input is fetched two sub-chunks ahead.
 //
 // Strong forgetting: K^ = k / gamma leaves fp32 range when a channel forgets
 // nearly everything inside the sub-chunk.  A block whose gate total passes
@@ -82,17 +82,15 @@ struct Smem {
 // them down, while the total work still has to fit.
 //   W    state columns per workgroup (a chain's d_v columns are split over
 //        d_v / W workgroups that each form the gate side);
-//   DED  a dedicated solve wave (else the last gate wave solves as well);
 //   OCC  the most workgroups a CU may hold (0: as registers and LDS allow),
 //        enforced through the workgroup's LDS size.
 template <int DK, int DV>
 struct Cfg {
     static constexpr int W = DK == 128 ? (DV >= 64 ? 64 : DV) : (DV < 32 ? DV : 32);
-    static constexpr bool DED = !(DK == 128 && W == 64);
     static constexpr int OCC = DK == 128 ? (W == 64 ? 2 : 1) : (DK == 64 ? (DV == 16 ? 1 : 0) : (DV == 128 ? 0 : 2));
     static constexpr int NS = W == 128 ? 4 : W / 16;                   // state waves
     static constexpr int NBLK = DK < 32 ? 1 : DK / 32;                 // gate waves
-    static constexpr int NW = NS + NBLK + (DED ? 1 : 0);               // waves
+    static constexpr int NW = NS + NBLK;                               // waves
     static constexpr int WGS = OCC ? OCC : 3;                           // workgroups per CU aimed at
     static constexpr int WPE = (NW * WGS + 3) / 4 > 2 ? (NW * WGS + 3) / 4 : 2;
     static constexpr int LDS_CU = 160 * 1024;
@@ -113,16 +111,13 @@ void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     constexpr int XS = DV / W;
     constexpr int NT = W == 128 ? 2 : 1;        // state tiles per state wave
     constexpr int NS = Cfg<DK, DV>::NS;         // state waves (waves 0 .. NS - 1)
-    // gate waves NS .. NS + NBLK - 1 form blocks; the solve wave follows them
-    // (or is the last gate wave)
-    constexpr int SW = Cfg<DK, DV>::DED ? NBLK : NBLK - 1;
     constexpr int PAD = Cfg<DK, DV>::PAD;
     __shared__ __align__(16) Smem<DK> sm;
     __shared__ char occupancy_pad[PAD > 0 ? PAD : 1];  // caps the workgroups per CU
 
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool state = w < NS;                // then the gate waves and the solve wave
+    const bool state = w < NS;                // then the gate waves, one per block
     const int gw = w - NS;
     const int r16 = l & 15, g4 = l >> 4;
     // Workgroups go to the 8 XCDs in turn (block b to XCD b % 8).  The XS
@@ -297,7 +292,7 @@ void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
         for (int i = 0; i < 4; ++i) sm.gp[j & 1][gw][4 * g4 + i][r16] = gacc[i];
     };
 
-    // ---- the solve of sub-chunk j (one wave): N = -A and P on lane (a8, b8);
+    // ---- the solve of sub-chunk j (state wave 0): N = -A and P on lane (a8, b8);
     // T = (I + N)(I + N^2)(I + N^4), P T ----
     auto solve = [&](int j) {
         const int rk = 4 * (a8 & 3) + (a8 >> 2);  // row of K~ of token a8 in [K~; Q~]
@@ -397,9 +392,10 @@ void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
         }
     };
 
-    // Iteration i: the state waves run sub-chunk i; the gate waves solve
-    // sub-chunk i + 1 (its partial Grams were written one iteration earlier)
-    // and form the factors and partial Grams of sub-chunk i + 2.  Tiles of
+    // Iteration i: the state waves run sub-chunk i and state wave 0 then
+    // solves sub-chunk i + 1 (its partial Grams were written one iteration
+    // earlier); the gate waves form the factors and partial Grams of
+    // sub-chunk i + 2.  Tiles of
     // sub-chunk j live in buffer j % 3 (partial Grams and solves: j % 2), so
     // one barrier per iteration orders every producer before its consumer
     // and every consumer before the overwrite.
@@ -409,8 +405,8 @@ void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
                 state_step(i, vx);
                 if (i + 2 < n) vfetch(i + 2, vx);
             }
+            if (w == 0 && i + 1 < n) solve(i + 1);
         } else {
-            if (gw == SW && i + 1 < n) solve(i + 1);
             if (aw && i + 2 < n) {
                 gate_block(i + 2, r);
                 if (i + 4 < n) gfetch(i + 4, r);
@@ -438,7 +434,7 @@ void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
         }
     }
     __syncthreads();
-    if (!state && gw == SW && 0 < n) solve(0);
+    if (w == 0 && 0 < n) solve(0);
     __syncthreads();
 
     for (int i = 0; i < n; i += 2) {
