@@ -313,10 +313,12 @@ void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     auto state_step = [&](int i, const float (&vc)[2][NT]) {
         const int bi = i % 3;
         const int64_t s0 = t0 + static_cast<int64_t>(C) * i;
-        // [K~; Q~] S, over even and odd row tiles in two accumulators
-        f4 y2[2][NT];
+        // [K~; Q~] S over the row tiles in up to four accumulators (shorter
+        // dependent MFMA chains), summed at the end
+        constexpr int NY = MT >= 4 ? 4 : MT;
+        f4 y2[NY][NT];
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
+        for (int e = 0; e < NY; ++e)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) y2[e][nt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -325,11 +327,15 @@ void chunk8_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) y2[mt & 1][nt] = mfma4(av[ii], acc[mt][nt][ii], y2[mt & 1][nt]);
+                for (int nt = 0; nt < NT; ++nt) y2[mt % NY][nt] = mfma4(av[ii], acc[mt][nt][ii], y2[mt % NY][nt]);
         }
         f4 y[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) y[nt] = y2[0][nt] + y2[1][nt];
+        for (int nt = 0; nt < NT; ++nt) {
+            y[nt] = y2[0][nt];
+#pragma unroll
+            for (int e = 1; e < NY; ++e) y[nt] += y2[e][nt];
+        }
 
         // X = Diag(beta)(V - K~ S) for tokens g4 and 4 + g4; [T; P T] X
         const float bg = sm.beta[bi][g4], b4 = sm.beta[bi][4 + g4];
