@@ -31,6 +31,24 @@ def test_exports_match_header():
         assert hasattr(kda.lib, n), n
 
 
+def header_enum(name):
+    """{member: value} of `typedef enum name { ... }` in kda.h."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef enum %s\s*\{(.*?)\}" % name, src, flags=re.S).group(1)
+    return {m: int(v) for m, v in re.findall(r"(KDA_[A-Z0-9_]+)\s*=\s*(\d+)", body)}
+
+
+def test_binding_constants_match_header():
+    variants = header_enum("kda_variant")
+    assert {("KDA_VARIANT_" + k.upper()): v for k, v in _lib.VARIANTS.items()} == variants
+    status = header_enum("kda_status")
+    assert sorted(status.values()) == list(range(10))
+    assert (OK, NULL, SHAPE, DTYPE, UNSUP, SEQ, ALIAS, ALIGN, WS, HIP) == tuple(
+        status["KDA_" + n] for n in ("OK", "ERR_NULL", "ERR_SHAPE", "ERR_DTYPE", "ERR_UNSUPPORTED",
+                                     "ERR_SEQLENS", "ERR_ALIAS", "ERR_ALIGN", "ERR_WORKSPACE", "ERR_HIP"))
+    assert header_enum("kda_dtype") == {"KDA_F32": F32, "KDA_BF16": BF16}
+
+
 def test_abi_version_and_status_strings():
     assert kda.abi_version() == 1
     for code in range(10):
