@@ -710,6 +710,23 @@ def test_chunk8_bf16_inputs_other_head_sizes(dk, dv):
     assert bool(np.all(err <= 2.0 ** -8 * np.abs(np.asarray(o_ref)) + 1e-6)), float(np.max(err))
 
 
+def test_chunk8_prefill_shape_fp32():
+    """The single-sequence prefill shape (T = 4096, H = 8, d = 128, random
+    initial state) with fp32 q/k/v through AUTO: eight chains of 512
+    sub-chunks each on the fp32 chunk kernel, o and final states within the
+    fp32 bound of the oracle."""
+    say("AUTO fp32 prefill T=4096 H=8 d=128")
+    w = synth.WORKLOADS["prefill"]
+    q, k, v, beta, g = synth.draw_tokens(4096, 8, 128, 128, torch.float32, w.g_mu, w.g_sigma, 59)
+    x = synth.KDAInputs(q[None], k[None], v[None], g[None], beta[None], w.scale,
+                        synth.draw_state(1, 8, 128, 128, w.h0_std, 59), None)
+    o, f = run_prefill(x)
+    o_ref, f_ref = oracle_prefill(x)
+    eo = assert_parity(o, o_ref, torch.float32, "o")
+    ef = assert_parity(f, f_ref, torch.float32, "final")
+    say(f"  o max-abs {eo:.2e} final max-abs {ef:.2e}")
+
+
 def test_chunk8_strong_forget_fp32():
     """The strong-forget gates (alpha = 0 tokens, e^-20 and e^-60 channels,
     g = -1e30) on fp32 inputs: the entry-by-entry Gram path keeps the fp32
